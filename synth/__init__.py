@@ -1,0 +1,289 @@
+"""Seeded synthetic inputs for the fused low-bit dequant-matmul path.
+
+This module builds the *stored tensors* (codes, tables, signs, scales,
+envelopes) and the activations that both the CPU oracle and the GPU library
+consume.  It is the only code the two sides share, and it holds none of the
+method's arithmetic: no bit packing, no decode, no matrix product.  What it
+does hold is quantizer-side input construction (level placement, nearest-level
+assignment, per-block statistics, a 1-D k-means), which the pages describe as
+the offline step that produces the stored format.
+
+Every array is unpacked (one element per weight / sign / index); the packed
+byte layouts are produced independently by the oracle's packers and by the
+library's pack kernels.
+
+Sources (page titles; no code is copied from them):
+  * "Qwen3.8-27B - BenQ 6-bit" model card, sections "What BenQ stores" and
+    "Why equal-width shells": 6-bit codes = 1 sign + 5 tier bits indexing a
+    per-row table of 64 signed bf16 magnitudes (32 negative ascending, then 32
+    positive); equal-width shells; nearest-level assignment as the
+    uncalibrated fallback.
+  * "FABQ-RC" README ("Key Ideas") and model card ("How It Works",
+    "Quantization Details"): top 5 % channels at higher precision (int4 in the
+    model card), the rest binary with per-block scales, a residual codebook.
+  * OneCompression "MDBF" documentation ("Algorithm"): sign matrices S_A, S_B
+    and fp16 envelopes A_amp, B_amp, Q_U, Q_V.
+
+Seeds: numpy PCG64 ``default_rng``.  A config's weights use ``seed``; its
+activations use the stream ``[seed, 1, batch]``.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_from_f64",
+    "fp16_bits_from_f64",
+    "activations",
+    "Lut6Input",
+    "lut6_input",
+    "FabqInput",
+    "fabq_input",
+    "fabq_quantize",
+    "MdbfInput",
+    "mdbf_input",
+    "CONFIGS",
+]
+
+
+# ---------------------------------------------------------------------------
+# storage rounding used to *build* inputs (fp64 -> fp32 -> bf16, each RNE)
+# ---------------------------------------------------------------------------
+def bf16_bits_from_f64(a) -> np.ndarray:
+    """fp64 -> fp32 (RNE) -> bf16 (RNE); returns uint16 bit patterns."""
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def _bf16_bits_to_f64(bits) -> np.ndarray:
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def fp16_bits_from_f64(a) -> np.ndarray:
+    """fp64 -> fp16 (RNE); returns uint16 bit patterns."""
+    return np.asarray(a, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def activations(batch: int, cols: int, seed: int) -> np.ndarray:
+    """x[batch][cols] ~ N(0,1) stored as bf16 bits (stream [seed, 1, batch])."""
+    rng = np.random.default_rng([seed, 1, batch])
+    return bf16_bits_from_f64(rng.standard_normal((batch, cols)))
+
+
+# ---------------------------------------------------------------------------
+# per-row LUT, 6-bit codes (BenQ)
+# ---------------------------------------------------------------------------
+@dataclass
+class Lut6Input:
+    codes: np.ndarray  # uint8 [rows][cols], 0..63
+    lut: np.ndarray    # uint16 bf16 bits [rows][64], ascending by value
+    rows: int
+    cols: int
+    seed: int
+
+
+def lut6_input(rows: int, cols: int, seed: int, *, exact_argmin: bool = False) -> Lut6Input:
+    """Gaussian rows, 32 equal-width shells per sign, nearest-level codes.
+
+    sigma_r is log-uniform on [0.005, 0.05]; w ~ N(0, sigma_r^2) in fp64.
+    With M_r = max_k |w_rk| and D_r = M_r / 32, the 32 magnitude levels sit at
+    the shell centres (t + 1/2) D_r.  The table is the 64 signed levels sorted
+    ascending (-l_31 ... -l_0, l_0 ... l_31), rounded fp64 -> fp32 -> bf16.
+    A weight's code is the index of the nearest bf16 level (fp64 distance,
+    ties to the lower index).
+    """
+    rng = np.random.default_rng(seed)
+    sigma = np.exp(rng.uniform(math.log(0.005), math.log(0.05), size=rows))
+    w = rng.standard_normal((rows, cols)) * sigma[:, None]
+    amax = np.abs(w).max(axis=1)
+    delta = amax / 32.0
+    t = np.arange(32, dtype=np.float64) + 0.5
+    pos = t[None, :] * delta[:, None]                       # [rows][32]
+    table = np.concatenate([-pos[:, ::-1], pos], axis=1)   # ascending by value
+    lut = bf16_bits_from_f64(table)
+    lutv = _bf16_bits_to_f64(lut)
+    if exact_argmin:
+        codes = _nearest_full(w, lutv)
+    else:
+        codes = _nearest_shell(w, delta, lutv)
+    return Lut6Input(codes=codes, lut=lut, rows=rows, cols=cols, seed=seed)
+
+
+def _nearest_full(w, lutv):
+    d = np.abs(w[:, :, None] - lutv[:, None, :])
+    return np.argmin(d, axis=2).astype(np.uint8)  # first minimum = lower index
+
+
+def _nearest_shell(w, delta, lutv, chunk_rows: int = 1024):
+    """Shell index, then a +-1 neighbour check against the bf16 levels.
+
+    bf16 rounding moves a level by at most 2^-9 of its value (< 0.07 D), so the
+    nearest rounded level is the shell's own level or an adjacent one.
+    """
+    rows, cols = w.shape
+    out = np.empty((rows, cols), dtype=np.uint8)
+    for r0 in range(0, rows, chunk_rows):
+        ws = w[r0:r0 + chunk_rows]
+        lv = lutv[r0:r0 + chunk_rows]
+        dl = delta[r0:r0 + chunk_rows, None]
+        tier = np.minimum(np.floor(np.abs(ws) / dl), 31).astype(np.int64)
+        c0 = np.where(ws >= 0, 32 + tier, 31 - tier)
+        cand = np.stack([np.clip(c0 - 1, 0, 63), c0, np.clip(c0 + 1, 0, 63)], axis=0)
+        vals = np.take_along_axis(np.broadcast_to(lv[None], (3,) + lv.shape), cand, axis=2)
+        dist = np.abs(ws[None] - vals)
+        pick = np.argmin(dist, axis=0)
+        out[r0:r0 + chunk_rows] = np.take_along_axis(cand, pick[None], axis=0)[0]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# FABQ-RC-style binary core
+# ---------------------------------------------------------------------------
+@dataclass
+class FabqInput:
+    rows: int
+    cols: int
+    blocksize: int
+    row_of: np.ndarray      # int32 [rows]: output row of stored row i (int4 rows first)
+    n_hi: int
+    q4: np.ndarray          # int8 [n_hi][cols], -8..7
+    s_hi: np.ndarray        # uint16 fp16 bits [n_hi]
+    signs: np.ndarray       # uint8 [n_lo][cols], 1 -> +1, 0 -> -1
+    s_blk: np.ndarray       # uint16 fp16 bits [n_lo][cols/bs]
+    idx: np.ndarray         # uint8 [n_lo][cols/bs], 0..15
+    codebook: np.ndarray    # uint16 fp16 bits [16]
+    seed: int
+
+
+def fabq_blocksize_draw(seed: int) -> int:
+    """The layer's blocksize: one seeded draw from {64, 128, 256, 512}."""
+    rng = np.random.default_rng([seed, 2])
+    return int(rng.choice([64, 128, 256, 512]))
+
+
+def fabq_input(rows: int, cols: int, seed: int, blocksize: int | None = None,
+               hi_frac: float = 0.05, n_codes: int = 16) -> FabqInput:
+    """Gaussian rows (per-row sigma as for the LUT rows); seeded importance.
+
+    * importance ~ U(0,1) per output row; the top ``hi_frac`` rows are int4:
+      s_r = fp16(max|w_r| / 7), q = clip(rint(w / s_r), -8, 7).
+    * every other row is binary per block of ``blocksize`` columns:
+      s_b = fp16(mean|w|), sign = (w >= 0), residual mean
+      mu_b = mean(w - s_b * sign_pm1).
+    * codebook: 1-D Lloyd k-means (16 centroids) over all mu_b, started at the
+      (i + 1/2)/16 quantiles, run until assignments stop changing (<= 100
+      iterations; an empty cluster keeps its centroid), rounded to fp16;
+      idx_b = nearest fp16 centroid (ties to the lower index).
+    """
+    bs = fabq_blocksize_draw(seed) if blocksize is None else int(blocksize)
+    rng = np.random.default_rng(seed)
+    sigma = np.exp(rng.uniform(math.log(0.005), math.log(0.05), size=rows))
+    w = rng.standard_normal((rows, cols)) * sigma[:, None]
+    importance = rng.uniform(size=rows)
+    return fabq_quantize(w, importance, bs, hi_frac=hi_frac, n_codes=n_codes, seed=seed)
+
+
+def fabq_quantize(w: np.ndarray, importance: np.ndarray, bs: int, hi_frac: float = 0.05,
+                  n_codes: int = 16, seed: int = -1) -> FabqInput:
+    """Quantizer-side construction of the stored tensors from fp64 weights."""
+    rows, cols = w.shape
+    if cols % bs:
+        raise ValueError("blocksize must divide cols")
+    n_hi = int(round(hi_frac * rows))
+    order = np.argsort(-np.asarray(importance), kind="stable")
+    hi_rows = np.sort(order[:n_hi])
+    lo_rows = np.sort(order[n_hi:])
+    row_of = np.concatenate([hi_rows, lo_rows]).astype(np.int32)
+
+    wh = w[hi_rows]
+    s_hi = fp16_bits_from_f64(np.abs(wh).max(axis=1) / 7.0)
+    s_hi_v = s_hi.view(np.float16).astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s_hi_v[:, None] > 0, np.rint(wh / s_hi_v[:, None]), 0.0)
+    q4 = np.clip(q, -8, 7).astype(np.int8)
+
+    wl = w[lo_rows]
+    nb = cols // bs
+    wb = wl.reshape(len(lo_rows), nb, bs)
+    s_blk = fp16_bits_from_f64(np.abs(wb).mean(axis=2))
+    s_blk_v = s_blk.view(np.float16).astype(np.float64)
+    pos = wb >= 0
+    pm1 = np.where(pos, 1.0, -1.0)
+    mu = (wb - s_blk_v[:, :, None] * pm1).mean(axis=2)
+    codebook = _lloyd_1d(mu.ravel(), n_codes) if mu.size else np.zeros(n_codes)
+    cb_bits = fp16_bits_from_f64(codebook)
+    cb_v = cb_bits.view(np.float16).astype(np.float64)
+    idx = np.argmin(np.abs(mu[:, :, None] - cb_v[None, None, :]), axis=2).astype(np.uint8)
+    signs = pos.reshape(len(lo_rows), cols).astype(np.uint8)
+    return FabqInput(rows=rows, cols=cols, blocksize=bs, row_of=row_of, n_hi=n_hi,
+                     q4=q4, s_hi=s_hi, signs=signs, s_blk=s_blk, idx=idx,
+                     codebook=cb_bits, seed=seed)
+
+
+def _lloyd_1d(v: np.ndarray, k: int, max_iter: int = 100) -> np.ndarray:
+    c = np.quantile(v, (np.arange(k) + 0.5) / k)
+    assign = None
+    for _ in range(max_iter):
+        new = np.argmin(np.abs(v[:, None] - c[None, :]), axis=1)
+        if assign is not None and np.array_equal(new, assign):
+            break
+        assign = new
+        sums = np.bincount(assign, weights=v, minlength=k)
+        cnt = np.bincount(assign, minlength=k)
+        nz = cnt > 0
+        c = c.copy()
+        c[nz] = sums[nz] / cnt[nz]
+    return c
+
+
+# ---------------------------------------------------------------------------
+# MDBF double-binary factorisation
+# ---------------------------------------------------------------------------
+@dataclass
+class MdbfInput:
+    n: int
+    m: int
+    r: int
+    l: int
+    P: int
+    S_A: list   # P x uint8 [n][r], 1 -> +1
+    S_B: list   # P x uint8 [r][m]
+    A_amp: list  # P x uint16 fp16 bits [n][l]
+    B_amp: list  # P x uint16 fp16 bits [m][l]
+    Q_U: list    # P x uint16 fp16 bits [r][l]
+    Q_V: list    # P x uint16 fp16 bits [r][l]
+    seed: int
+
+
+def mdbf_input(n: int, m: int, r: int, l: int, P: int, seed: int,
+               amp_scale: float = 0.05) -> MdbfInput:
+    """Random +-1 sign matrices (Bernoulli 1/2) and fp16 envelopes |N(0,1)|*0.05."""
+    rng = np.random.default_rng(seed)
+    out = dict(S_A=[], S_B=[], A_amp=[], B_amp=[], Q_U=[], Q_V=[])
+    for _ in range(P):
+        out["S_A"].append(rng.integers(0, 2, size=(n, r), dtype=np.uint8))
+        out["S_B"].append(rng.integers(0, 2, size=(r, m), dtype=np.uint8))
+        out["A_amp"].append(fp16_bits_from_f64(np.abs(rng.standard_normal((n, l))) * amp_scale))
+        out["B_amp"].append(fp16_bits_from_f64(np.abs(rng.standard_normal((m, l))) * amp_scale))
+        out["Q_U"].append(fp16_bits_from_f64(np.abs(rng.standard_normal((r, l))) * amp_scale))
+        out["Q_V"].append(fp16_bits_from_f64(np.abs(rng.standard_normal((r, l))) * amp_scale))
+    return MdbfInput(n=n, m=m, r=r, l=l, P=P, seed=seed, **out)
+
+
+# ---------------------------------------------------------------------------
+# the workloads (shapes of the pages' 27B-class layers)
+# ---------------------------------------------------------------------------
+CONFIGS = {
+    "tiny_lut6": dict(rows=256, cols=512, seed=1, batches=(1,), y="f32"),
+    "lut6_up": dict(rows=17408, cols=5120, seed=2, batches=(1, 8), y="bf16"),
+    "lut6_down": dict(rows=5120, cols=17408, seed=3, batches=(1, 8), y="bf16"),
+    "prefill": dict(M=2048, weights="lut6_up", seed=4),
+    "fabq": dict(rows=5120, cols=5120, seed=5, batches=(1, 8)),
+    "mdbf": dict(n=4096, m=4096, r=2000, l=2, P=1, seed=6, batches=(1, 16)),
+}
