@@ -1,0 +1,71 @@
+// Internal declarations shared by the library's HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fqm.h"
+
+namespace fqm {
+
+// ---- small device helpers -------------------------------------------------
+
+// bf16 bits -> fp32 (exact: a bf16 is the top half of an fp32).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+// The two bf16 halves of a packed dword.
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// fp16 bits -> fp32 (exact).
+__device__ __forceinline__ float fp16_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Sum over the 64 lanes of a wavefront; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// The 16 six-bit codes of a 12-byte piece (three little-endian dwords):
+// code j sits at bits [6j, 6j+6) of the 96-bit value.
+__device__ __forceinline__ void codes16(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t c[16]) {
+#pragma unroll
+    for (int j = 0; j < 5; ++j) c[j] = (d0 >> (6 * j)) & 63u;
+    c[5] = __builtin_amdgcn_alignbit(d1, d0, 30) & 63u;
+#pragma unroll
+    for (int j = 6; j < 10; ++j) c[j] = (d1 >> (6 * j - 32)) & 63u;
+    c[10] = __builtin_amdgcn_alignbit(d2, d1, 28) & 63u;
+#pragma unroll
+    for (int j = 11; j < 16; ++j) c[j] = (d2 >> (6 * j - 64)) & 63u;
+}
+
+// ---- launchers (host side, one per kernel family) ---------------------------
+
+hipError_t launch_pack_bits(const uint8_t* vals, uint8_t* out, int64_t rows, int64_t cols,
+                            int bits, int64_t ld, int32_t* d_err, hipStream_t s);
+hipError_t launch_unpack6(const uint8_t* packed, uint8_t* codes, int64_t rows, int64_t cols,
+                          int64_t ld, hipStream_t s);
+hipError_t launch_dequant_lut6(const fqm_weights& w, uint16_t* W, hipStream_t s);
+hipError_t launch_dequant_fabq(const fqm_weights& w, uint16_t* W, hipStream_t s);
+
+hipError_t launch_lut6_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
+                            int batch, hipStream_t s);
+hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M,
+                            hipStream_t s);
+hipError_t launch_fabq_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
+                            int batch, hipStream_t s);
+hipError_t launch_mdbf_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
+                            int batch, float* z, hipStream_t s);
+
+}  // namespace fqm

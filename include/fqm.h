@@ -1,0 +1,206 @@
+/*
+ * fqm.h - fused low-bit dequant-matmul for AMD MI355X (gfx950), C ABI.
+ *
+ * The library computes the weight-only quantized products y = W x (GEMV,
+ * batch 1..16) and Y = X W^T (GEMM) where W is stored in one of three packed
+ * formats and is decoded inside the kernels; W is never written out in full
+ * (fqm_dequant exists for testing only).
+ *
+ * Formats (pages named by title and section):
+ *   FQM_LUT6  "Qwen3.8-27B - BenQ 6-bit", "What BenQ stores": one 6-bit code
+ *             per weight (1 sign bit + 5 magnitude-tier bits) indexing its
+ *             output row's own table of 64 signed bf16 levels (32 negative in
+ *             ascending order, then 32 positive); decoding W is the row-wise
+ *             gather of codes into the tables, and the card's kernel fuses
+ *             that gather into the matrix product.  Codes are packed four per
+ *             three bytes, the packing its usage note says the format needs.
+ *   FQM_FABQ  "FABQ-RC" README "Key Ideas" and the FABQ-RC model card
+ *             "How It Works" / "Quantization Details": the top 5 % of output
+ *             rows as int4 with an fp16 row scale, the rest binary +-1 with an
+ *             fp16 scale per block of `blocksize` columns plus a per-block
+ *             4-bit index into a 16-entry fp16 residual codebook whose
+ *             centroid is added back at inference:
+ *                 w = s_b * (+-1) + c[idx_b].
+ *   FQM_MDBF  OneCompression "MDBF", "Algorithm": W = sum_p F_p G_p with
+ *             F = S_A (.) (A_amp Q_U^T), G = S_B (.) (Q_V B_amp^T), sign
+ *             matrices packed 8 per byte and fp16 envelopes; evaluated as
+ *                 z = sum_k q_V,k (.) (S_B (b_k (.) x)),
+ *                 y = sum_k a_k (.) (S_A (q_U,k (.) z)).
+ *
+ * Packed bit fields.  Every packed tensor uses one rule: a row of `cols`
+ * fields of b bits is a little-endian bit stream; field k occupies stream
+ * bits [b*k, b*k + b), least significant bit first, and stream bit i is bit
+ * (i mod 8) of byte (i div 8).  Rows start every `ld` bytes; bytes after the
+ * last field are zero (fqm_pack writes them) and are ignored by the kernels.
+ *   b = 6: LUT6 codes.  b = 1: signs, bit 1 = +1, bit 0 = -1.
+ *   b = 4: int4 weights (two's complement) and codebook indices.
+ *
+ * Numbers.  bf16 and fp16 values are passed as their uint16_t bit patterns.
+ * Products accumulate in fp32; bf16 outputs are rounded to nearest even.
+ *
+ * Conventions shared by every call.
+ *   - Ownership: the caller allocates and frees every buffer.  All tensor
+ *     pointers are DEVICE pointers unless stated otherwise; descriptor
+ *     structs (fqm_weights) are HOST memory and are read during the call
+ *     only.  The library allocates nothing, frees nothing, keeps no pointer
+ *     after returning and holds no mutable global state; calls on different
+ *     streams may run concurrently.
+ *   - Ordering: every call only enqueues work on `stream` (a hipStream_t
+ *     passed as void*, NULL = the null stream) and returns; inputs must stay
+ *     valid and unmodified, and outputs unread, until the stream passes the
+ *     call.
+ *   - Errors: arguments are checked on the host before anything is enqueued.
+ *     A non-zero fqm_status means nothing was enqueued, except FQM_E_HIP
+ *     (a launch failed; earlier kernels of the same call may have run).
+ *     Data-dependent errors (a value too wide for its field in fqm_pack*)
+ *     are reported through a device flag instead.
+ *   - Alignment: every tensor base pointer must be 16-byte aligned and every
+ *     row stride `ld` a multiple of 16 bytes (FQM_E_ALIGN otherwise).
+ *   - Empty work: rows == 0, batch rows == 0 or M == 0 enqueue nothing and
+ *     return FQM_OK; cols == 0 writes zeros to y.
+ */
+#ifndef FQM_H
+#define FQM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FQM_VERSION 1
+
+typedef enum fqm_status {
+    FQM_OK = 0,
+    FQM_E_NULL = 1,        /* a required pointer is NULL */
+    FQM_E_ALIGN = 2,       /* a base pointer or row stride breaks the 16-byte rule */
+    FQM_E_SHAPE = 3,       /* sizes negative, out of range or inconsistent */
+    FQM_E_FORMAT = 4,      /* unknown format tag or format parameter out of range */
+    FQM_E_WORKSPACE = 5,   /* workspace missing or smaller than fqm_workspace_size */
+    FQM_E_UNSUPPORTED = 6, /* valid request this build does not implement */
+    FQM_E_HIP = 7          /* a HIP launch failed */
+} fqm_status;
+
+enum fqm_format { FQM_LUT6 = 1, FQM_FABQ = 2, FQM_MDBF = 3 };
+enum fqm_dtype { FQM_BF16 = 0, FQM_F32 = 1 };
+
+/* Per-row LUT, 6-bit codes (rows = N outputs, cols = K inputs).
+ * cols must be a multiple of 64 (one 48-byte group holds 64 codes). */
+typedef struct fqm_lut6 {
+    const uint8_t* packed;  /* [rows][ld] bytes, 6-bit fields */
+    const uint16_t* lut;    /* [rows][64] bf16, entry j is the level of code j */
+    int64_t ld;             /* bytes per packed row, >= cols*3/4 */
+} fqm_lut6;
+
+/* FABQ-RC-style core (rows = N, cols = K).  Stored row i (0 <= i < rows)
+ * produces output row row_of[i]; stored rows 0..n_hi-1 are int4 rows, stored
+ * rows n_hi..rows-1 are binary rows (binary row j = stored row n_hi + j).
+ * row_of must be a permutation of 0..rows-1 (not checked: a repeated entry
+ * makes two rows write the same output). */
+typedef struct fqm_fabq {
+    int32_t blocksize;          /* 64, 128, 256 or 512; divides cols */
+    int32_t n_hi;               /* int4 rows, 0..rows */
+    const int32_t* row_of;      /* [rows] */
+    const uint8_t* q4;          /* [n_hi][ld_q4], 4-bit two's complement fields */
+    int64_t ld_q4;              /* >= cols/2 */
+    const uint16_t* s_hi;       /* [n_hi] fp16 row scales */
+    const uint8_t* signs;       /* [rows-n_hi][ld_signs], 1-bit fields */
+    int64_t ld_signs;           /* >= cols/8 */
+    const uint16_t* s_blk;      /* [rows-n_hi][cols/blocksize] fp16, dense */
+    const uint8_t* idx;         /* [rows-n_hi][ld_idx], 4-bit fields, one per block */
+    int64_t ld_idx;             /* >= ceil(cols/blocksize/2) */
+    const uint16_t* codebook;   /* [16] fp16 centroids */
+} fqm_fabq;
+
+/* One MDBF path (rows = n outputs, cols = m inputs, rank r, envelope rank l). */
+typedef struct fqm_mdbf_path {
+    const uint8_t* S_A;         /* [n][ld_A], 1-bit fields along r */
+    int64_t ld_A;               /* >= ceil(r/8) */
+    const uint8_t* S_B;         /* [r][ld_B], 1-bit fields along m */
+    int64_t ld_B;               /* >= m/8 */
+    const uint16_t* A_amp;      /* [n][l] fp16 */
+    const uint16_t* B_amp;      /* [m][l] fp16 */
+    const uint16_t* Q_U;        /* [r][l] fp16 */
+    const uint16_t* Q_V;        /* [r][l] fp16 */
+} fqm_mdbf_path;
+
+typedef struct fqm_mdbf {
+    int32_t r;                  /* 1..65536 */
+    int32_t l;                  /* 1..16 */
+    int32_t P;                  /* 1 or 2; path[0..P-1] are used */
+    fqm_mdbf_path path[2];
+} fqm_mdbf;
+
+/* Weight descriptor: `format` selects which member is read. */
+typedef struct fqm_weights {
+    int32_t format;             /* enum fqm_format */
+    int64_t rows;               /* outputs (N, or n for MDBF) */
+    int64_t cols;               /* inputs  (K, or m for MDBF; MDBF needs m % 32 == 0) */
+    fqm_lut6 lut6;
+    fqm_fabq fabq;
+    fqm_mdbf mdbf;
+} fqm_weights;
+
+/* Library version (FQM_VERSION). */
+int32_t fqm_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fqm_status_str(int32_t status);
+
+/* Pack `bits`-wide unsigned fields (bits = 1, 4 or 6): vals [rows][cols]
+ * uint8, one field per byte, row-major and dense; out [rows][ld] bytes under
+ * the packed-field rule above, padding bytes zeroed.  A value >= 2^bits is
+ * packed as (value & (2^bits - 1)) and sets bit 0 of *d_err (a device int32
+ * the caller zeroes beforehand; may be NULL).  Signed int4 values are passed
+ * as (q & 15).  Requires ld >= ceil(cols*bits/8); vals needs no alignment.
+ * The bit-field rule is this project's convention; the pages fix only the
+ * field widths (see the format list above). */
+fqm_status fqm_pack_bits(const uint8_t* vals, uint8_t* out, int64_t rows, int64_t cols,
+                         int32_t bits, int64_t ld, int32_t* d_err, void* stream);
+
+/* Pack LUT6 codes (0..63), four per three bytes: fqm_pack_bits with bits = 6.
+ * Source: "Qwen3.8-27B - BenQ 6-bit", usage note on packing the stored
+ * uint8 codes to 6 bits (~28 GB -> ~21 GB). */
+fqm_status fqm_pack(const uint8_t* codes, uint8_t* packed, int64_t rows, int64_t cols,
+                    int64_t ld, int32_t* d_err, void* stream);
+
+/* Test helper: unpack 6-bit codes back to one byte per code, codes [rows][cols]
+ * dense.  Requires cols % 4 == 0. */
+fqm_status fqm_unpack(const uint8_t* packed, uint8_t* codes, int64_t rows, int64_t cols,
+                      int64_t ld, void* stream);
+
+/* Test helper: write the decoded weights W [rows][cols] as bf16, row-major,
+ * row index = output row.  LUT6: W[r][k] = lut[r][code] (an exact copy).
+ * FABQ: the exact value of q*s or s_b*(+-1) + c[idx] rounded once to bf16
+ * (nearest even).  MDBF: FQM_E_UNSUPPORTED (W is a product of factors). */
+fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
+
+/* Bytes of device workspace fqm_gemv needs for this descriptor and batch:
+ * MDBF P*batch*r*4 (the fp32 intermediate z); 0 for LUT6 and FABQ.
+ * Returns 0 for an invalid descriptor. */
+size_t fqm_workspace_size(const fqm_weights* w, int32_t batch);
+
+/* y = W x for `batch` activation rows (1..16).
+ * x: [batch][cols] bf16, row-major.  y: [batch][rows], bf16 (y_dtype =
+ * FQM_BF16) or fp32 (FQM_F32).  workspace: device memory of at least
+ * fqm_workspace_size(w, batch) bytes (may be NULL when that is 0); its
+ * contents on entry do not matter and are clobbered.
+ * LUT6 follows the BenQ card's decode (a gather into the row's table) fused
+ * into the product; FABQ and MDBF follow the decode stated with each format
+ * above; every decoded weight stays in fp32 (never rounded to bf16). */
+fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
+                    int32_t batch, void* workspace, size_t ws_bytes, void* stream);
+
+/* Y = X W^T for a LUT6 descriptor (prefill): X [M][cols] bf16, Y [M][rows]
+ * bf16, both row-major.  W tiles are decoded to bf16 in on-chip memory (exact:
+ * the levels are bf16) and contracted on the bf16 matrix cores with fp32
+ * accumulation.  FABQ / MDBF descriptors return FQM_E_UNSUPPORTED. */
+fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_t M,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FQM_H */

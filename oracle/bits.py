@@ -22,30 +22,35 @@ def packed_row_bytes(cols: int, b: int) -> int:
     return (cols * b + 7) // 8
 
 
-def pack(vals, b: int, ld: int | None = None) -> np.ndarray:
+def pack(vals, b: int, ld: int | None = None, chunk_rows: int = 256) -> np.ndarray:
     vals = np.asarray(vals)
     rows, cols = vals.shape
-    v = vals.astype(np.int64) & ((1 << b) - 1)
-    bitmat = ((v[:, :, None] >> np.arange(b)) & 1).astype(np.uint8)  # [rows][cols][b]
-    stream = bitmat.reshape(rows, cols * b)
-    packed = np.packbits(stream, axis=1, bitorder="little")
     nbytes = packed_row_bytes(cols, b)
     ld = nbytes if ld is None else ld
     if ld < nbytes:
         raise ValueError("row stride too small")
     out = np.zeros((rows, ld), dtype=np.uint8)
-    out[:, :nbytes] = packed
+    for r0 in range(0, rows, chunk_rows):
+        v = vals[r0:r0 + chunk_rows].astype(np.int64) & ((1 << b) - 1)
+        bitmat = ((v[:, :, None] >> np.arange(b)) & 1).astype(np.uint8)  # [rows][cols][b]
+        stream = bitmat.reshape(v.shape[0], cols * b)
+        out[r0:r0 + chunk_rows, :nbytes] = np.packbits(stream, axis=1, bitorder="little")
     return out
 
 
-def unpack(packed, cols: int, b: int) -> np.ndarray:
+def unpack(packed, cols: int, b: int, chunk_rows: int = 256) -> np.ndarray:
     """Unsigned field values [rows][cols] (int64)."""
     packed = np.asarray(packed, dtype=np.uint8)
     rows = packed.shape[0]
     nbytes = packed_row_bytes(cols, b)
-    stream = np.unpackbits(packed[:, :nbytes], axis=1, bitorder="little")[:, :cols * b]
-    bitmat = stream.reshape(rows, cols, b).astype(np.int64)
-    return (bitmat << np.arange(b)).sum(axis=2)
+    out = np.empty((rows, cols), dtype=np.int64)
+    weights = (1 << np.arange(b)).astype(np.int64)
+    for r0 in range(0, rows, chunk_rows):
+        stream = np.unpackbits(packed[r0:r0 + chunk_rows, :nbytes], axis=1,
+                               bitorder="little")[:, :cols * b]
+        bitmat = stream.reshape(stream.shape[0], cols, b).astype(np.int64)
+        out[r0:r0 + chunk_rows] = bitmat @ weights
+    return out
 
 
 def to_signed(u, b: int) -> np.ndarray:

@@ -1,0 +1,143 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before anything touches a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dequant_matmul_amd as fqm
+from conftest import ROOT
+
+E = dict(OK=0, NULL=1, ALIGN=2, SHAPE=3, FORMAT=4, WORKSPACE=5, UNSUPPORTED=6, HIP=7)
+FAKE = 0x7f0000000000  # a 16-byte-aligned address the host never dereferences
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fqm.LIB_PATH):
+        from dequant_matmul_amd import build
+        build.build()
+    return fqm.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fqm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(fqm_[a-z_]+)\s*\(", text))
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = declared_functions()
+    assert decl == set(fqm.SYMBOLS)
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert lib.fqm_version() == 1
+
+
+def test_status_strings(lib):
+    for code in E.values():
+        assert lib.fqm_status_str(code)
+    assert lib.fqm_status_str(99) == b"unknown status"
+
+
+def lut6(rows=64, cols=128, ld=96, packed=FAKE, lut=FAKE):
+    w = fqm._Weights()
+    w.format, w.rows, w.cols = fqm.FQM_LUT6, rows, cols
+    w.lut6.packed, w.lut6.lut, w.lut6.ld = packed, lut, ld
+    return w
+
+
+def gemv(lib, w, x=FAKE, y=FAKE, dt=0, batch=1, ws=None, wsb=0):
+    return lib.fqm_gemv(ctypes.byref(w), x, y, dt, batch, ws, wsb, None)
+
+
+def test_lut6_argument_errors(lib):
+    assert lib.fqm_gemv(None, FAKE, FAKE, 0, 1, None, 0, None) == E["NULL"]
+    assert gemv(lib, lut6(cols=100)) == E["SHAPE"]            # cols % 64
+    assert gemv(lib, lut6(ld=80)) == E["SHAPE"]               # ld < cols*3/4
+    assert gemv(lib, lut6(ld=104)) == E["ALIGN"]              # ld % 16
+    assert gemv(lib, lut6(packed=FAKE + 4)) == E["ALIGN"]
+    assert gemv(lib, lut6(lut=None)) == E["NULL"]
+    assert gemv(lib, lut6(), batch=0) == E["SHAPE"]
+    assert gemv(lib, lut6(), batch=17) == E["SHAPE"]
+    assert gemv(lib, lut6(), dt=5) == E["FORMAT"]
+    assert gemv(lib, lut6(), x=None) == E["NULL"]
+    assert gemv(lib, lut6(), y=FAKE + 2) == E["ALIGN"]
+    bad = lut6()
+    bad.format = 9
+    assert gemv(lib, bad) == E["FORMAT"]
+    assert gemv(lib, lut6(rows=-1)) == E["SHAPE"]
+    # empty work returns before any launch
+    assert gemv(lib, lut6(rows=0, packed=None, lut=None)) == E["OK"]
+    assert lib.fqm_gemm(ctypes.byref(lut6()), FAKE, FAKE, 0, None) == E["OK"]
+    assert lib.fqm_gemm(ctypes.byref(lut6()), FAKE, FAKE, -1, None) == E["SHAPE"]
+    assert lib.fqm_gemm(ctypes.byref(lut6()), None, FAKE, 4, None) == E["NULL"]
+
+
+def test_pack_argument_errors(lib):
+    assert lib.fqm_pack_bits(FAKE, FAKE, 4, 64, 3, 64, None, None) == E["FORMAT"]
+    assert lib.fqm_pack_bits(FAKE, FAKE, 4, 64, 6, 32, None, None) == E["SHAPE"]   # ld < 48
+    assert lib.fqm_pack_bits(FAKE, FAKE, 4, 64, 6, 56, None, None) == E["ALIGN"]
+    assert lib.fqm_pack_bits(FAKE, FAKE + 8, 4, 64, 6, 48, None, None) == E["ALIGN"]
+    assert lib.fqm_pack_bits(FAKE, None, 4, 64, 6, 48, None, None) == E["NULL"]
+    assert lib.fqm_pack_bits(FAKE, FAKE, 0, 64, 6, 48, None, None) == E["OK"]
+    assert lib.fqm_pack(FAKE, FAKE, -2, 64, 48, None, None) == E["SHAPE"]
+    assert lib.fqm_unpack(FAKE, FAKE, 4, 66, 64, None) == E["SHAPE"]
+
+
+def fabq(bs=128, n_hi=4, rows=64, cols=512):
+    w = fqm._Weights()
+    w.format, w.rows, w.cols = fqm.FQM_FABQ, rows, cols
+    f = w.fabq
+    f.blocksize, f.n_hi = bs, n_hi
+    f.row_of = f.q4 = f.s_hi = f.signs = f.s_blk = f.idx = f.codebook = FAKE
+    f.ld_q4, f.ld_signs, f.ld_idx = 256, 64, 16
+    return w
+
+
+def test_fabq_argument_errors(lib):
+    assert gemv(lib, fabq()) != E["FORMAT"]  # sanity: the base descriptor is valid
+    assert gemv(lib, fabq(bs=96)) == E["FORMAT"]
+    assert gemv(lib, fabq(bs=512, cols=768)) == E["SHAPE"]   # bs does not divide cols
+    assert gemv(lib, fabq(n_hi=65)) == E["SHAPE"]
+    w = fabq()
+    w.fabq.ld_signs = 48
+    assert gemv(lib, w) == E["SHAPE"]
+    w = fabq()
+    w.fabq.codebook = None
+    assert gemv(lib, w) == E["NULL"]
+    w = fabq(n_hi=64)  # no binary rows: their pointers are not needed
+    w.fabq.codebook = w.fabq.signs = None
+    assert lib.fqm_gemm(ctypes.byref(w), FAKE, FAKE, 1, None) == E["UNSUPPORTED"]
+    assert lib.fqm_workspace_size(ctypes.byref(fabq()), 4) == 0
+
+
+def mdbf(r=2000, l=2, P=1, n=4096, m=4096):
+    w = fqm._Weights()
+    w.format, w.rows, w.cols = fqm.FQM_MDBF, n, m
+    md = w.mdbf
+    md.r, md.l, md.P = r, l, P
+    for p in range(2):
+        q = md.path[p]
+        q.S_A = q.S_B = q.A_amp = q.B_amp = q.Q_U = q.Q_V = FAKE
+        q.ld_A, q.ld_B = 256, 512
+    return w
+
+
+def test_mdbf_argument_errors_and_workspace(lib):
+    w = mdbf()
+    need = lib.fqm_workspace_size(ctypes.byref(w), 16)
+    assert need == 16 * 2000 * 4
+    assert gemv(lib, w, batch=16, ws=None, wsb=0) == E["WORKSPACE"]
+    assert gemv(lib, w, batch=16, ws=FAKE, wsb=need - 4) == E["WORKSPACE"]
+    assert gemv(lib, mdbf(l=0)) == E["FORMAT"]
+    assert gemv(lib, mdbf(l=17)) == E["FORMAT"]
+    assert gemv(lib, mdbf(P=3)) == E["FORMAT"]
+    assert gemv(lib, mdbf(m=4100)) == E["SHAPE"]
+    w = mdbf()
+    w.mdbf.path[0].ld_A = 240   # < ceil(2000/8)
+    assert gemv(lib, w) == E["SHAPE"]
+    assert lib.fqm_workspace_size(ctypes.byref(mdbf(P=2)), 3) == 2 * 3 * 2000 * 4
+    assert lib.fqm_dequant(ctypes.byref(mdbf()), FAKE, None) == E["UNSUPPORTED"]
+    assert lib.fqm_gemm(ctypes.byref(mdbf()), FAKE, FAKE, 1, None) == E["UNSUPPORTED"]

@@ -1,0 +1,47 @@
+"""GPU parity for the MDBF two-pass double-binary GEMV."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_amd as fqm
+import oracle
+import synth
+from gpu_common import DEV, assert_close, bf16_dev, canaries_intact, guarded, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=None)
+def case(n, m, r, l, P, seed):
+    inp = synth.mdbf_input(n, m, r, l, P, seed)
+    return inp, oracle.mdbf.pack(inp)
+
+
+def weights(inp):
+    return fqm.MdbfWeights.from_arrays(inp.n, inp.m, inp.r, inp.l, inp.S_A, inp.S_B, inp.A_amp,
+                                       inp.B_amp, inp.Q_U, inp.Q_V, device=DEV)
+
+
+@pytest.mark.parametrize("batch", [1, 16])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_config_shape(batch, out):
+    inp, paths = case(4096, 4096, 2000, 2, 1, 6)
+    x = synth.activations(batch, 4096, 6)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    buf, y = guarded((batch, 4096), dt)
+    fqm.gemv(weights(inp), bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    yo = oracle.mdbf.gemv_factored(paths, x, 4096, 4096, 2000)
+    assert_close(to_f64(y), yo, out, f"b{batch}")
+
+
+@pytest.mark.parametrize("l,P", [(1, 1), (1, 2), (3, 1), (4, 2), (16, 1)])
+def test_variants(l, P):
+    n, m, r = 300, 512, 77
+    inp, paths = case(n, m, r, l, P, 60 + l + P)
+    x = synth.activations(5, m, 61)
+    y = fqm.gemv(weights(inp), bf16_dev(x), out_dtype=torch.float32)
+    assert_close(to_f64(y), oracle.mdbf.gemv_dense(paths, x, n, m, r), "f32", f"l={l} P={P}")
