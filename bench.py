@@ -1,0 +1,313 @@
+"""Benchmark of the fused low-bit dequant-matmul path on one MI355X.
+
+A step is one pass over every row of the path, each on its own seeded
+synthetic input already resident in HBM:
+
+  lut6_up_b1, lut6_down_b1   LUT6 GEMV, batch 1 (W 17408x5120 and 5120x17408)
+  lut6_up_b8, lut6_down_b8   LUT6 GEMV, batch 8
+  prefill                    LUT6 GEMM, X 2048x5120 times the up weights
+  fabq_b1, fabq_b8           FABQ-RC-style GEMV, 5120x5120, the layer's drawn blocksize
+  mdbf_b1, mdbf_b16          MDBF GEMV, n = m = 4096, r = 2000, l = 2, P = 1
+
+``value`` is the batch-1 LUT-GEMV effective bandwidth: algorithmic bytes of
+the up and down calls divided by their summed kernel time.  Weight tensors are
+rotated over several device copies so each call reads its weights from HBM,
+not from the 256 MB last-level cache.  Kernel times come from HIP events
+recorded on the launch stream around each call.
+
+``--profile ROW`` runs only ROW (for rocprofv3); ``--copy-calib MB`` runs a
+plain device copy of that size (the reference point for the HBM counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+METRIC = "LUT-GEMV effective HBM GB/s (% of peak) at batch 1; prefill GEMM TFLOP/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=4, help="device copies of each weight set")
+    ap.add_argument("--profile", default=None, help="run only this row (for rocprofv3)")
+    ap.add_argument("--copy-calib", type=float, default=0.0, help="MB of a plain device copy")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path is a single-GPU kernel library "
+              "(row sharding across GPUs is described in DESIGN.md but not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dequant_matmul_amd as fqm
+    import synth
+
+    fqm.load()  # fails loudly if the library is not built
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.copy_calib:
+        n = int(args.copy_calib * 1e6)
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n, "launches": args.steps}))
+        return
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t_gen = time.time()
+    C = synth.CONFIGS
+    rows = {}
+    need = None if args.profile is None else {args.profile}
+
+    def wanted(*names):
+        return need is None or any(n in need for n in names)
+
+    # ---- LUT6 weights (up, down), packed on the GPU, rotated copies --------------
+    lut6 = {}
+    lut6_inputs = {}
+    for name in ("up", "down"):
+        cfg = C[f"lut6_{name}"]
+        if not wanted(f"lut6_{name}_b1", f"lut6_{name}_b8", "prefill" if name == "up" else "-"):
+            continue
+        inp = synth.lut6_input(cfg["rows"], cfg["cols"], cfg["seed"])
+        lut6_inputs[name] = inp
+        w0 = fqm.Lut6Weights.from_codes(inp.codes, inp.lut, device=dev)
+        lut6[name] = [w0] + [w0.clone() for _ in range(args.copies - 1)]
+        for b in cfg["batches"]:
+            key = f"lut6_{name}_b{b}"
+            if not wanted(key):
+                continue
+            x = bf16(synth.activations(b, cfg["cols"], cfg["seed"]))
+            y = torch.empty((b, cfg["rows"]), dtype=torch.bfloat16, device=dev)
+            nbytes = w0.nbytes() + x.numel() * 2 + y.numel() * 2
+            off = 0 if b == 1 else args.copies // 2
+            rows[key] = dict(
+                fn=(lambda s, ws=lut6[name], x=x, y=y, off=off:
+                    fqm.gemv(ws[(s + off) % len(ws)], x, y=y)),
+                bytes=nbytes, flops=2 * b * cfg["rows"] * cfg["cols"], bound="hbm",
+                kernel=f"lut6_gemv batch {b}")
+    if wanted("prefill"):
+        M = C["prefill"]["M"]
+        ws = lut6["up"]
+        X = bf16(synth.activations(M, C["lut6_up"]["cols"], C["prefill"]["seed"]))
+        Y = torch.empty((M, C["lut6_up"]["rows"]), dtype=torch.bfloat16, device=dev)
+        Nn, K = C["lut6_up"]["rows"], C["lut6_up"]["cols"]
+        rows["prefill"] = dict(
+            fn=lambda s, ws=ws, X=X, Y=Y: fqm.gemm(ws[(s + 1) % len(ws)], X, Y=Y),
+            bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * K,
+            bound="mfma", kernel="lut6_gemm")
+
+    # ---- FABQ (5120^2, the layer's drawn blocksize) ------------------------------
+    fabq_bs = None
+    if wanted("fabq_b1", "fabq_b8"):
+        cfg = C["fabq"]
+        inp = synth.fabq_input(cfg["rows"], cfg["cols"], cfg["seed"])
+        fabq_bs = inp.blocksize
+        fcopies = [fqm.FabqWeights.from_arrays(inp.rows, inp.cols, inp.blocksize, inp.n_hi,
+                                               inp.row_of, inp.q4, inp.s_hi, inp.signs,
+                                               inp.s_blk, inp.idx, inp.codebook, device=dev)
+                   for _ in range(max(2, args.copies))]
+        for b in cfg["batches"]:
+            key = f"fabq_b{b}"
+            if not wanted(key):
+                continue
+            x = bf16(synth.activations(b, cfg["cols"], cfg["seed"]))
+            y = torch.empty((b, cfg["rows"]), dtype=torch.bfloat16, device=dev)
+            rows[key] = dict(fn=lambda s, ws=fcopies, x=x, y=y: fqm.gemv(ws[s % len(ws)], x, y=y),
+                             bytes=fcopies[0].nbytes() + x.numel() * 2 + y.numel() * 2,
+                             flops=2 * b * cfg["rows"] * cfg["cols"], bound="alu",
+                             kernel=f"fabq_gemv batch {b}")
+
+    # ---- MDBF (n = m = 4096, r = 2000, l = 2, P = 1) ------------------------------
+    if wanted("mdbf_b1", "mdbf_b16"):
+        cfg = C["mdbf"]
+        inp = synth.mdbf_input(cfg["n"], cfg["m"], cfg["r"], cfg["l"], cfg["P"], cfg["seed"])
+        mcopies = [fqm.MdbfWeights.from_arrays(inp.n, inp.m, inp.r, inp.l, inp.S_A, inp.S_B,
+                                               inp.A_amp, inp.B_amp, inp.Q_U, inp.Q_V, device=dev)
+                   for _ in range(max(2, args.copies))]
+        for b in cfg["batches"]:
+            key = f"mdbf_b{b}"
+            if not wanted(key):
+                continue
+            x = bf16(synth.activations(b, cfg["m"], cfg["seed"]))
+            y = torch.empty((b, cfg["n"]), dtype=torch.bfloat16, device=dev)
+            wsp = torch.empty(fqm.workspace_size(mcopies[0], b), dtype=torch.uint8, device=dev)
+            rows[key] = dict(
+                fn=lambda s, ws=mcopies, x=x, y=y, wsp=wsp: fqm.gemv(ws[s % len(ws)], x, y=y, workspace=wsp),
+                bytes=mcopies[0].nbytes() + x.numel() * 2 + y.numel() * 2,
+                flops=2 * b * 2 * cfg["l"] * cfg["r"] * (cfg["n"] + cfg["m"]), bound="alu",
+                kernel=f"mdbf_gemv batch {b} (2 launches)")
+    t_gen = time.time() - t_gen
+    if args.profile and args.profile not in rows:
+        print(f"unknown row {args.profile}; rows: {sorted(rows)}", file=sys.stderr)
+        sys.exit(2)
+
+    order = list(rows)
+    stream = torch.cuda.current_stream()
+
+    def step(s, events=None, e=0):
+        for k in order:
+            if events is not None:
+                events[k][0][e].record(stream)
+            rows[k]["fn"](s)
+            if events is not None:
+                events[k][1][e].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    K = args.steps
+    events = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
+                  [torch.cuda.Event(enable_timing=True) for _ in range(K)]) for k in order}
+    t0 = time.perf_counter()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for s in range(K):
+        step(args.warmup + s, events, s)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = t_start.elapsed_time(t_end) / K
+
+    if args.profile:
+        print(json.dumps({"profile": args.profile, "steps": K, "ms_per_step": ms_per_step}))
+        return
+
+    res = {}
+    for k in order:
+        ts = np.array([events[k][0][s].elapsed_time(events[k][1][s]) for s in range(K)])
+        r = rows[k]
+        med = float(np.median(ts))
+        res[k] = dict(kernel=r["kernel"], us_mean=float(ts.mean() * 1e3), us_median=med * 1e3,
+                      us_p10=float(np.percentile(ts, 10) * 1e3), us_p90=float(np.percentile(ts, 90) * 1e3),
+                      bytes=r["bytes"], flops=r["flops"],
+                      gbs=r["bytes"] / (ts.mean() * 1e-3) / 1e9,
+                      tflops=r["flops"] / (ts.mean() * 1e-3) / 1e12)
+        res[k]["frac_hbm"] = res[k]["gbs"] / HBM_PEAK_GBS
+        if r["bound"] == "mfma":
+            res[k]["frac_mfma"] = res[k]["tflops"] / BF16_PEAK_TFLOPS
+
+    b1 = [k for k in ("lut6_up_b1", "lut6_down_b1") if k in res]
+    tot_bytes = sum(res[k]["bytes"] for k in b1)
+    tot_s = sum(res[k]["us_mean"] for k in b1) * 1e-6
+    value = tot_bytes / tot_s / 1e9
+
+    roofline = dict(bound="hbm", achieved=round(value, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(value / HBM_PEAK_GBS, 4), traffic=traffic_record(),
+                    kernel="lut6_gemv batch 1 (up and down launches)",
+                    bytes_per_launch={k: res[k]["bytes"] for k in b1})
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(lut6_inputs, rows, res, fqm, bf16, dev)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": "LUT6 GEMV batch 1 over a 27B-class MLP pair: W up 17408x5120 and "
+                        "down 5120x17408, 6-bit codes packed 4 per 3 bytes + 64-entry bf16 "
+                        "table per row, bf16 x and y, fp32 accumulate",
+            "weight_copies_rotated": args.copies,
+            "fabq_blocksize": fabq_bs,
+        },
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "prefill_gemm_tflops": round(res["prefill"]["tflops"], 1) if "prefill" in res else None,
+        "prefill_frac_of_bf16_peak": round(res["prefill"]["frac_mfma"], 4) if "prefill" in res else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": {k: {kk: (round(v, 3) if isinstance(v, float) else v) for kk, v in d.items()}
+                 for k, d in res.items()},
+        "setup_s": round(t_gen, 1), "timed_wall_s": round(wall, 3),
+    }
+    print(json.dumps(out))
+
+
+def traffic_record():
+    """HBM traffic per launch of the batch-1 LUT6 GEMV from rocprofv3 counters,
+    if the committed counter summary was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "lut6_gemv_b1_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_sha():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("lut6_gemv.hip", "fqm_internal.h"):
+        h.update(open(os.path.join(ROOT, "dequant_matmul_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def cpu_baseline(lut6_inputs, rows, res, fqm, bf16, dev):
+    """The oracle (numpy fp64: unpack, decode, product) on the host cores, on
+    the batch-1 up and down layers once each; also checks the GPU result of
+    those calls against it."""
+    import torch
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    C = synth.CONFIGS
+    tot_bytes, tot_t, parity = 0, 0.0, {}
+    for name, inp in lut6_inputs.items():
+        key = f"lut6_{name}_b1"
+        if key not in rows:
+            continue
+        cfg = C[f"lut6_{name}"]
+        x = synth.activations(1, cfg["cols"], cfg["seed"])
+        packed = oracle.lut6.pack_codes(inp.codes)  # input preparation, not timed
+        t0 = time.perf_counter()
+        yo = oracle.lut6.gemv(packed, inp.lut, x, cfg["cols"])
+        tot_t += time.perf_counter() - t0
+        tot_bytes += rows[key]["bytes"]
+        w = fqm.Lut6Weights.from_codes(inp.codes, inp.lut, device=dev)
+        y = fqm.gemv(w, bf16(x)).float().cpu().numpy().astype(np.float64)
+        ok, m = oracle.compare.check(y, yo, "bf16")
+        parity[key] = dict(ok=ok, rel_l2=m["rel_l2"], max_rel=m["max_rel"])
+    if not tot_bytes:
+        return None
+    return dict(value=round(tot_bytes / tot_t / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
+                sample="one batch-1 call each of the up (17408x5120) and down (5120x17408) "
+                       "layers: numpy fp64 unpack + decode + matmul; cores = BLAS threads "
+                       "(unpack and decode run on one thread)",
+                seconds=round(tot_t, 3), cpu=platform.processor() or platform.machine(),
+                parity_vs_gpu=parity)
+
+
+if __name__ == "__main__":
+    main()
