@@ -11,9 +11,10 @@ synthetic input already resident in HBM:
 
 ``value`` is the batch-1 LUT-GEMV effective bandwidth: algorithmic bytes of
 the up and down calls divided by their summed kernel time.  Weight tensors are
-rotated over several device copies so each call reads its weights from HBM,
-not from the 256 MB last-level cache.  Kernel times come from HIP events
-recorded on the launch stream around each call.
+rotated over enough device copies (1.2 GB per weight set by default) that each
+call reads its weights from HBM, not from the 256 MB last-level cache.  Each
+row's K calls run back to back between two HIP events recorded on the launch
+stream; a row's time is the average call duration in that stream.
 
 ``--profile ROW`` runs only ROW (for rocprofv3); ``--copy-calib MB`` runs a
 plain device copy of that size (the reference point for the HBM counters).
@@ -43,7 +44,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--copies", type=int, default=4, help="device copies of each weight set")
+    ap.add_argument("--rotate-gb", type=float, default=1.2,
+                    help="each weight set is copied until the copies exceed this many GB, so "
+                         "successive calls read HBM rather than the 256 MB last-level cache")
     ap.add_argument("--profile", default=None, help="run only this row (for rocprofv3)")
     ap.add_argument("--copy-calib", type=float, default=0.0, help="MB of a plain device copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -78,6 +81,9 @@ def main():
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
+    def n_copies(w):
+        return max(2, int(np.ceil(args.rotate_gb * 1e9 / w.nbytes())))
+
     t_gen = time.time()
     C = synth.CONFIGS
     rows = {}
@@ -96,7 +102,7 @@ def main():
         inp = synth.lut6_input(cfg["rows"], cfg["cols"], cfg["seed"])
         lut6_inputs[name] = inp
         w0 = fqm.Lut6Weights.from_codes(inp.codes, inp.lut, device=dev)
-        lut6[name] = [w0] + [w0.clone() for _ in range(args.copies - 1)]
+        lut6[name] = [w0] + [w0.clone() for _ in range(n_copies(w0) - 1)]
         for b in cfg["batches"]:
             key = f"lut6_{name}_b{b}"
             if not wanted(key):
@@ -104,7 +110,7 @@ def main():
             x = bf16(synth.activations(b, cfg["cols"], cfg["seed"]))
             y = torch.empty((b, cfg["rows"]), dtype=torch.bfloat16, device=dev)
             nbytes = w0.nbytes() + x.numel() * 2 + y.numel() * 2
-            off = 0 if b == 1 else args.copies // 2
+            off = 0 if b == 1 else len(lut6[name]) // 2
             rows[key] = dict(
                 fn=(lambda s, ws=lut6[name], x=x, y=y, off=off:
                     fqm.gemv(ws[(s + off) % len(ws)], x, y=y)),
@@ -127,10 +133,10 @@ def main():
         cfg = C["fabq"]
         inp = synth.fabq_input(cfg["rows"], cfg["cols"], cfg["seed"])
         fabq_bs = inp.blocksize
-        fcopies = [fqm.FabqWeights.from_arrays(inp.rows, inp.cols, inp.blocksize, inp.n_hi,
-                                               inp.row_of, inp.q4, inp.s_hi, inp.signs,
-                                               inp.s_blk, inp.idx, inp.codebook, device=dev)
-                   for _ in range(max(2, args.copies))]
+        f0 = fqm.FabqWeights.from_arrays(inp.rows, inp.cols, inp.blocksize, inp.n_hi,
+                                         inp.row_of, inp.q4, inp.s_hi, inp.signs,
+                                         inp.s_blk, inp.idx, inp.codebook, device=dev)
+        fcopies = [f0] + [f0.clone() for _ in range(n_copies(f0) - 1)]
         for b in cfg["batches"]:
             key = f"fabq_b{b}"
             if not wanted(key):
@@ -146,9 +152,9 @@ def main():
     if wanted("mdbf_b1", "mdbf_b16"):
         cfg = C["mdbf"]
         inp = synth.mdbf_input(cfg["n"], cfg["m"], cfg["r"], cfg["l"], cfg["P"], cfg["seed"])
-        mcopies = [fqm.MdbfWeights.from_arrays(inp.n, inp.m, inp.r, inp.l, inp.S_A, inp.S_B,
-                                               inp.A_amp, inp.B_amp, inp.Q_U, inp.Q_V, device=dev)
-                   for _ in range(max(2, args.copies))]
+        m0 = fqm.MdbfWeights.from_arrays(inp.n, inp.m, inp.r, inp.l, inp.S_A, inp.S_B,
+                                         inp.A_amp, inp.B_amp, inp.Q_U, inp.Q_V, device=dev)
+        mcopies = [m0] + [m0.clone() for _ in range(n_copies(m0) - 1)]
         for b in cfg["batches"]:
             key = f"mdbf_b{b}"
             if not wanted(key):
@@ -169,27 +175,29 @@ def main():
     order = list(rows)
     stream = torch.cuda.current_stream()
 
-    def step(s, events=None, e=0):
-        for k in order:
-            if events is not None:
-                events[k][0][e].record(stream)
-            rows[k]["fn"](s)
-            if events is not None:
-                events[k][1][e].record(stream)
-
+    # Warm-up: W passes over every row.
     for s in range(args.warmup):
-        step(s)
+        for k in order:
+            rows[k]["fn"](s)
     torch.cuda.synchronize()
+
+    # Timed region: K passes over the path.  Each row's K calls run back to
+    # back between two HIP events recorded on the launch stream, so the
+    # per-call time is the row's average launch duration in a stream of calls
+    # (what a decode loop sees), weights rotating across device copies.
     K = args.steps
-    events = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
-                  [torch.cuda.Event(enable_timing=True) for _ in range(K)]) for k in order}
-    t0 = time.perf_counter()
+    ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for k in order}
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
-    for s in range(K):
-        step(args.warmup + s, events, s)
+    for k in order:
+        ev[k][0].record(stream)
+        for s in range(K):
+            rows[k]["fn"](args.warmup + s)
+        ev[k][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -201,21 +209,17 @@ def main():
 
     res = {}
     for k in order:
-        ts = np.array([events[k][0][s].elapsed_time(events[k][1][s]) for s in range(K)])
         r = rows[k]
-        med = float(np.median(ts))
-        res[k] = dict(kernel=r["kernel"], us_mean=float(ts.mean() * 1e3), us_median=med * 1e3,
-                      us_p10=float(np.percentile(ts, 10) * 1e3), us_p90=float(np.percentile(ts, 90) * 1e3),
-                      bytes=r["bytes"], flops=r["flops"],
-                      gbs=r["bytes"] / (ts.mean() * 1e-3) / 1e9,
-                      tflops=r["flops"] / (ts.mean() * 1e-3) / 1e12)
+        us = ev[k][0].elapsed_time(ev[k][1]) * 1e3 / K
+        res[k] = dict(kernel=r["kernel"], us_per_call=us, bytes=r["bytes"], flops=r["flops"],
+                      gbs=r["bytes"] / (us * 1e-6) / 1e9, tflops=r["flops"] / (us * 1e-6) / 1e12)
         res[k]["frac_hbm"] = res[k]["gbs"] / HBM_PEAK_GBS
         if r["bound"] == "mfma":
             res[k]["frac_mfma"] = res[k]["tflops"] / BF16_PEAK_TFLOPS
 
     b1 = [k for k in ("lut6_up_b1", "lut6_down_b1") if k in res]
     tot_bytes = sum(res[k]["bytes"] for k in b1)
-    tot_s = sum(res[k]["us_mean"] for k in b1) * 1e-6
+    tot_s = sum(res[k]["us_per_call"] for k in b1) * 1e-6
     value = tot_bytes / tot_s / 1e9
 
     roofline = dict(bound="hbm", achieved=round(value, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -235,7 +239,7 @@ def main():
             "workload": "LUT6 GEMV batch 1 over a 27B-class MLP pair: W up 17408x5120 and "
                         "down 5120x17408, 6-bit codes packed 4 per 3 bytes + 64-entry bf16 "
                         "table per row, bf16 x and y, fp32 accumulate",
-            "weight_copies_rotated": args.copies,
+            "weight_rotation_gb": args.rotate_gb,
             "fabq_blocksize": fabq_bs,
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),

@@ -275,6 +275,11 @@ class FabqWeights(_WeightsBase):
                    t16(np.asarray(s_blk).reshape(n_lo, nb)).view(torch.float16), idx_p,
                    t16(codebook).view(torch.float16))
 
+    def clone(self):
+        t = {k: v.clone() for k, v in self.tensors.items()}
+        return FabqWeights(self.rows, self.cols, self.blocksize, self.n_hi, t["row_of"], t["q4"],
+                           t["s_hi"], t["signs"], t["s_blk"], t["idx"], t["codebook"])
+
     def nbytes(self) -> int:
         """Algorithmic bytes: int4 rows + scales, sign bits + block scales +
         4-bit indices, codebook and row map (all unpadded)."""
@@ -318,6 +323,10 @@ class MdbfWeights(_WeightsBase):
             paths.append(dict(S_A=sa, S_B=sb, A_amp=t16(A_amp[p]), B_amp=t16(B_amp[p]),
                               Q_U=t16(Q_U[p]), Q_V=t16(Q_V[p])))
         return cls(n, m, r, l, paths)
+
+    def clone(self):
+        return MdbfWeights(self.rows, self.cols, self.r, self.l,
+                           [{k: v.clone() for k, v in t.items()} for t in self.paths])
 
     def nbytes(self) -> int:
         """Algorithmic bytes: sign bits (unpadded) + fp16 envelopes, all paths."""

@@ -37,6 +37,25 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Sum over the 64 lanes with DPP moves only (no LDS traffic); the total is
+// exact in lane 63 only.  Steps: pairs and quads (quad_perm), 8 lanes
+// (row_half_mirror), 16 lanes (row_mirror), then row 0 -> 1 and 2 -> 3
+// (row_bcast:15 into rows 1 and 3) and rows 0-1 -> 2-3 (row_bcast:31 into
+// rows 2 and 3).  Rows left out of a broadcast add zero.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+    v += dpp_or_zero<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v += dpp_or_zero<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v += dpp_or_zero<0x141, 0xF>(v);  // row_half_mirror
+    v += dpp_or_zero<0x140, 0xF>(v);  // row_mirror
+    v += dpp_or_zero<0x142, 0xA>(v);  // row_bcast:15
+    v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast:31
+    return v;
+}
+
 // The 16 six-bit codes of a 12-byte piece (three little-endian dwords):
 // code j sits at bits [6j, 6j+6) of the 96-bit value.
 __device__ __forceinline__ void codes16(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t c[16]) {

@@ -128,3 +128,51 @@ def test_gemv_zero_cols_and_padded_rows():
     x = synth.activations(2, 1088, 7)
     y = fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32)
     assert_close(to_f64(y), oracle.lut6.gemv(packed, inp.lut, x, 1088), "f32")
+
+
+# Batch-1 shapes with cols a multiple of 1024 (the cell-streaming kernel):
+# one cell per row with fewer rows than workgroups (most waves idle), rows
+# not dividing the grid, 16 cells per row, and a row count that makes the
+# launcher double the grid (rows split 5/6 per workgroup).
+B1_SHAPES = [(77, 1024, 9), (1000, 3072, 8), (513, 2048, 12), (600, 16384, 10), (5200, 17408, 13)]
+
+
+@pytest.mark.parametrize("rows,cols,seed", B1_SHAPES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemv_b1_cells(rows, cols, seed, out):
+    inp, packed = lut6_case(rows, cols, seed)
+    w = lut6_weights(rows, cols, seed)
+    x = synth.activations(1, cols, seed)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    buf, y = guarded((1, rows), dt)
+    fqm.gemv(w, bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.lut6.gemv(packed, inp.lut, x, cols), out, f"{rows}x{cols} {out}")
+
+
+def test_gemv_b1_exact_invariants():
+    rows, cols, seed = 1000, 3072, 8
+    inp, _ = lut6_case(rows, cols, seed)
+    w = lut6_weights(rows, cols, seed)
+    lv = oracle.numerics.bf16_to_f64(inp.lut)
+    for k in (0, 1023, 1024, 2047 + 17, cols - 1):
+        x = np.zeros((1, cols), np.uint16)
+        x[0, k] = 0x3F80
+        y = fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32)
+        assert np.array_equal(to_f64(y)[0], lv[np.arange(rows), inp.codes[:, k]]), k
+    x = synth.activations(1, cols, seed)
+    y = to_f64(fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32))
+    # Mirrored codes negate every weight.  This path accumulates with
+    # v_dot2_f32_bf16, whose rounding is not symmetric under negation, so the
+    # negation holds to within accumulated rounding (a few fp32 ulps per
+    # step), not bit for bit.
+    wm = fqm.Lut6Weights.from_codes(63 - inp.codes, inp.lut, device=DEV)
+    ym = to_f64(fqm.gemv(wm, bf16_dev(x), out_dtype=torch.float32))
+    assert np.linalg.norm(ym + y) <= 1e-5 * np.linalg.norm(y)
+    x4 = x.astype(np.uint32) + (2 << 7)
+    x4 = np.where((x & 0x7FFF) == 0, x, x4).astype(np.uint16)
+    assert np.array_equal(to_f64(fqm.gemv(w, bf16_dev(x4), out_dtype=torch.float32)), 4 * y)
+    # the same call twice gives the same bits (partial rows combine in a fixed order)
+    y2 = to_f64(fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32))
+    assert np.array_equal(y, y2)
