@@ -73,26 +73,6 @@ __global__ __launch_bounds__(256) void lut6_gemv_generic(const uint8_t* __restri
     }
 }
 
-// ---------------------------------------------------------------------------
-// Batch 1, cols a multiple of 1024.
-//
-// A "cell" is 1024 consecutive weights of one row: 64 lanes x one 12-byte
-// piece (16 codes) each, 768 contiguous bytes, so a cell is one fully
-// coalesced load instruction.  Workgroup g owns rows [g*rows/G, (g+1)*rows/G)
-// (at least one row per wave); it stages x (cols bf16) and its rows' tables
-// (128 B each) in LDS once, and its waves split the group's cells, taken row
-// by row, into equal contiguous ranges of at most NC cells, so no row spans
-// more than two waves.  A wave issues the loads of all its cells at once
-// (its only HBM traffic) and then works through them in order with no
-// branches, so the compiler can overlap one cell's gathers with the next
-// cell's address arithmetic.  Per cell a lane does 16 gathers from the row's
-// table (one row per instruction: lanes hit distinct banks or share a
-// dword), pairs them, and meets the matching x pair in v_dot2_f32_bf16 (fp32
-// accumulate).  Each lane stores its running sum into an LDS partial slot
-// when a row ends (into a discard slot otherwise); after a barrier every row
-// adds its two slots per lane and reduces across the wave with DPP, in a
-// fixed order, so the result does not depend on timing.
-// ---------------------------------------------------------------------------
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -120,116 +100,90 @@ __device__ __forceinline__ uint32_t code_x2(uint32_t d0, uint32_t d1, uint32_t d
     else return d2 >> (bit - 65);
 }
 
-constexpr int kB1Waves = 8;    // waves per workgroup (2 per SIMD; two groups per CU)
-constexpr int kB1Cells = 22;   // most cells per wave
-constexpr int kB1Ring = 8;     // cells in flight per wave
-constexpr int kB1Stage = 5;    // 16-byte staging pieces per thread (x and tables)
-
-template <int NC, int D, int CPR>
-__global__ __launch_bounds__(64 * kB1Waves) __attribute__((amdgpu_waves_per_eu(4))) void lut6_gemv_b1(
-    const uint8_t* __restrict__ packed, int64_t ld, const uint16_t* __restrict__ lut,
-    const uint16_t* __restrict__ x, void* __restrict__ y, int y_f32, int rq, int rr) {
-    // Workgroup g owns R = rq (+1 for g < rr) rows starting at r0; its cells,
-    // row by row, go to the kB1Waves waves in equal contiguous ranges.
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int nw = kB1Waves;
-    constexpr int cpr = CPR;  // cells per row = cols / 1024
-    constexpr int cols = 1024 * CPR;
+// ---------------------------------------------------------------------------
+// Batch 1, cols a multiple of 1024.  A row is CPR chunks of 1024 weights; in
+// chunk c lane i owns the 12-byte piece i (16 codes, bytes [768c + 12i, +12)
+// of the row: one fully coalesced 768-byte load per chunk) and the matching
+// 16 x values (32 bytes, read from L2).  Each row is split over S waves
+// (wave s takes chunks [s*CPR/S, (s+1)*CPR/S)); a workgroup holds WPG waves,
+// i.e. WPG/S rows.  Codes are requested PC chunks ahead and x PX chunks
+// ahead, every load unconditional within the unrolled chunk loop, so the
+// compiler's waits are exact.  A wave's row table sits in its own LDS slot
+// at a compile-time offset, so a code becomes a gather address in two VALU
+// ops (shift, mask) and all 64 lanes of a gather read one 128-byte table
+// (distinct banks or a shared dword).  Two gathered bf16 are paired
+// (v_perm_b32) and meet the x pair in v_dot2_f32_bf16 (fp32 accumulate).
+// Each wave reduces its partial row sum once with DPP; with S > 1 the S
+// partials are added in wave order through LDS, so the result does not
+// depend on timing.
+// ---------------------------------------------------------------------------
+template <int CPR, int S, int WPG, int PC>
+__global__ __launch_bounds__(64 * WPG) void lut6_gemv_rows(const uint8_t* __restrict__ packed,
+                                                           int64_t ld,
+                                                           const uint16_t* __restrict__ lut,
+                                                           const uint16_t* __restrict__ x,
+                                                           void* __restrict__ y, int y_f32,
+                                                           int rows) {
+    constexpr int RPG = WPG / S;                           // rows per workgroup
+    constexpr int NCH = (CPR + S - 1) / S;                 // most chunks per wave
+    constexpr int NX = CPR * 128;                          // x in 16-byte pieces
+    constexpr int XS = (NX + 64 * WPG - 1) / (64 * WPG);   // staging pieces per thread
+    __shared__ __attribute__((aligned(16))) u32x4_t s_x[NX];
+    __shared__ __attribute__((aligned(16))) uint32_t s_tab[WPG][32];
+    __shared__ float s_part[WPG];
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = blockIdx.x;
-    const int r0 = g * rq + min(g, rr);
-    const int R = rq + (g < rr ? 1 : 0);
-    const int C = R * cpr;
-    const int cb = (w * C) / nw, ce = ((w + 1) * C) / nw;
-    const int n = ce - cb;  // cells of this wave, cpr..NC
-    const int rl0 = cb / cpr, cj0 = cb - rl0 * cpr;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rr = wv / S, sp = wv - rr * S;   // row within the group, split index
+    const int row_u = blockIdx.x * RPG + rr;
+    const int row = min(row_u, rows - 1);  // rows past the end repeat the last row (not stored)
+    const int cs = (sp * CPR) / S, n = ((sp + 1) * CPR) / S - cs;  // this wave's chunks [cs, cs + n)
+    const uint8_t* rowp = packed + (int64_t)row * ld + 768 * cs + 12 * lane;
 
-    // LDS: x [cols] bf16 (swizzled, see staging) | tables [R][64] bf16 |
-    //      partials [R][2][64] fp32 | discard slots [nw][64] fp32
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
-    const uint32_t x_off = lds0;
-    const uint32_t tab_off = lds0 + (uint32_t)(cols * 2);
-    const uint32_t part_off = tab_off + (uint32_t)R * 128u;
-    const uint32_t drop_off = part_off + (uint32_t)R * 512u + (uint32_t)w * 256u;
-
-    // Staging loads for x and the tables go out first (kB1Stage 16-byte
-    // pieces per thread), then the cell loads; the staging stores below then
-    // wait only for the staging loads.
-    const int nx = (int)(cols >> 3), nst = nx + R * 8;
-    const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(x);
-    const u32x4_t* ts = reinterpret_cast<const u32x4_t*>(lut + r0 * 64);
-    u32x4_t stage[kB1Stage];
+    // x staging loads and the table load go out first, then the first PC
+    // chunks of codes; the LDS stores below wait only for the former.
+    u32x4_t xs[XS];
 #pragma unroll
-    for (int u = 0; u < kB1Stage; ++u) {
-        const int k = min(tid + u * (64 * nw), nst - 1);  // clamped: no branches
-        stage[u] = *(k < nx ? xs + k : ts + (k - nx));
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the staging loads ahead of the cell loads
-
-    // Per-cell bookkeeping, computed once: lane e (< NC) holds the values of
-    // the wave's cell e, and each cell reads them with v_readlane.  (Done per
-    // cell in scalar code this is ~30 SALU instructions a cell, and the CU's
-    // scalar pipe, shared by its waves, becomes the bottleneck.)
-    // Cell e is column block (cj0 + e) % cpr of row rl0 + (cj0 + e) / cpr;
-    // cells past n stand for the last cell (its bytes are read again, an L2
-    // hit; its sum is discarded), so every load is issued unconditionally and
-    // every wait is exact.
-    const uint8_t* wbase = packed + (int64_t)(r0 + rl0) * ld + 768 * cj0;  // wave-uniform
-    const uint32_t lofs = 12u * lane;
-    uint32_t t_load, t_base, t_xoff, t_dst;
-    float t_keep;
-    {
-        const int e = min(lane, n - 1);
-        const int t = cj0 + e, rl = rl0 + t / cpr, cj = t % cpr;
-        t_load = (uint32_t)(t / cpr) * (uint32_t)ld + 768u * (uint32_t)(cj - cj0);
-        t_base = tab_off + (uint32_t)rl * 128u;
-        t_xoff = x_off + (uint32_t)cj * 2048u;
-        const bool end = lane < n && (cj == cpr - 1 || lane == n - 1);
-        const uint32_t sl = (rl == rl0 && cj0 != 0) ? 1u : 0u;
-        t_dst = end ? part_off + ((uint32_t)rl * 2u + sl) * 256u : drop_off;
-        t_keep = end ? 0.f : 1.f;
-    }
-    auto cell_ptr = [&](int e) {
-        return reinterpret_cast<const uint32_t*>(wbase + __builtin_amdgcn_readlane(t_load, e) + lofs);
-    };
-    // A window of D cells is in flight per wave: cell e + D is requested as
-    // soon as cell e's codes have been turned into addresses, so requests
-    // go out (and return) roughly in cell order.
-    uint32_t ring[D][3];
-#pragma unroll
-    for (int e = 0; e < D; ++e) {
-        const uint32_t* q = cell_ptr(e);
-        ring[e][0] = __builtin_nontemporal_load(q);
-        ring[e][1] = __builtin_nontemporal_load(q + 1);
-        ring[e][2] = __builtin_nontemporal_load(q + 2);
-    }
+    for (int u = 0; u < XS; ++u)
+        xs[u] = reinterpret_cast<const u32x4_t*>(x)[min(tid + u * 64 * WPG, NX - 1)];
+    const uint32_t tv = reinterpret_cast<const uint32_t*>(lut + (int64_t)row * 64)[lane & 31];
     __builtin_amdgcn_sched_barrier(0);
 
-    {
-        u32x4_t* dst = reinterpret_cast<u32x4_t*>(smem);
+    uint32_t cr[PC + 1][3];
+    // chunk c of this wave (c < NCH); c >= n repeats the wave's last chunk
+    auto load_codes = [&](int c) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(rowp + 768 * min(c, n - 1));
+        cr[c % (PC + 1)][0] = __builtin_nontemporal_load(q);
+        cr[c % (PC + 1)][1] = __builtin_nontemporal_load(q + 1);
+        cr[c % (PC + 1)][2] = __builtin_nontemporal_load(q + 2);
+    };
 #pragma unroll
-        for (int u = 0; u < kB1Stage; ++u) {
-            // x piece p = 64*cj + lane (32 bytes, halves h = 0, 1) goes to
-            // 16-byte slot cj*128 + h*64 + lane, so that each of a cell's two
-            // x reads covers 1 KB of consecutive LDS (no bank conflicts).
-            const int k = min(tid + u * (64 * nw), nst - 1);
-            const int slot = k < nx ? (((k >> 7) << 7) | ((k & 1) << 6) | ((k >> 1) & 63)) : k;
-            dst[slot] = stage[u];  // clamped duplicates store equal values
-        }
+    for (int c = 0; c < PC && c < NCH; ++c) load_codes(c);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // x piece p = 64*cj + l (32 bytes = 16-byte halves h = 0, 1) goes to
+    // slot cj*128 + h*64 + l, so that each half-read of a chunk covers 1 KB of
+    // consecutive LDS (no bank conflicts).
+#pragma unroll
+    for (int u = 0; u < XS; ++u) {
+        const int k = min(tid + u * 64 * WPG, NX - 1);
+        s_x[((k >> 7) << 7) | ((k & 1) << 6) | ((k >> 1) & 63)] = xs[u];  // clamped duplicates store equal values
     }
+    if (lane < 32) s_tab[wv][lane] = tv;
     __syncthreads();
 
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_u8*)s_tab + 128u * wv;  // multiple of 128
     uint32_t mask = 0x7Eu;
-    asm volatile("" : "+v"(mask));  // keep the mask in a VGPR: v_and_or_b32 takes no literal
+    asm volatile("" : "+v"(mask));  // in a VGPR: (code & mask) | base is one v_and_or_b32
+    const uint32_t xb = (uint32_t)(uintptr_t)(lds_u8*)s_x + 2048u * cs + 16u * lane;
     float acc0 = 0.f, acc1 = 0.f;
-    // Cell d of this wave is column block cj = (cj0 + d) % cpr of row
-    // rl0 + (cj0 + d) / cpr.  Slots past n hold the last cell again: they are
-    // computed like the others (no branch) and their sums are discarded.
 #pragma unroll
-    for (int d = 0; d < NC; ++d) {
-        const uint32_t base = __builtin_amdgcn_readlane(t_base, d);
-        const uint32_t d0 = ring[d % D][0], d1 = ring[d % D][1], d2 = ring[d % D][2];
+    for (int c = 0; c < NCH; ++c) {
+        if (c + PC < NCH) load_codes(c + PC);
+        const uint32_t cc = (uint32_t)min(c, n - 1);
+        const u32x4_t xl = *(lds_u4*)(uintptr_t)(xb + 2048u * cc);
+        const u32x4_t xh = *(lds_u4*)(uintptr_t)(xb + 2048u * cc + 1024u);
+        const uint32_t xv[8] = {xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]};
+        const uint32_t d0 = cr[c % (PC + 1)][0], d1 = cr[c % (PC + 1)][1], d2 = cr[c % (PC + 1)][2];
         uint32_t a[16];
         a[0] = (code_x2<0>(d0, d1, d2) & mask) | base;
         a[1] = (code_x2<1>(d0, d1, d2) & mask) | base;
@@ -247,55 +201,55 @@ __global__ __launch_bounds__(64 * kB1Waves) __attribute__((amdgpu_waves_per_eu(4
         a[13] = (code_x2<13>(d0, d1, d2) & mask) | base;
         a[14] = (code_x2<14>(d0, d1, d2) & mask) | base;
         a[15] = (code_x2<15>(d0, d1, d2) & mask) | base;
-        if (d + D < NC) {  // compile-time condition: refill this slot with cell d + D
-            const uint32_t* q = cell_ptr(d + D);
-            ring[d % D][0] = __builtin_nontemporal_load(q);
-            ring[d % D][1] = __builtin_nontemporal_load(q + 1);
-            ring[d % D][2] = __builtin_nontemporal_load(q + 2);
-        }
-        // x pairs of this lane's piece (halves 1 KB apart, see the staging)
-        const uint32_t xa = __builtin_amdgcn_readlane(t_xoff, d) + 16u * lane;
-        const u32x4_t xl = *(lds_u4*)(uintptr_t)xa, xh = *(lds_u4*)(uintptr_t)(xa + 1024);
-        const uint32_t xv[8] = {xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]};
+        float p0 = 0.f, p1 = 0.f;
+        float& s0 = (NCH * S == CPR) ? acc0 : p0;  // uneven split: the repeated chunk is dropped
+        float& s1 = (NCH * S == CPR) ? acc1 : p1;
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-            // two gathered bf16 -> one dword: bytes [lo.0, lo.1, hi.0, hi.1] (v_perm_b32)
             const uint32_t w0 = __builtin_amdgcn_perm(*(lds_u16*)(uintptr_t)a[2 * j + 1],
                                                       *(lds_u16*)(uintptr_t)a[2 * j], 0x05040100u);
             const uint32_t w1 = __builtin_amdgcn_perm(*(lds_u16*)(uintptr_t)a[2 * j + 3],
                                                       *(lds_u16*)(uintptr_t)a[2 * j + 2], 0x05040100u);
-            acc0 = dot2(w0, xv[j], acc0);
-            acc1 = dot2(w1, xv[j + 1], acc1);
+            s0 = dot2(w0, xv[j], s0);
+            s1 = dot2(w1, xv[j + 1], s1);
         }
-        // Row end: this lane's sum goes to partial slot [row][s] (s = 1 only
-        // for a row an earlier wave started) and the sums restart; otherwise
-        // the store goes to the discard slot and keep = 1.
-        const uint32_t dst = __builtin_amdgcn_readlane(t_dst, d);
-        *(lds_f32*)(uintptr_t)(dst + 4u * lane) = acc0 + acc1;
-        const float keep = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t_keep), d));
-        acc0 *= keep;
-        acc1 *= keep;
+        if (NCH * S != CPR) {
+            const float keep = c < n ? 1.f : 0.f;
+            acc0 = fmaf(p0, keep, acc0);
+            acc1 = fmaf(p1, keep, acc1);
+        }
     }
-    __syncthreads();
-    const float* part = reinterpret_cast<const float*>(smem + cols * 2 + R * 128);
-    for (int i = w; i < R; i += nw) {
-        // Slot 1 holds data only if a wave range starts strictly inside row i.
-        bool split = false;
-#pragma unroll
-        for (int k = 1; k < nw; ++k) {
-            const int b = (k * C) / nw;
-            split |= b > i * cpr && b < (i + 1) * cpr;
-        }
-        float v = part[i * 128 + lane];
-        if (split) v += part[i * 128 + 64 + lane];
-        const float sum = wave_sum_lane63(v);
-        if (lane == 63) {
+    const float sum = wave_sum_lane63(acc0 + acc1);
+    if (S == 1) {
+        if (lane == 63 && row_u < rows) {
             if (y_f32)
-                reinterpret_cast<float*>(y)[r0 + i] = sum;
+                reinterpret_cast<float*>(y)[row_u] = sum;
             else
-                reinterpret_cast<uint16_t*>(y)[r0 + i] = f32_to_bf16(sum);
+                reinterpret_cast<uint16_t*>(y)[row_u] = f32_to_bf16(sum);
+        }
+    } else {
+        // the S partial sums of a row are added in wave order
+        if (lane == 63) s_part[wv] = sum;
+        __syncthreads();
+        if (sp == 0 && lane == 0 && row_u < rows) {
+            float t = s_part[wv];
+#pragma unroll
+            for (int q = 1; q < S; ++q) t += s_part[wv + q];
+            if (y_f32)
+                reinterpret_cast<float*>(y)[row_u] = t;
+            else
+                reinterpret_cast<uint16_t*>(y)[row_u] = f32_to_bf16(t);
         }
     }
+}
+
+template <int CPR, int S, int WPG, int PC>
+hipError_t launch_rows(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
+    constexpr int RPG = WPG / S;
+    const unsigned grid = (unsigned)((w.rows + RPG - 1) / RPG);
+    hipLaunchKernelGGL((lut6_gemv_rows<CPR, S, WPG, PC>), dim3(grid), dim3(64 * WPG), 0, s,
+                       w.lut6.packed, w.lut6.ld, w.lut6.lut, x, y, y_f32, (int)w.rows);
+    return hipGetLastError();
 }
 
 template <int B>
@@ -306,10 +260,13 @@ hipError_t launch_b(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
     return hipGetLastError();
 }
 
-// Cells per row (cols / 1024) with a compiled variant; other widths take the
-// generic kernel.  5 and 17 are the 27B-class MLP widths (5120, 17408).
-bool b1_cpr_supported(int64_t cpr) {
-    switch (cpr) {
+// Batch-1 variants by cells per row (cols / 1024): rows of at most eight
+// chunks use 4-wave workgroups, longer rows 10-wave workgroups (x for a
+// 17408-column row is 34 KB of LDS, so a CU holds four such groups); codes
+// are requested four chunks ahead.  Other widths take the generic kernel.
+bool rows_supported(const fqm_weights& w) {
+    if (w.cols <= 0 || (w.cols & 1023) || w.rows <= 0 || w.rows > 0x7fffffff) return false;
+    switch (w.cols >> 10) {
         case 1: case 2: case 3: case 4: case 5: case 6: case 8: case 12: case 16: case 17: case 20:
             return true;
         default:
@@ -317,55 +274,19 @@ bool b1_cpr_supported(int64_t cpr) {
     }
 }
 
-// Grid: 512 workgroups (two per CU on 256 CUs) when the row count allows,
-// with every workgroup holding at least one row per wave (so a row spans at
-// most two waves) and at most kB1Cells cells per wave.
-constexpr int64_t kB1MaxLds = 64 * 1024;  // dynamic LDS per workgroup
-
-bool b1_fits(const fqm_weights& w, int64_t* groups, size_t* lds) {
-    if (w.cols <= 0 || (w.cols & 1023) || w.rows < kB1Waves || w.rows > 0x7fffffff) return false;
-    if (w.lut6.ld > 0xffffffffLL / (kB1Cells + 1)) return false;  // 32-bit cell offsets
-    const int64_t cpr = w.cols >> 10;
-    if (cpr > kB1Cells || !b1_cpr_supported(cpr)) return false;
-    const int64_t rmax = (int64_t)kB1Cells * kB1Waves / cpr;   // rows per group, at most
-    const int64_t lo = (w.rows + rmax - 1) / rmax;              // fewest groups
-    const int64_t hi = w.rows / kB1Waves;                        // most groups
-    int64_t g = 512;
-    if (g < lo) g = lo;
-    if (g > hi) g = hi;
-    if (g < lo || g > 0x7fffffff) return false;
-    const int64_t r = (w.rows + g - 1) / g;
-    const int64_t bytes = w.cols * 2 + r * (128 + 512) + kB1Waves * 256;
-    if (bytes > kB1MaxLds) return false;
-    if (w.cols / 8 + r * 8 > (int64_t)kB1Stage * 64 * kB1Waves) return false;
-    *groups = g;
-    *lds = (size_t)bytes;
-    return true;
-}
-
-template <int CPR>
-hipError_t launch_b1_cpr(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
-                         int64_t groups, size_t lds, hipStream_t s) {
-    hipLaunchKernelGGL((lut6_gemv_b1<kB1Cells, kB1Ring, CPR>), dim3((unsigned)groups),
-                       dim3(64 * kB1Waves), lds, s, w.lut6.packed, w.lut6.ld, w.lut6.lut, x, y, y_f32,
-                       (int)(w.rows / groups), (int)(w.rows % groups));
-    return hipGetLastError();
-}
-
-hipError_t launch_b1(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int64_t groups,
-                     size_t lds, hipStream_t s) {
+hipError_t launch_b1(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
     switch (w.cols >> 10) {
-        case 1: return launch_b1_cpr<1>(w, x, y, y_f32, groups, lds, s);
-        case 2: return launch_b1_cpr<2>(w, x, y, y_f32, groups, lds, s);
-        case 3: return launch_b1_cpr<3>(w, x, y, y_f32, groups, lds, s);
-        case 4: return launch_b1_cpr<4>(w, x, y, y_f32, groups, lds, s);
-        case 5: return launch_b1_cpr<5>(w, x, y, y_f32, groups, lds, s);
-        case 6: return launch_b1_cpr<6>(w, x, y, y_f32, groups, lds, s);
-        case 8: return launch_b1_cpr<8>(w, x, y, y_f32, groups, lds, s);
-        case 12: return launch_b1_cpr<12>(w, x, y, y_f32, groups, lds, s);
-        case 16: return launch_b1_cpr<16>(w, x, y, y_f32, groups, lds, s);
-        case 17: return launch_b1_cpr<17>(w, x, y, y_f32, groups, lds, s);
-        case 20: return launch_b1_cpr<20>(w, x, y, y_f32, groups, lds, s);
+        case 1: return launch_rows<1, 1, 4, 4>(w, x, y, y_f32, s);
+        case 2: return launch_rows<2, 1, 4, 4>(w, x, y, y_f32, s);
+        case 3: return launch_rows<3, 1, 4, 4>(w, x, y, y_f32, s);
+        case 4: return launch_rows<4, 1, 4, 4>(w, x, y, y_f32, s);
+        case 5: return launch_rows<5, 1, 4, 4>(w, x, y, y_f32, s);
+        case 6: return launch_rows<6, 1, 4, 4>(w, x, y, y_f32, s);
+        case 8: return launch_rows<8, 1, 4, 4>(w, x, y, y_f32, s);
+        case 12: return launch_rows<12, 1, 10, 4>(w, x, y, y_f32, s);
+        case 16: return launch_rows<16, 1, 10, 4>(w, x, y, y_f32, s);
+        case 17: return launch_rows<17, 1, 10, 4>(w, x, y, y_f32, s);
+        case 20: return launch_rows<20, 1, 10, 4>(w, x, y, y_f32, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -374,9 +295,7 @@ hipError_t launch_b1(const fqm_weights& w, const uint16_t* x, void* y, int y_f32
 
 hipError_t launch_lut6_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
                             int batch, hipStream_t s) {
-    int64_t groups = 0;
-    size_t lds = 0;
-    if (batch == 1 && b1_fits(w, &groups, &lds)) return launch_b1(w, x, y, y_f32, groups, lds, s);
+    if (batch == 1 && rows_supported(w)) return launch_b1(w, x, y, y_f32, s);
     switch (batch) {
         case 1: return launch_b<1>(w, x, y, y_f32, s);
         case 2: return launch_b<2>(w, x, y, y_f32, s);

@@ -131,9 +131,9 @@ def test_gemv_zero_cols_and_padded_rows():
 
 
 # Batch-1 shapes with cols a multiple of 1024 (the cell-streaming kernel):
-# one cell per row with fewer rows than workgroups (most waves idle), rows
-# not dividing the grid, 16 cells per row, and a row count that makes the
-# launcher double the grid (rows split 5/6 per workgroup).
+# one 1024-weight chunk per row, rows not a multiple of the workgroup size,
+# 16 and 17 chunks per row (the 10-wave workgroup variants), and a row count
+# that leaves a partial last workgroup.
 B1_SHAPES = [(77, 1024, 9), (1000, 3072, 8), (513, 2048, 12), (600, 16384, 10), (5200, 17408, 13)]
 
 
