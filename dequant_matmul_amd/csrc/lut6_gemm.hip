@@ -8,21 +8,32 @@
 // X, and contracts them on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16,
 // fp32 accumulate).
 //
-// Decode: one row's 64 codes of a K step sit on the 64 lanes of a wave (lane
-// l takes code l, bits [6l, 6l+6) of the row's 48-byte segment), so every
-// gather of an instruction reads the same 128-byte table (distinct banks or a
-// shared dword: no bank conflicts), and each lane stores its bf16 value at
-// its column.  The BN row tables stay in LDS for the whole K loop.
+// Data movement per K step (one workgroup, 8 waves):
+//   - X block: 32 KB, four 16-byte loads per thread into registers one step
+//     ahead, then ds_write_b128 into the X tile.
+//   - codes: the 128 rows x 48 bytes of the step, one 16-byte load per thread
+//     into a small LDS code buffer, so the global loads carry each code byte
+//     once.
+//   - decode: a wave instruction covers two rows, 32 lanes each; lane j takes
+//     the code pair (2j, 2j+1) of its row from one 8-byte LDS read, gathers
+//     both bf16 values from the row table (the two tables sit in opposite
+//     halves of the 64 banks: no conflicts) and stores them as one dword.
+// X and W tiles are 128-byte rows whose 16-byte chunks are XOR-swizzled by
+// (row / 2) % 8, so the MFMA operand reads (16 rows per quarter wave, same
+// chunk) hit 16 distinct bank groups.
 //
-// Pipeline: LDS tiles are double-buffered; while the waves run the MFMAs of
-// step t they decode step t+1 (codes already in registers) into the other
-// buffer, store the prefetched X block of step t+1, and issue the global
-// loads of step t+2.  One barrier per step.
+// Pipeline: the decode is spread over steps (codes read one step before
+// their gathers; gathers, X stores and W writes issued between the MFMAs of
+// the current step) so no wave waits on an LDS round trip with its matrix
+// instructions idle.  The order inside a step is fixed in the source with
+// scheduling barriers.  One workgroup barrier per step.
 //
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, and
 // workgroup b computes M tile b % 8 (for M = 8 * BM), so each XCD keeps one
 // X panel (BM x K bf16, 2.6 MB at K = 5120) in its own L2 while the W panels
 // stream through; other M take the same mapping modulo the M tile count.
+#include <type_traits>
+
 #include "fqm_internal.h"
 
 namespace fqm {
@@ -32,21 +43,35 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef u32x2 u32x2_a4 __attribute__((aligned(4)));
 typedef __attribute__((address_space(3))) uint8_t lds8;
 typedef __attribute__((address_space(3))) const uint16_t lds16c;
-typedef __attribute__((address_space(3))) uint16_t lds16;
+typedef __attribute__((address_space(3))) uint32_t lds32;
+typedef __attribute__((address_space(3))) const u32x2_a4 lds64c;
 typedef __attribute__((address_space(3))) u32x4 lds128;
 typedef __attribute__((address_space(3))) const u32x4 lds128c;
 
 constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int NWAVE = 8;                  // 4 (M) x 2 (N) waves, 64 x 64 outputs each
-constexpr int LDT = BK + 8;               // LDS row stride of the X and W tiles, bf16 elements
-constexpr int XT_BYTES = BM * LDT * 2;    // one X tile
-constexpr int WT_BYTES = BN * LDT * 2;    // one W tile
-constexpr int TAB_BYTES = BN * 128;       // BN row tables
-constexpr int LDS_BYTES = 2 * XT_BYTES + 2 * WT_BYTES + TAB_BYTES;
-constexpr int ROWS_PER_WAVE = BN / NWAVE; // W rows each wave decodes per step
+constexpr int NWAVE = 8;                     // 4 (M) x 2 (N) waves, 64 x 64 outputs each
+constexpr int XT_BYTES = BM * BK * 2;        // one X tile, 128-byte rows
+constexpr int WT_BYTES = BN * BK * 2;        // one W tile, 128-byte rows
+constexpr int TAB_BYTES = BN * 128;          // BN row tables
+constexpr int CODE_BYTES = BN * BK * 3 / 4;  // one step of codes, 48 bytes per row
+constexpr int OFF_W = 2 * XT_BYTES;
+constexpr int OFF_TAB = OFF_W + 2 * WT_BYTES;
+// The code buffers keep 16 bytes of slack on both sides: the first lane pair
+// of a row reads the dword before the row, the last one the dword after it
+// (both only feed bits that are masked off).
+constexpr int OFF_CODE = OFF_TAB + TAB_BYTES + 16;
+constexpr int LDS_BYTES = OFF_CODE + 2 * CODE_BYTES + 16;
 constexpr int XPT = BM * BK * 2 / 16 / (64 * NWAVE);  // 16-byte X pieces per thread per step
+constexpr int CPT = CODE_BYTES / 16;                  // 16-byte code pieces per step
+constexpr int PAIRS = BN / NWAVE / 2;                 // row pairs each wave decodes per step
+static_assert(XPT == 4 && CPT <= 64 * NWAVE && PAIRS == 8, "tile constants");
+static_assert(OFF_TAB % 256 == 0, "tables must start on a 256-byte bank line");
+
+template <int BUF>
+using Buf = std::integral_constant<int, BUF>;
 
 __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* __restrict__ X,
                                                                const uint8_t* __restrict__ packed,
@@ -56,8 +81,6 @@ __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* _
                                                                int N, int K, int mtiles) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds8*)smem;
-    const uint32_t xt0 = lds0, wt0 = lds0 + 2 * XT_BYTES;
-    const uint32_t tab0 = wt0 + 2 * WT_BYTES;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -65,149 +88,180 @@ __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* _
     const int mt = b % mtiles, nt = b / mtiles;
     const int m0 = mt * BM, n0 = nt * BN;
     const int wm = wave >> 1, wn = wave & 1;  // this wave's 64 x 64 output block
+    const int h = lane >> 5, j = lane & 31;
 
-    // ---- row tables (resident) -------------------------------------------------
+    // ---- row tables (resident for the whole K loop) ---------------------------
     for (int i = tid; i < BN * 8; i += 64 * NWAVE) {
         const int r = i >> 3, part = i & 7;
         u32x4 v = {0u, 0u, 0u, 0u};
         if (n0 + r < N) v = *reinterpret_cast<const u32x4*>(lut + (int64_t)(n0 + r) * 64 + part * 8);
-        *(lds128*)(uintptr_t)(tab0 + (uint32_t)i * 16u) = v;
+        *(lds128*)(uintptr_t)(lds0 + OFF_TAB + (uint32_t)i * 16u) = v;
     }
 
-    // ---- per-lane decode constants --------------------------------------------
-    // Lane l owns code l of a 64-code segment, bits [6l, 6l+6).  A funnel shift
-    // by p = 6l - 1 of the dword pair holding bit p puts the code at bits 1..6
-    // (its table byte offset); lane 0 shifts its first dword left by one
-    // (pair (d0, d0), shift 31).  Lanes 59..63 end inside dword 11 and read no
-    // dword past it.
-    const int p6 = 6 * lane - 1;
-    const uint32_t clo = lane == 0 ? 0u : (uint32_t)(p6 >> 5);
-    const uint32_t chi = lane == 0 ? 0u : (clo < 11u ? clo + 1u : 11u);
-    const uint32_t csh = (uint32_t)(p6 & 31);
+    // ---- global sources and LDS destinations of the staged pieces -------------
+    // X piece u of this thread: row (tid / 8) + 64 u, chunk tid % 8.
+    const uint16_t* xsrc[XPT];
+#pragma unroll
+    for (int u = 0; u < XPT; ++u)
+        xsrc[u] = X + (int64_t)min(m0 + (tid >> 3) + 64 * u, M - 1) * K + 8 * (tid & 7);
+    const uint32_t xdst = (uint32_t)(128 * (tid >> 3) + 16 * ((tid & 7) ^ ((tid >> 4) & 7)));
+    // Code piece of this thread: 16 bytes of row p / 3 (threads past the last
+    // piece repeat an earlier one: same bytes to the same address).
+    const int cp = tid < CPT ? tid : tid - CPT;
+    const uint8_t* csrc = packed + (int64_t)min(n0 + cp / 3, N - 1) * ld + 16 * (cp % 3);
+    const uint32_t cdst = (uint32_t)(16 * cp);
+
+    // ---- decode constants ------------------------------------------------------
+    // Wave w decodes rows 2w + 16 p + h (p = 0..7); lane j of each half takes
+    // the codes 2j and 2j + 1, bits [12j, 12j + 12) of the row's 48 bytes.  A
+    // funnel shift by 12j - 1 of the dword pair holding bit 12j - 1 puts code
+    // 2j at bits 1..6 (its table byte offset) and code 2j + 1 at bits 7..12.
+    const int q12 = 12 * j - 1;
+    const uint32_t crd = (uint32_t)(OFF_CODE + 48 * (2 * wave + h) + 4 * (q12 >> 5));  // + buffer
+    const uint32_t csh = (uint32_t)(q12 & 31);
+    const uint32_t tabw = lds0 + OFF_TAB + (uint32_t)(128 * (2 * wave + h));  // multiple of 128
+    const uint32_t wst = (uint32_t)(OFF_W + 128 * (2 * wave + h) + 16 * ((j >> 2) ^ wave) + 4 * (j & 3));
     uint32_t vmask = 0x7Eu;
     asm volatile("" : "+v"(vmask));  // in a VGPR: (v & mask) | base is one v_and_or_b32
 
-    // this wave decodes rows wave + NWAVE*i of the tile
-    const uint8_t* crow[ROWS_PER_WAVE];
+    // ---- MFMA operand addresses ------------------------------------------------
+    // A: row wm*64 + 32 i + (lane % 32) of the X tile, B: row wn*64 + 32 jj +
+    // (lane % 32) of the W tile; k slice q, 8 elements at 8 h: chunk 2q + h.
+    uint32_t aq[BK / 16], bq[BK / 16];
 #pragma unroll
-    for (int i = 0; i < ROWS_PER_WAVE; ++i) {
-        const int r = min(n0 + wave + NWAVE * i, N - 1);
-        crow[i] = packed + (int64_t)r * ld;
-    }
-    // X pieces of this thread: row xr, 16-byte piece xc (8 per 64-element row)
-    const uint16_t* xsrc[XPT];
-    uint32_t xdst[XPT];
-#pragma unroll
-    for (int u = 0; u < XPT; ++u) {
-        const int p = tid + u * 64 * NWAVE;
-        const int xr = p >> 3, xc = p & 7;
-        xsrc[u] = X + (int64_t)min(m0 + xr, M - 1) * K + 8 * xc;
-        xdst[u] = (uint32_t)(xr * LDT + 8 * xc) * 2u;
+    for (int q = 0; q < BK / 16; ++q) {
+        const uint32_t c = (uint32_t)(16 * ((2 * q + h) ^ ((lane >> 1) & 7)));
+        aq[q] = lds0 + (uint32_t)(128 * (wm * 64 + j)) + c;
+        bq[q] = lds0 + OFF_W + (uint32_t)(128 * (wn * 64 + j)) + c;
     }
 
     const int steps = K / BK;
-    uint32_t cw[ROWS_PER_WAVE][2];  // codes of the next step to decode
-    u32x4 xw[XPT];            // X pieces of the next step to store
-    auto load_step = [&](int t) {
-        const int kb = t * BK;
+    u32x4 xw[XPT];          // X pieces of the next step
+    u32x4 cw;               // a 16-byte code piece, three steps ahead
+    u32x2 cc[PAIRS];        // this lane's code dwords for the next W tile
+    uint32_t g0[PAIRS], g1[PAIRS];  // gathered bf16 values of the next W tile
+    auto load_x = [&](int t) {
 #pragma unroll
-        for (int i = 0; i < ROWS_PER_WAVE; ++i) {
-            const uint32_t* seg = reinterpret_cast<const uint32_t*>(crow[i] + (kb * 3) / 4);
-            cw[i][0] = seg[clo];
-            cw[i][1] = seg[chi];
-        }
-#pragma unroll
-        for (int u = 0; u < XPT; ++u) xw[u] = *reinterpret_cast<const u32x4*>(xsrc[u] + kb);
+        for (int u = 0; u < XPT; ++u) xw[u] = *reinterpret_cast<const u32x4*>(xsrc[u] + t * BK);
     };
-    auto store_step = [&](int buf) {
-        const uint32_t xt = xt0 + (uint32_t)buf * XT_BYTES, wt = wt0 + (uint32_t)buf * WT_BYTES;
-#pragma unroll
-        for (int u = 0; u < XPT; ++u) *(lds128*)(uintptr_t)(xt + xdst[u]) = xw[u];
-        // all gathers first, then the stores: the table reads of the rows overlap
-        uint32_t w16[ROWS_PER_WAVE];
-#pragma unroll
-        for (int i = 0; i < ROWS_PER_WAVE; ++i) {
-            const uint32_t tb = tab0 + 128u * (uint32_t)(wave + NWAVE * i);  // multiple of 128
-            const uint32_t v = __builtin_amdgcn_alignbit(cw[i][1], cw[i][0], csh);
-            w16[i] = *(lds16c*)(uintptr_t)((v & vmask) | tb);
-        }
-        const uint32_t wl = wt + (uint32_t)(wave * LDT + lane) * 2u;
-#pragma unroll
-        for (int i = 0; i < ROWS_PER_WAVE; ++i)
-            *(lds16*)(uintptr_t)(wl + (uint32_t)(NWAVE * i * LDT) * 2u) = (uint16_t)w16[i];
+    auto load_c = [&](int t) { cw = *reinterpret_cast<const u32x4*>(csrc + t * (BK * 3 / 4)); };
+    auto store_x = [&](int buf, int u) {
+        *(lds128*)(uintptr_t)(lds0 + xdst + (uint32_t)(buf * XT_BYTES + 8192 * u)) = xw[u];
+    };
+    auto store_c = [&](int buf) {
+        *(lds128*)(uintptr_t)(lds0 + OFF_CODE + (uint32_t)(buf * CODE_BYTES) + cdst) = cw;
+    };
+    auto read_codes = [&](int buf, int p) {
+        cc[p] = *(lds64c*)(uintptr_t)(lds0 + crd + (uint32_t)(buf * CODE_BYTES + 768 * p));
+    };
+    auto gather = [&](int p) {
+        const uint32_t v = __builtin_amdgcn_alignbit(cc[p].y, cc[p].x, csh);
+        const uint32_t a0 = (v & vmask) | tabw;
+        const uint32_t a1 = ((v >> 6) & vmask) | tabw;
+        g0[p] = *(lds16c*)(uintptr_t)(a0 + 2048u * p);
+        g1[p] = *(lds16c*)(uintptr_t)(a1 + 2048u * p);
+    };
+    auto write_w = [&](int buf, int p) {
+        *(lds32*)(uintptr_t)(lds0 + wst + (uint32_t)(buf * WT_BYTES + 2048 * p)) = g0[p] | (g1[p] << 16);
     };
 
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
 
-    load_step(0);
-    __syncthreads();  // tables in LDS
-    store_step(0);
-    load_step(min(1, steps - 1));
+    // ---- prologue ----------------------------------------------------------------
+    // State at the top of step t (buffer B = t % 2): X and W buffers B hold
+    // X(t) and W(t); cc holds the codes of step t+1; code buffer B holds the
+    // codes of step t+2; xw and cw hold (or are loading) X(t+1) and the codes
+    // of step t+3.
+    load_x(0);
+    load_c(0);
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) store_x(0, u);
+    store_c(0);
+    load_c(min(1, steps - 1));
+    store_c(1);
+    __syncthreads();  // tables, X(0), codes of steps 0 and 1
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) read_codes(0, p);
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) gather(p);
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) write_w(0, p);
+#pragma unroll
+    for (int p = 0; p < PAIRS; ++p) read_codes(1, p);
+    load_c(min(2, steps - 1));
+    load_x(min(1, steps - 1));
+    __syncthreads();  // W(0) written, code buffer 0 free
+    store_c(0);
+    load_c(min(3, steps - 1));
     __syncthreads();
 
-    // MFMA operand addresses: A rows wm*64 + 32*i + (lane % 32), B rows wn*64 + 32*j + (lane % 32),
-    // 8 consecutive k at 8*(lane / 32) within each 16-wide k slice.
-    const uint32_t aoff = (uint32_t)((wm * 64 + (lane & 31)) * LDT + 8 * (lane >> 5)) * 2u;
-    const uint32_t boff = (uint32_t)((wn * 64 + (lane & 31)) * LDT + 8 * (lane >> 5)) * 2u;
-    for (int t = 0; t < steps; ++t) {
-        const int buf = t & 1;
-        const uint32_t xt = xt0 + (uint32_t)buf * XT_BYTES + aoff;
-        const uint32_t wt = wt0 + (uint32_t)buf * WT_BYTES + boff;
-        // Operand fragments are double-buffered across the four 16-wide k slices.
+    // ---- main loop -----------------------------------------------------------------
+    // Step t issues, in this order with the MFMAs of step t spread between
+    // them: the gathers of W(t+1) (codes read one step earlier), the code
+    // reads of step t+2, the stores of X(t+1) and of the codes of step t+3,
+    // the writes of W(t+1), and the global loads of X(t+2) and of the codes
+    // of step t+4.  Past the end the indices are clamped; the extra work lands
+    // in buffers that are never read.
+    auto step = [&](auto bufc, int t) {
+        constexpr int B = decltype(bufc)::value;
         bf16x8 a[2][2], bb[2][2];
-        auto frag = [&](int kk, int f) {
+        auto frag = [&](int q) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                a[f][i] = __builtin_bit_cast(bf16x8, *(lds128c*)(uintptr_t)(xt + (uint32_t)(32 * i * LDT + kk) * 2u));
+                a[q & 1][i] = __builtin_bit_cast(bf16x8, *(lds128c*)(uintptr_t)(aq[q] + (uint32_t)(B * XT_BYTES + 4096 * i)));
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bb[f][j] = __builtin_bit_cast(bf16x8, *(lds128c*)(uintptr_t)(wt + (uint32_t)(32 * j * LDT + kk) * 2u));
+            for (int jj = 0; jj < 2; ++jj)
+                bb[q & 1][jj] = __builtin_bit_cast(bf16x8, *(lds128c*)(uintptr_t)(bq[q] + (uint32_t)(B * WT_BYTES + 4096 * jj)));
         };
-        frag(0, 0);
-#pragma unroll
-        for (int q = 0; q < BK / 16; ++q) {
-            if (q + 1 < BK / 16) frag(16 * (q + 1), (q + 1) & 1);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[q & 1][i], bb[q & 1][j], acc[i][j], 0, 0, 0);
-        }
-        // Decode step t+1 into the other buffer and request step t+2, in the
-        // same basic block as the MFMAs so the two interleave.  Past the end
-        // the step index is clamped: the extra decode lands in a buffer that is
-        // never read and the extra loads re-read the last step.
-        store_step(buf ^ 1);
-        load_step(min(t + 2, steps - 1));
-        // Interleave: each MFMA followed by a share of the decode's VALU, LDS
-        // and global-load instructions (scheduling hint only).
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global load
-        }
+        auto mma = [&](int q, int i, int jj) {
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[q & 1][i], bb[q & 1][jj], acc[i][jj], 0, 0, 0);
+        };
+#define FQM_SLOT __builtin_amdgcn_sched_barrier(0)
+        frag(0);
+        frag(1);
+        FQM_SLOT;
+        mma(0, 0, 0); gather(0); gather(1); FQM_SLOT;
+        mma(0, 0, 1); gather(2); gather(3); FQM_SLOT;
+        mma(0, 1, 0); gather(4); gather(5); FQM_SLOT;
+        mma(0, 1, 1); gather(6); gather(7); FQM_SLOT;
+        frag(2); FQM_SLOT;
+        mma(1, 0, 0); read_codes(B, 0); read_codes(B, 1); FQM_SLOT;
+        mma(1, 0, 1); read_codes(B, 2); read_codes(B, 3); FQM_SLOT;
+        mma(1, 1, 0); read_codes(B, 4); read_codes(B, 5); FQM_SLOT;
+        mma(1, 1, 1); read_codes(B, 6); read_codes(B, 7); FQM_SLOT;
+        frag(3); FQM_SLOT;
+        mma(2, 0, 0); store_x(B ^ 1, 0); store_x(B ^ 1, 1); FQM_SLOT;
+        mma(2, 0, 1); store_x(B ^ 1, 2); store_x(B ^ 1, 3); FQM_SLOT;
+        mma(2, 1, 0); store_c(B ^ 1); write_w(B ^ 1, 0); write_w(B ^ 1, 1); FQM_SLOT;
+        mma(2, 1, 1); write_w(B ^ 1, 2); write_w(B ^ 1, 3); FQM_SLOT;
+        mma(3, 0, 0); write_w(B ^ 1, 4); write_w(B ^ 1, 5); FQM_SLOT;
+        mma(3, 0, 1); write_w(B ^ 1, 6); write_w(B ^ 1, 7); FQM_SLOT;
+        mma(3, 1, 0); load_x(min(t + 2, steps - 1)); FQM_SLOT;
+        mma(3, 1, 1); load_c(min(t + 4, steps - 1)); FQM_SLOT;
+#undef FQM_SLOT
         __syncthreads();
+    };
+    for (int t = 0; t < steps; t += 2) {
+        step(Buf<0>{}, t);
+        if (t + 1 < steps) step(Buf<1>{}, t + 1);
     }
 
     // D layout of a 32x32 block: lane l, item r -> row (r % 4) + 8 * (r / 4) + 4 * (l / 32), column l % 32.
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + 32 * i + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
-                const int n = n0 + wn * 64 + 32 * j + (lane & 31);
-                if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16(acc[i][j][r]);
+                const int m = m0 + wm * 64 + 32 * i + (r & 3) + 8 * (r >> 2) + 4 * h;
+                const int n = n0 + wn * 64 + 32 * jj + j;
+                if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16(acc[i][jj][r]);
             }
 }
 
