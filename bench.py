@@ -114,11 +114,13 @@ def main():
             y = torch.empty((b, cfg["rows"]), dtype=torch.bfloat16, device=dev)
             nbytes = w0.nbytes() + x.numel() * 2 + y.numel() * 2
             off = 0 if b == 1 else len(lut6[name]) // 2
+            ws_bytes = fqm.workspace_size(w0, b)
+            wsp = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
             rows[key] = dict(
-                fn=(lambda s, ws=lut6[name], x=x, y=y, off=off:
-                    fqm.gemv(ws[(s + off) % len(ws)], x, y=y)),
+                fn=(lambda s, ws=lut6[name], x=x, y=y, off=off, wsp=wsp:
+                    fqm.gemv(ws[(s + off) % len(ws)], x, y=y, workspace=wsp)),
                 bytes=nbytes, flops=2 * b * cfg["rows"] * cfg["cols"], bound="hbm",
-                kernel=f"lut6_gemv batch {b}")
+                kernel="lut6_gemv_rows, batch 1" if b == 1 else f"lut6_gemv_mfma, batch {b}")
     if wanted("prefill"):
         M = C["prefill"]["M"]
         ws = lut6["up"]

@@ -138,6 +138,7 @@ fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream) {
 
 size_t fqm_workspace_size(const fqm_weights* w, int32_t batch) {
     if (check_weights(w) != FQM_OK || batch < 1 || batch > 16) return 0;
+    if (w->format == FQM_LUT6) return fqm::lut6_gemv_mfma_workspace(*w, batch);
     if (w->format != FQM_MDBF) return 0;
     return (size_t)w->mdbf.P * (size_t)batch * (size_t)w->mdbf.r * sizeof(float);
 }
@@ -154,7 +155,13 @@ fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_
     const int y_f32 = y_dtype == FQM_F32;
     hipStream_t s = as_stream(stream);
     switch (w->format) {
-        case FQM_LUT6: return hip_status(launch_lut6_gemv(*w, x, y, y_f32, batch, s));
+        case FQM_LUT6: {
+            const size_t need = fqm_workspace_size(w, batch);
+            if (need && (!workspace || ws_bytes < need)) return FQM_E_WORKSPACE;
+            if (need && !aligned16(workspace)) return FQM_E_ALIGN;
+            return hip_status(
+                launch_lut6_gemv(*w, x, y, y_f32, batch, static_cast<float*>(workspace), s));
+        }
         case FQM_FABQ: return hip_status(launch_fabq_gemv(*w, x, y, y_f32, batch, s));
         case FQM_MDBF: {
             const size_t need = fqm_workspace_size(w, batch);

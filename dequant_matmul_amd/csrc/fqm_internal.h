@@ -79,7 +79,13 @@ hipError_t launch_dequant_lut6(const fqm_weights& w, uint16_t* W, hipStream_t s)
 hipError_t launch_dequant_fabq(const fqm_weights& w, uint16_t* W, hipStream_t s);
 
 hipError_t launch_lut6_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
-                            int batch, hipStream_t s);
+                            int batch, float* ws, hipStream_t s);
+// Batch 2..16 on the matrix cores (cols a multiple of 1024); K may be split
+// over workgroups, with fp32 partial sums in the caller's workspace.
+bool lut6_gemv_mfma_supported(const fqm_weights& w, int batch);
+size_t lut6_gemv_mfma_workspace(const fqm_weights& w, int batch);
+hipError_t launch_lut6_gemv_mfma(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
+                                 float* ws, hipStream_t s);
 hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M,
                             hipStream_t s);
 hipError_t launch_fabq_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,

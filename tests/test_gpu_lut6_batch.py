@@ -1,0 +1,79 @@
+"""GPU parity for the batch 2..16 per-row LUT 6-bit GEMV on the matrix cores
+("Qwen3.8-27B - BenQ 6-bit", "What BenQ stores"): cols a multiple of 1024,
+row counts that leave a partial 16-row block, and row counts small enough
+that K is split over workgroups (evenly, unevenly, one chunk per split)."""
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_amd as fqm
+import oracle
+import synth
+from gpu_common import (DEV, assert_close, bf16_dev, canaries_intact, guarded, lut6_case,
+                        lut6_weights, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+# (rows, cols, seed, batches): 1 chunk and a partial block; a 4-way split of
+# 4 chunks; 3 chunks in 3 splits; 17 chunks in 17 splits; 5 chunks, 5 splits;
+# 17 chunks in splits of 5, 5, 5, 2.  (K is split unless there are at least
+# 1024 row blocks of 16.)
+CASES = [(77, 1024, 9, (2, 16)), (300, 4096, 21, (3, 8)), (1000, 3072, 8, (5, 13)),
+         (600, 17408, 10, (2, 8)), (2000, 5120, 5, (16,)), (4100, 17408, 4, (4,))]
+
+
+@pytest.mark.parametrize("rows,cols,seed,batches", CASES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemv_mfma_cases(rows, cols, seed, batches, out):
+    inp, packed = lut6_case(rows, cols, seed)
+    w = lut6_weights(rows, cols, seed)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    for b in batches:
+        x = synth.activations(b, cols, seed + b)
+        buf, y = guarded((b, rows), dt)
+        need = fqm.workspace_size(w, b)
+        wsp = torch.empty(need, dtype=torch.uint8, device=DEV) if need else None
+        print(f"lut6 mfma gemv {rows}x{cols} batch {b} {out} workspace {need}", flush=True)
+        fqm.gemv(w, bf16_dev(x), y=y, workspace=wsp)
+        torch.cuda.synchronize()
+        assert canaries_intact(buf)
+        assert_close(to_f64(y), oracle.lut6.gemv(packed, inp.lut, x, cols), out, f"{rows}x{cols} b{b} {out}")
+
+
+def test_gemv_mfma_workspace_rule():
+    # few rows -> K split with workspace; 1024 or more row blocks -> none
+    assert fqm.workspace_size(lut6_weights(300, 4096, 21), 8) == 4 * 8 * 300 * 4
+    assert fqm.workspace_size(lut6_weights(4100, 17408, 4), 8) == 4 * 8 * 4100 * 4
+    assert fqm.workspace_size(lut6_weights(16384, 1024, 4), 8) == 0
+    assert fqm.workspace_size(lut6_weights(300, 4096, 21), 1) == 0
+    # a too-small workspace is refused
+    w = lut6_weights(300, 4096, 21)
+    x = bf16_dev(synth.activations(8, 4096, 1))
+    with pytest.raises(RuntimeError):
+        fqm.gemv(w, x, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+
+
+def test_gemv_mfma_exact_invariants():
+    rows, cols, seed = 300, 4096, 21
+    inp, _ = lut6_case(rows, cols, seed)
+    w = lut6_weights(rows, cols, seed)
+    lv = oracle.numerics.bf16_to_f64(inp.lut)
+    # one-hot x rows return decoded columns exactly (each batch row its own k)
+    ks = [0, 1023, 1024, 2047 + 17, 3000, cols - 1]
+    x = np.zeros((len(ks), cols), np.uint16)
+    for b, k in enumerate(ks):
+        x[b, k] = 0x3F80
+    y = to_f64(fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32))
+    for b, k in enumerate(ks):
+        assert np.array_equal(y[b], lv[np.arange(rows), inp.codes[:, k]]), k
+    # scaling x by 4 scales y by 4 exactly; the same call twice gives the same bits
+    x = synth.activations(6, cols, seed)
+    y = to_f64(fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32))
+    x4 = x.astype(np.uint32) + (2 << 7)
+    x4 = np.where((x & 0x7FFF) == 0, x, x4).astype(np.uint16)
+    assert np.array_equal(to_f64(fqm.gemv(w, bf16_dev(x4), out_dtype=torch.float32)), 4 * y)
+    assert np.array_equal(to_f64(fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32)), y)
+    # each batch row is independent of the others: row b alone equals row b of the batch
+    y1 = to_f64(fqm.gemv(w, bf16_dev(np.repeat(x[2:3], 2, axis=0)), out_dtype=torch.float32))
+    assert np.array_equal(y1[0], y1[1])
+    assert np.linalg.norm(y1[0] - y[2]) <= 1e-6 * np.linalg.norm(y[2])
