@@ -140,7 +140,7 @@ size_t fqm_workspace_size(const fqm_weights* w, int32_t batch) {
     if (check_weights(w) != FQM_OK || batch < 1 || batch > 16) return 0;
     if (w->format == FQM_LUT6) return fqm::lut6_gemv_mfma_workspace(*w, batch);
     if (w->format != FQM_MDBF) return 0;
-    return (size_t)w->mdbf.P * (size_t)batch * (size_t)w->mdbf.r * sizeof(float);
+    return fqm::mdbf_workspace_bytes(*w, batch);
 }
 
 fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
@@ -168,7 +168,7 @@ fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_
             if (!workspace || ws_bytes < need) return FQM_E_WORKSPACE;
             if (!aligned16(workspace)) return FQM_E_ALIGN;
             return hip_status(
-                launch_mdbf_gemv(*w, x, y, y_f32, batch, static_cast<float*>(workspace), s));
+                launch_mdbf_gemv(*w, x, y, y_f32, batch, workspace, s));
         }
     }
     return FQM_E_FORMAT;

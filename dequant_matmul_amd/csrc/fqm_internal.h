@@ -90,7 +90,9 @@ hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y
                             hipStream_t s);
 hipError_t launch_fabq_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
                             int batch, hipStream_t s);
-hipError_t launch_mdbf_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
-                            int batch, float* z, hipStream_t s);
+// MDBF: workspace holds the bf16 hi/lo dense operands of both passes.
+size_t mdbf_workspace_bytes(const fqm_weights& w, int batch);
+hipError_t launch_mdbf_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch, void* ws,
+                            hipStream_t s);
 
 }  // namespace fqm

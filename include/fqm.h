@@ -177,7 +177,8 @@ fqm_status fqm_unpack(const uint8_t* packed, uint8_t* codes, int64_t rows, int64
 fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
 
 /* Bytes of device workspace fqm_gemv needs for this descriptor and batch:
- * MDBF P*batch*r*4 (the fp32 intermediate z); LUT6 with batch >= 2 and
+ * MDBF 6*P*l*batch*(roundup(m,256) + roundup(r,256)) (the dense operands of
+ * both passes, each fp32 value as three bf16 parts); LUT6 with batch >= 2 and
  * cols a multiple of 1024 splits K over workgroups when there are few rows,
  * and then needs S*batch*rows*4 (S fp32 partial sums per output, S <= cols /
  * 1024, a function of rows and cols only), else 0; 0 for FABQ.

@@ -45,3 +45,31 @@ def test_variants(l, P):
     x = synth.activations(5, m, 61)
     y = fqm.gemv(weights(inp), bf16_dev(x), out_dtype=torch.float32)
     assert_close(to_f64(y), oracle.mdbf.gemv_dense(paths, x, n, m, r), "f32", f"l={l} P={P}")
+
+
+# Batch slices per workgroup are 32 // l rows: l = 16 splits a batch of 16 into
+# eight slices, l = 3 into slices of 10 and 6 (a partly empty second column
+# block); m = 544 and r = 300 are not multiples of the 256-column K block.
+@pytest.mark.parametrize("l,P,batch", [(16, 1, 16), (3, 2, 16), (2, 1, 7), (1, 2, 1)])
+def test_batch_slices_and_padding(l, P, batch):
+    n, m, r = 333, 544, 300
+    inp, paths = case(n, m, r, l, P, 70 + l + P)
+    x = synth.activations(batch, m, 71)
+    buf, y = guarded((batch, n), torch.float32)
+    print(f"mdbf n={n} m={m} r={r} l={l} P={P} batch {batch}", flush=True)
+    fqm.gemv(weights(inp), bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.mdbf.gemv_dense(paths, x, n, m, r), "f32", f"l={l} P={P} b={batch}")
+
+
+def test_deterministic_and_batch_independent():
+    inp, paths = case(4096, 4096, 2000, 2, 1, 6)
+    w = weights(inp)
+    x = synth.activations(16, 4096, 9)
+    y1 = to_f64(fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32))
+    y2 = to_f64(fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32))
+    assert np.array_equal(y1, y2)
+    # a batch row computed alone matches its row of the batch
+    y3 = to_f64(fqm.gemv(w, bf16_dev(x[5:6]), out_dtype=torch.float32))
+    assert np.linalg.norm(y3[0] - y1[5]) <= 1e-6 * np.linalg.norm(y1[5])
