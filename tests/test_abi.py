@@ -75,6 +75,19 @@ def test_lut6_argument_errors(lib):
     assert lib.fqm_gemm(ctypes.byref(lut6()), None, FAKE, 4, None) == E["NULL"]
 
 
+def test_lut6_workspace_rule(lib):
+    # batch >= 2 with cols % 1024 == 0 splits K over workgroups while there are
+    # fewer than 1024 row blocks of 16: ceil(1024 / blocks) splits, capped at
+    # cols / 1024 chunks, evened out over the chunks
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=4096, ld=3072)), 8) == 4 * 8 * 300 * 4
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=5120, cols=17408, ld=13056)), 8) == 4 * 8 * 5120 * 4
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=17408, cols=5120, ld=3840)), 8) == 0
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=4096, ld=3072)), 1) == 0
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=4032, ld=3024)), 8) == 0
+    # a missing workspace is refused before anything is enqueued
+    assert gemv(lib, lut6(rows=300, cols=4096, ld=3072), batch=8) == E["WORKSPACE"]
+
+
 def test_pack_argument_errors(lib):
     assert lib.fqm_pack_bits(FAKE, FAKE, 4, 64, 3, 64, None, None) == E["FORMAT"]
     assert lib.fqm_pack_bits(FAKE, FAKE, 4, 64, 6, 32, None, None) == E["SHAPE"]   # ld < 48
@@ -128,7 +141,8 @@ def mdbf(r=2000, l=2, P=1, n=4096, m=4096):
 def test_mdbf_argument_errors_and_workspace(lib):
     w = mdbf()
     need = lib.fqm_workspace_size(ctypes.byref(w), 16)
-    assert need == 16 * 2000 * 4
+    # three bf16 parts per dense value, both passes, K padded to 256
+    assert need == 6 * 1 * 2 * 16 * (4096 + 2048)
     assert gemv(lib, w, batch=16, ws=None, wsb=0) == E["WORKSPACE"]
     assert gemv(lib, w, batch=16, ws=FAKE, wsb=need - 4) == E["WORKSPACE"]
     assert gemv(lib, mdbf(l=0)) == E["FORMAT"]
@@ -138,6 +152,6 @@ def test_mdbf_argument_errors_and_workspace(lib):
     w = mdbf()
     w.mdbf.path[0].ld_A = 240   # < ceil(2000/8)
     assert gemv(lib, w) == E["SHAPE"]
-    assert lib.fqm_workspace_size(ctypes.byref(mdbf(P=2)), 3) == 2 * 3 * 2000 * 4
+    assert lib.fqm_workspace_size(ctypes.byref(mdbf(P=2)), 3) == 6 * 2 * 2 * 3 * (4096 + 2048)
     assert lib.fqm_dequant(ctypes.byref(mdbf()), FAKE, None) == E["UNSUPPORTED"]
     assert lib.fqm_gemm(ctypes.byref(mdbf()), FAKE, FAKE, 1, None) == E["UNSUPPORTED"]
