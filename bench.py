@@ -171,7 +171,7 @@ def main():
                 fn=lambda s, ws=mcopies, x=x, y=y, wsp=wsp: fqm.gemv(ws[s % len(ws)], x, y=y, workspace=wsp),
                 bytes=mcopies[0].nbytes() + x.numel() * 2 + y.numel() * 2,
                 flops=2 * b * 2 * cfg["l"] * cfg["r"] * (cfg["n"] + cfg["m"]), bound="alu",
-                kernel=f"mdbf_gemv batch {b} (2 launches)")
+                kernel=f"mdbf_gemv batch {b} (3 launches)")
     t_gen = time.time() - t_gen
     if args.profile and args.profile not in rows:
         print(f"unknown row {args.profile}; rows: {sorted(rows)}", file=sys.stderr)
