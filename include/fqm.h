@@ -179,9 +179,9 @@ fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
 /* Bytes of device workspace fqm_gemv needs for this descriptor and batch:
  * MDBF 6*P*l*batch*(roundup(m,256) + roundup(r,256)) (the dense operands of
  * both passes, each fp32 value as three bf16 parts); LUT6 with batch >= 2 and
- * cols a multiple of 1024 splits K over workgroups when there are few rows,
- * and then needs S*batch*rows*4 (S fp32 partial sums per output, S <= cols /
- * 1024, a function of rows and cols only), else 0; 0 for FABQ.
+ * cols a multiple of 512 splits K over workgroups unless rows >= 32768, and
+ * then needs S*batch*rows*4 (S fp32 partial sums per output, S <= cols / 512,
+ * a function of rows and cols only), else 0; 0 for FABQ.
  * Returns 0 for an invalid descriptor. */
 size_t fqm_workspace_size(const fqm_weights* w, int32_t batch);
 

@@ -1,7 +1,7 @@
 """GPU parity for the batch 2..16 per-row LUT 6-bit GEMV on the matrix cores
-("Qwen3.8-27B - BenQ 6-bit", "What BenQ stores"): cols a multiple of 1024,
-row counts that leave a partial 16-row block, and row counts small enough
-that K is split over workgroups (evenly, unevenly, one chunk per split)."""
+("Qwen3.8-27B - BenQ 6-bit", "What BenQ stores"): cols a multiple of 512,
+row counts that leave a partial 16-row block, and K split over workgroups
+(evenly, unevenly, one chunk per split)."""
 import numpy as np
 import pytest
 import torch
@@ -14,10 +14,10 @@ from gpu_common import (DEV, assert_close, bf16_dev, canaries_intact, guarded, l
 
 pytestmark = pytest.mark.gpu
 
-# (rows, cols, seed, batches): 1 chunk and a partial block; a 4-way split of
-# 4 chunks; 3 chunks in 3 splits; 17 chunks in 17 splits; 5 chunks, 5 splits;
-# 17 chunks in splits of 5, 5, 5, 2.  (K is split unless there are at least
-# 1024 row blocks of 16.)
+# (rows, cols, seed, batches), K in 512-wide chunks split into
+# ceil(chunks / ceil(chunks / ceil(2048 / row blocks))) parts:
+# 2 chunks in 2 splits with a partial row block; 8 in 8; 6 in 6; 34 in 34;
+# 10 in 10; 34 in splits of 5 (six) and 4.
 CASES = [(77, 1024, 9, (2, 16)), (300, 4096, 21, (3, 8)), (1000, 3072, 8, (5, 13)),
          (600, 17408, 10, (2, 8)), (2000, 5120, 5, (16,)), (4100, 17408, 4, (4,))]
 
@@ -41,10 +41,10 @@ def test_gemv_mfma_cases(rows, cols, seed, batches, out):
 
 
 def test_gemv_mfma_workspace_rule():
-    # few rows -> K split with workspace; 1024 or more row blocks -> none
-    assert fqm.workspace_size(lut6_weights(300, 4096, 21), 8) == 4 * 8 * 300 * 4
-    assert fqm.workspace_size(lut6_weights(4100, 17408, 4), 8) == 4 * 8 * 4100 * 4
-    assert fqm.workspace_size(lut6_weights(16384, 1024, 4), 8) == 0
+    # K is split while there are fewer than 2048 row blocks of 16
+    assert fqm.workspace_size(lut6_weights(300, 4096, 21), 8) == 8 * 8 * 300 * 4
+    assert fqm.workspace_size(lut6_weights(4100, 17408, 4), 8) == 7 * 8 * 4100 * 4
+    assert fqm.workspace_size(lut6_weights(32768, 1024, 4), 8) == 0
     assert fqm.workspace_size(lut6_weights(300, 4096, 21), 1) == 0
     # a too-small workspace is refused
     w = lut6_weights(300, 4096, 21)
