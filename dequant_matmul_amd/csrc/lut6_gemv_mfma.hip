@@ -48,7 +48,7 @@ constexpr int CH = 512;                        // k per chunk
 constexpr int PC = 2;                          // code chunks requested ahead
 constexpr int TILE = RB * CH * 2;              // one decoded W block (16 KB); an x block is XROWS KB
 constexpr int SLICES = CH / 32 / NW;           // k slices per wave per chunk
-constexpr int SPLIT_TARGET = 2048;             // aim for at least this many workgroups
+constexpr int SPLIT_TARGET = 1024;             // aim for at least this many workgroups
 
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t hi, uint32_t lo) {
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);

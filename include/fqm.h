@@ -179,7 +179,7 @@ fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
 /* Bytes of device workspace fqm_gemv needs for this descriptor and batch:
  * MDBF 6*P*l*batch*(roundup(m,256) + roundup(r,256)) (the dense operands of
  * both passes, each fp32 value as three bf16 parts); LUT6 with batch >= 2 and
- * cols a multiple of 512 splits K over workgroups unless rows >= 32768, and
+ * cols a multiple of 512 splits K over workgroups unless rows > 16368, and
  * then needs S*batch*rows*4 (S fp32 partial sums per output, S <= cols / 512,
  * a function of rows and cols only), else 0; 0 for FABQ.
  * Returns 0 for an invalid descriptor. */

@@ -77,12 +77,13 @@ def test_lut6_argument_errors(lib):
 
 def test_lut6_workspace_rule(lib):
     # batch >= 2 with cols % 512 == 0 splits K (512-wide chunks) while there
-    # are fewer than 2048 row blocks of 16: ceil(2048 / blocks) splits, capped
+    # are fewer than 1024 row blocks of 16: ceil(1024 / blocks) splits, capped
     # at the chunk count, evened out over the chunks; S*batch*rows fp32
     assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=4096, ld=3072)), 8) == 8 * 8 * 300 * 4
-    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=5120, cols=17408, ld=13056)), 8) == 7 * 8 * 5120 * 4
-    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=17408, cols=5120, ld=3840)), 8) == 2 * 8 * 17408 * 4
-    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=32768, cols=1024, ld=768)), 8) == 0
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=5120, cols=17408, ld=13056)), 8) == 4 * 8 * 5120 * 4
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=17408, cols=5120, ld=3840)), 8) == 0
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=16384, cols=1024, ld=768)), 8) == 0
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=16368, cols=1024, ld=768)), 8) == 2 * 8 * 16368 * 4
     assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=4096, ld=3072)), 1) == 0
     assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=4032, ld=3024)), 8) == 0
     # a missing workspace is refused before anything is enqueued

@@ -15,9 +15,9 @@ from gpu_common import (DEV, assert_close, bf16_dev, canaries_intact, guarded, l
 pytestmark = pytest.mark.gpu
 
 # (rows, cols, seed, batches), K in 512-wide chunks split into
-# ceil(chunks / ceil(chunks / ceil(2048 / row blocks))) parts:
+# ceil(chunks / ceil(chunks / ceil(1024 / row blocks))) parts:
 # 2 chunks in 2 splits with a partial row block; 8 in 8; 6 in 6; 34 in 34;
-# 10 in 10; 34 in splits of 5 (six) and 4.
+# 10 in 10; 34 in splits of 9, 9, 9, 7.
 CASES = [(77, 1024, 9, (2, 16)), (300, 4096, 21, (3, 8)), (1000, 3072, 8, (5, 13)),
          (600, 17408, 10, (2, 8)), (2000, 5120, 5, (16,)), (4100, 17408, 4, (4,))]
 
@@ -41,10 +41,10 @@ def test_gemv_mfma_cases(rows, cols, seed, batches, out):
 
 
 def test_gemv_mfma_workspace_rule():
-    # K is split while there are fewer than 2048 row blocks of 16
+    # K is split while there are fewer than 1024 row blocks of 16
     assert fqm.workspace_size(lut6_weights(300, 4096, 21), 8) == 8 * 8 * 300 * 4
-    assert fqm.workspace_size(lut6_weights(4100, 17408, 4), 8) == 7 * 8 * 4100 * 4
-    assert fqm.workspace_size(lut6_weights(32768, 1024, 4), 8) == 0
+    assert fqm.workspace_size(lut6_weights(4100, 17408, 4), 8) == 4 * 8 * 4100 * 4
+    assert fqm.workspace_size(lut6_weights(16384, 1024, 4), 8) == 0
     assert fqm.workspace_size(lut6_weights(300, 4096, 21), 1) == 0
     # a too-small workspace is refused
     w = lut6_weights(300, 4096, 21)
