@@ -16,9 +16,13 @@
 // as three bf16 columns, h0 = bf16(v), h1 = bf16(v - h0), h2 = bf16(v - h0 -
 // h1), whose sum carries the fp32 value (u is an exact fp32 product, v a
 // rounded one).  Three launches:
-//   prep:   D1[p][c][i] = part t of u_k[i] for column c = 3 (b l + k) + t;
-//   pass 1: sign products over S_B, then z and D2[p][c][j] = parts of v_k[j];
+//   prep:   D1 = parts of u_k[i], column 3 (b l + k) + t of batch slice b / bs;
+//   pass 1: sign products over S_B, then z and D2 = parts of v_k[j];
 //   pass 2: sign products over S_A for every path, then y.
+// D1 and D2 are stored fragment-major: for each batch slice, 32-column
+// block, 256-wide K block and 16-wide k slice, the 64 lanes' 16-byte MFMA
+// operand pieces are contiguous, so every operand load is one coalesced 1 KB
+// wave read.
 // A workgroup owns 32 rows and a batch slice; its 8 waves split K and their
 // partial sums are added in a fixed order in LDS, so results do not depend
 // on timing.  Columns past the logical width hold zeros in D1/D2, so the sign
@@ -34,7 +38,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NW = 8;        // waves per workgroup (K split)
+constexpr int NW1 = 16;      // waves per pass-1 workgroup (K split)
+constexpr int NW2 = 8;       // waves per pass-2 workgroup
 constexpr int KB = 256;      // columns per K block
 
 __host__ __device__ inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -43,8 +48,9 @@ __host__ __device__ inline int64_t round_up(int64_t v, int64_t a) { return (v + 
 __host__ __device__ inline int batch_slice(int l) { return 3 * l >= 64 ? 1 : 64 / (3 * l); }
 
 struct MdbfDims {
-    int64_t m_pad, r_pad;     // padded widths of D1 and D2 rows
-    int64_t cp;               // dense columns per path: 3 l batch
+    int64_t m_pad, r_pad;     // padded K widths of D1 and D2
+    int64_t nsg;              // batch slices
+    int64_t d1_path, d2_path; // elements of one path's D1 / D2
     size_t d1_elems, d2_elems;
 };
 
@@ -52,10 +58,24 @@ __host__ __device__ inline MdbfDims mdbf_dims(int64_t m, int64_t r, int l, int P
     MdbfDims d;
     d.m_pad = round_up(m, KB);
     d.r_pad = round_up(r, KB);
-    d.cp = 3LL * l * batch;
-    d.d1_elems = (size_t)P * d.cp * d.m_pad;
-    d.d2_elems = (size_t)P * d.cp * d.r_pad;
+    d.nsg = (batch + batch_slice(l) - 1) / batch_slice(l);
+    d.d1_path = d.nsg * (d.m_pad / KB) * 16384;
+    d.d2_path = d.nsg * (d.r_pad / KB) * 16384;
+    d.d1_elems = (size_t)P * d.d1_path;
+    d.d2_elems = (size_t)P * d.d2_path;
     return d;
+}
+
+// Element index of column lc (0..63) of batch slice sg at k in a fragment-major
+// operand with nkb 256-wide K blocks: slice s, lane half g, element e of k
+// within its K block follow the MFMA k order (k = 128 g + 8 s + e).
+__host__ __device__ inline int64_t dfrag_index(int64_t sg, int lc, int64_t k, int64_t nkb) {
+    const int nb = lc >> 5;
+    const int64_t kb = k >> 8;
+    const int rem = (int)(k & 255);
+    const int g = rem >> 7, s = (rem & 127) >> 3, e = rem & 7;
+    const int lane = (lc & 31) + 32 * g;
+    return ((((sg * 2 + nb) * nkb + kb) * 16 + s) * 64 + lane) * 8 + e;
 }
 
 // v = h0 + h1 + h2 (bf16 parts; each remainder is exact in fp32)
@@ -79,10 +99,11 @@ __device__ __forceinline__ bf16x8 expand_signs(uint32_t byte) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// D1[p][c][i]: c = 3 (b l + k) + t; zero for i >= m.
+// D1 of path p: parts of u_k[i] at column 3 (b l + k) + t of batch slice
+// b / bs; zero for i >= m.
 __global__ __launch_bounds__(256) void mdbf_prep(fqm_mdbf md, const uint16_t* __restrict__ x,
                                                  uint16_t* __restrict__ D1, int64_t m, int batch,
-                                                 int64_t m_pad) {
+                                                 int64_t m_pad, int64_t d1_path) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (p, b, k, i)
     const int l = md.l;
     const int64_t per_p = (int64_t)batch * l * m_pad;
@@ -96,48 +117,56 @@ __global__ __launch_bounds__(256) void mdbf_prep(fqm_mdbf md, const uint16_t* __
     const fqm_mdbf_path path = p == 0 ? md.path[0] : md.path[1];
     uint16_t h[3] = {0, 0, 0};
     if (i < m) split3_bf16(fp16_to_f32(path.B_amp[i * l + k]) * bf16_to_f32(x[(int64_t)b * m + i]), h);
-    const int64_t c = 3 * ((int64_t)b * l + k);
-    uint16_t* dp = D1 + (int64_t)p * 3 * batch * l * m_pad;
+    const int bs = batch_slice(l);
+    const int sg = b / bs, bl = b - sg * bs;
+    uint16_t* dp = D1 + (int64_t)p * d1_path;
 #pragma unroll
-    for (int t3 = 0; t3 < 3; ++t3) dp[(c + t3) * m_pad + i] = h[t3];
+    for (int t3 = 0; t3 < 3; ++t3) dp[dfrag_index(sg, 3 * (bl * l + k) + t3, i, m_pad / KB)] = h[t3];
 }
 
-// Sign products for one path: acc[nb] = S[row0 .. row0 + 31][:] * D[c0 + 32 nb + (0..31)][:]^T over
-// this wave's K blocks.  k order inside a 256-column block: slice s, lane half g, element e
-// -> column 128 g + 8 s + e (the same order for both operands).
+// Sign products for one path: acc[nb] = S[row0 .. row0 + 31][:] * (dense columns 32 nb + (0..31) of
+// batch slice sg)^T over this wave's K blocks.  k order inside a 256-column block: slice s, lane
+// half g, element e -> column 128 g + 8 s + e (the same order for both operands).
 template <int NB>
 __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int64_t ldS, int64_t rows,
-                                              const uint16_t* __restrict__ D, int64_t ldD, int64_t row0, int64_t c0, int64_t cend, int blk0, int blk1,
-                                              f32x16 (&acc)[NB]) {
+                                              const uint16_t* __restrict__ D, int64_t nkb, int64_t sg,
+                                              int64_t row0, int cend, int blk0, int blk1, f32x16 (&acc)[NB]) {
     const int lane = threadIdx.x & 63, g = lane >> 5, j = lane & 31;
     const uint8_t* srow = S + min(row0 + j, rows - 1) * ldS;
     const int64_t last16 = ldS - 16;  // the last 16-byte piece inside a row
-    // dense column c0 + 32 nb + j (columns past cend read as zeros)
+    // this lane's 16-byte pieces of column block nb (columns past cend read as zeros)
     const uint16_t* dcol[NB];
     bool dvalid[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const int64_t c = c0 + 32 * nb + j;
-        dvalid[nb] = c < cend;
-        dcol[nb] = D + (dvalid[nb] ? c : c0) * ldD + 128 * g;
+        dvalid[nb] = 32 * nb + j < cend;
+        dcol[nb] = D + (sg * 2 + nb) * nkb * 8192 + 8 * lane;
     }
     for (int blk = blk0; blk < blk1; ++blk) {
         const u32x4 sb = *reinterpret_cast<const u32x4*>(srow + min((int64_t)(32 * blk + 16 * g), last16));
-        // a clamped re-read only happens where the dense columns are zero
-        bf16x8 bf[NB][16];
+        // a clamped re-read only happens where the dense columns are zero;
+        // lanes of columns past cend fetch nothing; the 16 k slices go in
+        // groups of 16 / NB to bound the live operands
+        constexpr int SG = 16 / NB;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(dcol[nb] + (int64_t)KB * blk + 8 * s);
-                bf[nb][s] = __builtin_bit_cast(bf16x8, dvalid[nb] ? v : u32x4{0u, 0u, 0u, 0u});
-            }
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const bf16x8 a = expand_signs((sb[s >> 2] >> (8 * (s & 3))) & 255u);
+        for (int s0 = 0; s0 < 16; s0 += SG) {
+            bf16x8 bf[NB][SG];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[nb][s], acc[nb], 0, 0, 0);
+#pragma unroll
+                for (int s = 0; s < SG; ++s) {
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    if (dvalid[nb]) v = *reinterpret_cast<const u32x4*>(dcol[nb] + (int64_t)8192 * blk + 512 * (s0 + s));
+                    bf[nb][s] = __builtin_bit_cast(bf16x8, v);
+                }
+#pragma unroll
+            for (int s = 0; s < SG; ++s) {
+                const int ss = s0 + s;
+                const bf16x8 a = expand_signs((sb[ss >> 2] >> (8 * (ss & 3))) & 255u);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[nb][s], acc[nb], 0, 0, 0);
+            }
         }
     }
 }
@@ -145,7 +174,7 @@ __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int
 // Sum of the NW waves' partial blocks in a fixed tree order (waves w and
 // w + h for h = 4, 2, 1) into red[nb][row][col] (LDS).  D layout of a 32x32
 // block: lane l, item q -> row (q % 4) + 8 (q / 4) + 4 (l / 32), column l % 32.
-template <int NB>
+template <int NB, int NW>
 __device__ __forceinline__ void reduce_waves(f32x16 (&acc)[NB], float* buf, float* red) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
@@ -181,11 +210,13 @@ __device__ __forceinline__ void reduce_waves(f32x16 (&acc)[NB], float* buf, floa
 // D2[p][c][j] = parts of Q_U[j][k] z[j] (zero for j >= r, which the grid
 // covers up to r_pad).
 template <int NB>
-__global__ __launch_bounds__(64 * NW) void mdbf_pass1(fqm_mdbf md, const uint16_t* __restrict__ D1,
+__global__ __launch_bounds__(64 * NW1) void mdbf_pass1(fqm_mdbf md, const uint16_t* __restrict__ D1,
                                                       uint16_t* __restrict__ D2, int64_t m, int batch,
-                                                      int64_t m_pad, int64_t r_pad) {
-    __shared__ float red_buf[NW / 2 * NB * 1024];
+                                                      int64_t m_pad, int64_t r_pad, int64_t d1_path,
+                                                      int64_t d2_path) {
+    __shared__ float red_buf[NW1 / 2 * NB * 1024];
     __shared__ float red[NB * 1024];
+    __shared__ float qv_s[32 * 16], qu_s[32 * 16];  // Q_V, Q_U rows j0 .. j0 + 31
     const int p = blockIdx.z;
     const fqm_mdbf_path path = p == 0 ? md.path[0] : md.path[1];
     const int l = md.l;
@@ -193,11 +224,15 @@ __global__ __launch_bounds__(64 * NW) void mdbf_pass1(fqm_mdbf md, const uint16_
     const int bs = batch_slice(l);
     const int b0 = blockIdx.y * bs, nb_rows = min(bs, batch - b0);
     const int64_t j0 = (int64_t)blockIdx.x * 32;
-    const int64_t cp = 3LL * l * batch;
-    const uint16_t* Dp = D1 + (int64_t)p * cp * m_pad;
+    // the epilogue's envelope values, fetched before the long sign products
+    // (rows j0 .. j0 + 31 of the [r][l] arrays are one contiguous run)
+    const int64_t qo = j0 * l + threadIdx.x;
+    const bool qin = threadIdx.x < 32 * l && qo < r * l;
+    const uint16_t qv_h = qin ? path.Q_V[qo] : 0, qu_h = qin ? path.Q_U[qo] : 0;
+    const uint16_t* Dp = D1 + (int64_t)p * d1_path;
     const int wave = threadIdx.x >> 6;
     const int nblk = (int)(m_pad / KB);
-    const int per = (nblk + NW - 1) / NW;
+    const int per = (nblk + NW1 - 1) / NW1;
     const int blk0 = min(wave * per, nblk), blk1 = min(blk0 + per, nblk);
 
     f32x16 acc[NB];
@@ -205,13 +240,16 @@ __global__ __launch_bounds__(64 * NW) void mdbf_pass1(fqm_mdbf md, const uint16_
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[nb][q] = 0.f;
-    const int64_t c0 = 3LL * l * b0, cend = c0 + 3LL * l * nb_rows;
-    sign_products<NB>(path.S_B, path.ld_B, r, Dp, m_pad, j0, c0, cend, blk0, blk1, acc);
-    reduce_waves<NB>(acc, red_buf, red);
+    sign_products<NB>(path.S_B, path.ld_B, r, Dp, nblk, blockIdx.y, j0, 3 * l * nb_rows, blk0, blk1, acc);
+    if (threadIdx.x < 32 * l) {
+        qv_s[threadIdx.x] = fp16_to_f32(qv_h);
+        qu_s[threadIdx.x] = fp16_to_f32(qu_h);
+    }
+    reduce_waves<NB, NW1>(acc, red_buf, red);  // ends with a barrier
 
     // one thread per (row, batch row of the slice)
-    uint16_t* D2p = D2 + (int64_t)p * cp * r_pad;
-    for (int e = threadIdx.x; e < 32 * bs; e += 64 * NW) {
+    uint16_t* D2p = D2 + (int64_t)p * d2_path;
+    for (int e = threadIdx.x; e < 32 * bs; e += 64 * NW1) {
         const int jr = e & 31, bl = e >> 5;
         const int64_t jj = j0 + jr;
         if (bl >= nb_rows) continue;
@@ -222,37 +260,43 @@ __global__ __launch_bounds__(64 * NW) void mdbf_pass1(fqm_mdbf md, const uint16_
                 float t = 0.f;
 #pragma unroll
                 for (int t3 = 0; t3 < 3; ++t3) t += red[((cl + t3) >> 5) * 1024 + jr * 32 + ((cl + t3) & 31)];
-                z = fmaf(fp16_to_f32(path.Q_V[jj * l + k]), t, z);
+                z = fmaf(qv_s[jr * l + k], t, z);
             }
         }
         for (int k = 0; k < l; ++k) {
             uint16_t h[3] = {0, 0, 0};
-            if (jj < r) split3_bf16(fp16_to_f32(path.Q_U[jj * l + k]) * z, h);
-            const int64_t c = 3 * ((int64_t)(b0 + bl) * l + k);
+            if (jj < r) split3_bf16(qu_s[jr * l + k] * z, h);
 #pragma unroll
-            for (int t3 = 0; t3 < 3; ++t3) D2p[(c + t3) * r_pad + jj] = h[t3];
+            for (int t3 = 0; t3 < 3; ++t3) D2p[dfrag_index(blockIdx.y, 3 * (bl * l + k) + t3, jj, r_pad / KB)] = h[t3];
         }
     }
 }
 
 // Pass 2: rows i of S_A, summed over the paths; D2 columns of batch slice [b0, b0 + bs).
 template <int NB>
-__global__ __launch_bounds__(64 * NW) void mdbf_pass2(fqm_mdbf md, const uint16_t* __restrict__ D2,
+__global__ __launch_bounds__(64 * NW2) void mdbf_pass2(fqm_mdbf md, const uint16_t* __restrict__ D2,
                                                       void* __restrict__ y, int y_f32, int64_t n, int batch,
-                                                      int64_t r_pad) {
-    __shared__ float red_buf[NW / 2 * NB * 1024];
+                                                      int64_t r_pad, int64_t d2_path) {
+    __shared__ float red_buf[NW2 / 2 * NB * 1024];
     __shared__ float red[NB * 1024];
+    __shared__ float amp_s[2][32 * 16];  // A_amp rows i0 .. i0 + 31 of each path
     const int l = md.l;
     const int64_t r = md.r;
     const int bs = batch_slice(l);
     const int b0 = blockIdx.y * bs, nb_rows = min(bs, batch - b0);
     const int64_t i0 = (int64_t)blockIdx.x * 32;
-    const int64_t cp = 3LL * l * batch;
+    // the epilogue's envelope values, fetched before the long sign products
+    uint16_t amp_h[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int64_t ao = i0 * l + threadIdx.x;
+        const bool ain = p < md.P && threadIdx.x < 32 * l && ao < n * l;
+        amp_h[p] = ain ? md.path[p].A_amp[ao] : 0;
+    }
     const int wave = threadIdx.x >> 6;
     const int nblk = (int)(r_pad / KB);
-    const int per = (nblk + NW - 1) / NW;
+    const int per = (nblk + NW2 - 1) / NW2;
     const int blk0 = min(wave * per, nblk), blk1 = min(blk0 + per, nblk);
-    const int64_t c0 = 3LL * l * b0, cend = c0 + 3LL * l * nb_rows;
 
     float out[2] = {0.f, 0.f};  // (row, batch row) pairs e = tid, tid + 512 of this thread
     for (int p = 0; p < md.P; ++p) {
@@ -262,12 +306,16 @@ __global__ __launch_bounds__(64 * NW) void mdbf_pass2(fqm_mdbf md, const uint16_
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[nb][q] = 0.f;
-        sign_products<NB>(path.S_A, path.ld_A, n, D2 + (int64_t)p * cp * r_pad, r_pad, i0, c0, cend, blk0, blk1,
-                          acc);
-        reduce_waves<NB>(acc, red_buf, red);
+        sign_products<NB>(path.S_A, path.ld_A, n, D2 + (int64_t)p * d2_path, nblk, blockIdx.y, i0, 3 * l * nb_rows,
+                          blk0, blk1, acc);
+        if (p == 0 && threadIdx.x < 32 * l) {
+            amp_s[0][threadIdx.x] = fp16_to_f32(amp_h[0]);
+            amp_s[1][threadIdx.x] = fp16_to_f32(amp_h[1]);
+        }
+        reduce_waves<NB, NW2>(acc, red_buf, red);  // ends with a barrier
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int e = threadIdx.x + 64 * NW * h;
+            const int e = threadIdx.x + 64 * NW2 * h;
             const int ir = e & 31, bl = e >> 5;
             const int64_t ii = i0 + ir;
             if (bl >= nb_rows || ii >= n) continue;
@@ -277,7 +325,7 @@ __global__ __launch_bounds__(64 * NW) void mdbf_pass2(fqm_mdbf md, const uint16_
                 float t = 0.f;
 #pragma unroll
                 for (int t3 = 0; t3 < 3; ++t3) t += red[((cl + t3) >> 5) * 1024 + ir * 32 + ((cl + t3) & 31)];
-                v = fmaf(fp16_to_f32(path.A_amp[ii * l + k]), t, v);
+                v = fmaf(amp_s[p][ir * l + k], t, v);
             }
             out[h] = v;
         }
@@ -285,7 +333,7 @@ __global__ __launch_bounds__(64 * NW) void mdbf_pass2(fqm_mdbf md, const uint16_
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int e = threadIdx.x + 64 * NW * h;
+        const int e = threadIdx.x + 64 * NW2 * h;
         const int ir = e & 31, bl = e >> 5;
         const int64_t ii = i0 + ir;
         if (bl >= nb_rows || ii >= n) continue;
@@ -303,12 +351,12 @@ hipError_t launch_nb(const fqm_weights& w, const uint16_t* x, void* y, int y_f32
     const fqm_mdbf& md = w.mdbf;
     const int bs = batch_slice(md.l);
     const unsigned gy = (unsigned)((batch + bs - 1) / bs);
-    hipLaunchKernelGGL((mdbf_pass1<NB>), dim3((unsigned)(d.r_pad / 32), gy, (unsigned)md.P), dim3(64 * NW), 0, s,
-                       md, D1, D2, w.cols, batch, d.m_pad, d.r_pad);
+    hipLaunchKernelGGL((mdbf_pass1<NB>), dim3((unsigned)(d.r_pad / 32), gy, (unsigned)md.P), dim3(64 * NW1), 0, s,
+                       md, D1, D2, w.cols, batch, d.m_pad, d.r_pad, d.d1_path, d.d2_path);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mdbf_pass2<NB>), dim3((unsigned)((w.rows + 31) / 32), gy), dim3(64 * NW), 0, s, md, D2, y,
-                       y_f32, w.rows, batch, d.r_pad);
+    hipLaunchKernelGGL((mdbf_pass2<NB>), dim3((unsigned)((w.rows + 31) / 32), gy), dim3(64 * NW2), 0, s, md, D2, y,
+                       y_f32, w.rows, batch, d.r_pad, d.d2_path);
     return hipGetLastError();
 }
 
@@ -327,7 +375,7 @@ hipError_t launch_mdbf_gemv(const fqm_weights& w, const uint16_t* x, void* y, in
     uint16_t* D2 = D1 + d.d1_elems;
     const int64_t nprep = (int64_t)md.P * batch * md.l * d.m_pad;
     hipLaunchKernelGGL(mdbf_prep, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, s, md, x, D1, w.cols, batch,
-                       d.m_pad);
+                       d.m_pad, d.d1_path);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int bs = batch_slice(md.l);

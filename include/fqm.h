@@ -177,8 +177,10 @@ fqm_status fqm_unpack(const uint8_t* packed, uint8_t* codes, int64_t rows, int64
 fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
 
 /* Bytes of device workspace fqm_gemv needs for this descriptor and batch:
- * MDBF 6*P*l*batch*(roundup(m,256) + roundup(r,256)) (the dense operands of
- * both passes, each fp32 value as three bf16 parts); LUT6 with batch >= 2 and
+ * MDBF 128*P*S*(roundup(m,256) + roundup(r,256)) with S = ceil(batch / bs),
+ * bs = 1 if 3*l >= 64 else floor(64 / (3*l)) (the dense operands of both
+ * passes: each fp32 value as three bf16 parts, 64 columns per batch slice of
+ * bs rows); LUT6 with batch >= 2 and
  * cols a multiple of 512 splits K over workgroups unless rows > 16368, and
  * then needs S*batch*rows*4 (S fp32 partial sums per output, S <= cols / 512,
  * a function of rows and cols only), else 0; 0 for FABQ.

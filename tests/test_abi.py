@@ -143,8 +143,9 @@ def mdbf(r=2000, l=2, P=1, n=4096, m=4096):
 def test_mdbf_argument_errors_and_workspace(lib):
     w = mdbf()
     need = lib.fqm_workspace_size(ctypes.byref(w), 16)
-    # three bf16 parts per dense value, both passes, K padded to 256
-    assert need == 6 * 1 * 2 * 16 * (4096 + 2048)
+    # both passes' dense operands, 64 bf16 columns per batch slice (slices of
+    # 64 // (3 l) = 10 batch rows -> 2 slices), K padded to 256
+    assert need == 2 * 1 * 2 * 64 * (4096 + 2048)
     assert gemv(lib, w, batch=16, ws=None, wsb=0) == E["WORKSPACE"]
     assert gemv(lib, w, batch=16, ws=FAKE, wsb=need - 4) == E["WORKSPACE"]
     assert gemv(lib, mdbf(l=0)) == E["FORMAT"]
@@ -154,6 +155,6 @@ def test_mdbf_argument_errors_and_workspace(lib):
     w = mdbf()
     w.mdbf.path[0].ld_A = 240   # < ceil(2000/8)
     assert gemv(lib, w) == E["SHAPE"]
-    assert lib.fqm_workspace_size(ctypes.byref(mdbf(P=2)), 3) == 6 * 2 * 2 * 3 * (4096 + 2048)
+    assert lib.fqm_workspace_size(ctypes.byref(mdbf(P=2)), 3) == 2 * 2 * 1 * 64 * (4096 + 2048)
     assert lib.fqm_dequant(ctypes.byref(mdbf()), FAKE, None) == E["UNSUPPORTED"]
     assert lib.fqm_gemm(ctypes.byref(mdbf()), FAKE, FAKE, 1, None) == E["UNSUPPORTED"]
