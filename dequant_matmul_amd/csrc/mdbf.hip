@@ -146,8 +146,8 @@ __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int
         const u32x4 sb = *reinterpret_cast<const u32x4*>(srow + min((int64_t)(32 * blk + 16 * g), last16));
         // a clamped re-read only happens where the dense columns are zero;
         // lanes of columns past cend fetch nothing; the 16 k slices go in
-        // groups of 16 / NB to bound the live operands
-        constexpr int SG = 16 / NB;
+        // groups of 8 / NB to bound the live operands
+        constexpr int SG = 8 / NB;
 #pragma unroll
         for (int s0 = 0; s0 < 16; s0 += SG) {
             bf16x8 bf[NB][SG];
