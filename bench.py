@@ -127,10 +127,12 @@ def main():
         X = bf16(synth.activations(M, C["lut6_up"]["cols"], C["prefill"]["seed"]))
         Y = torch.empty((M, C["lut6_up"]["rows"]), dtype=torch.bfloat16, device=dev)
         Nn, K = C["lut6_up"]["rows"], C["lut6_up"]["cols"]
+        gws_bytes = fqm.gemm_workspace_size(ws[0], M)
+        gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev) if gws_bytes else None
         rows["prefill"] = dict(
-            fn=lambda s, ws=ws, X=X, Y=Y: fqm.gemm(ws[(s + 1) % len(ws)], X, Y=Y),
+            fn=lambda s, ws=ws, X=X, Y=Y, gws=gws: fqm.gemm(ws[(s + 1) % len(ws)], X, Y=Y, workspace=gws),
             bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * K,
-            bound="mfma", kernel="lut6_gemm")
+            bound="mfma", kernel="lut6_gemm (with its K-split last round and reduction)")
 
     # ---- FABQ (5120^2, the layer's drawn blocksize) ------------------------------
     fabq_bs = None

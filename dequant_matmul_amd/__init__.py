@@ -7,7 +7,7 @@ device memory and the current HIP stream; the functions take and return
 is not built, importing works but every call raises ``FqmNotBuilt``.
 
 Functions mirror the C ABI names: ``pack_bits``, ``pack``, ``unpack``,
-``dequant``, ``workspace_size``, ``gemv``, ``gemm``, ``version``,
+``dequant``, ``workspace_size``, ``gemv``, ``gemm_workspace_size``, ``gemm``, ``version``,
 ``status_str``.  Weight descriptors are built with ``Lut6Weights``,
 ``FabqWeights`` and ``MdbfWeights``; their ``from_*`` constructors upload
 unpacked host arrays and pack them on the GPU with ``fqm_pack_bits``.
@@ -28,13 +28,13 @@ FQM_BF16, FQM_F32 = 0, 1
 
 __all__ = [
     "FqmError", "FqmNotBuilt", "load", "version", "status_str", "pack_bits", "pack",
-    "unpack", "dequant", "workspace_size", "gemv", "gemm", "Lut6Weights", "FabqWeights",
+    "unpack", "dequant", "workspace_size", "gemv", "gemm_workspace_size", "gemm", "Lut6Weights", "FabqWeights",
     "MdbfWeights", "SYMBOLS",
 ]
 
 # Every symbol include/fqm.h declares.
 SYMBOLS = ("fqm_version", "fqm_status_str", "fqm_pack_bits", "fqm_pack", "fqm_unpack",
-           "fqm_dequant", "fqm_workspace_size", "fqm_gemv", "fqm_gemm")
+           "fqm_dequant", "fqm_workspace_size", "fqm_gemv", "fqm_gemm_workspace_size", "fqm_gemm")
 
 
 class FqmError(RuntimeError):
@@ -107,7 +107,9 @@ def load():
     lib.fqm_gemv.argtypes = [P(_Weights), c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                              ctypes.c_size_t, c_void_p]
     lib.fqm_gemm.restype = c_int32
-    lib.fqm_gemm.argtypes = [P(_Weights), c_void_p, c_void_p, c_int64, c_void_p]
+    lib.fqm_gemm.argtypes = [P(_Weights), c_void_p, c_void_p, c_int64, c_void_p, ctypes.c_size_t, c_void_p]
+    lib.fqm_gemm_workspace_size.restype = ctypes.c_size_t
+    lib.fqm_gemm_workspace_size.argtypes = [P(_Weights), c_int64]
     _lib = lib
     return lib
 
@@ -368,10 +370,20 @@ def gemv(w: _WeightsBase, x: torch.Tensor, y: torch.Tensor | None = None,
     return y
 
 
-def gemm(w: Lut6Weights, X: torch.Tensor, Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+def gemm_workspace_size(w: Lut6Weights, M: int) -> int:
+    return int(load().fqm_gemm_workspace_size(w.ref, M))
+
+
+def gemm(w: Lut6Weights, X: torch.Tensor, Y: torch.Tensor | None = None,
+         workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Y[M][rows] = X[M][cols] W^T in bf16 with fp32 accumulation."""
     M = X.shape[0]
     if Y is None:
         Y = torch.empty((M, w.rows), dtype=torch.bfloat16, device=X.device)
-    _check(load().fqm_gemm(w.ref, _ptr(X), _ptr(Y), M, _stream(stream)), "fqm_gemm")
+    need = gemm_workspace_size(w, M)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().fqm_gemm(w.ref, _ptr(X), _ptr(Y), M, _ptr(workspace), ws_bytes, _stream(stream)),
+           "fqm_gemm")
     return Y

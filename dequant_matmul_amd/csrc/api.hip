@@ -2,6 +2,8 @@
 // Nothing here allocates, synchronises or keeps state between calls.
 #include <string.h>
 
+#include <cstdint>
+
 #include "fqm_internal.h"
 
 using namespace fqm;
@@ -174,16 +176,27 @@ fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_
     return FQM_E_FORMAT;
 }
 
-fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_t M, void* stream) {
+size_t fqm_gemm_workspace_size(const fqm_weights* w, int64_t M) {
+    if (check_weights(w) != FQM_OK || w->format != FQM_LUT6 || M <= 0 || w->rows == 0) return 0;
+    if (w->cols % 64 || M * w->cols * 2 > INT32_MAX) return 0;
+    return fqm::lut6_gemm_workspace(*w, M);
+}
+
+fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_t M, void* workspace,
+                    size_t ws_bytes, void* stream) {
     const fqm_status st = check_weights(w);
     if (st != FQM_OK) return st;
     if (w->format != FQM_LUT6) return FQM_E_UNSUPPORTED;
     if (M < 0) return FQM_E_SHAPE;
     if (M > (int64_t)65535 * 128) return FQM_E_SHAPE;
     if (M == 0 || w->rows == 0) return FQM_OK;
-    if (!Y || (w->cols > 0 && !X)) return FQM_E_NULL;
-    if (!aligned16(Y) || (X && !aligned16(X))) return FQM_E_ALIGN;
-    return hip_status(launch_lut6_gemm(*w, X, Y, M, as_stream(stream)));
+    if (w->cols % 64 || M * w->cols * 2 > INT32_MAX) return FQM_E_SHAPE;
+    if (!Y || !X) return FQM_E_NULL;
+    if (!aligned16(Y) || !aligned16(X)) return FQM_E_ALIGN;
+    const size_t need = fqm_gemm_workspace_size(w, M);
+    if (need && (!workspace || ws_bytes < need)) return FQM_E_WORKSPACE;
+    if (need && !aligned16(workspace)) return FQM_E_ALIGN;
+    return hip_status(launch_lut6_gemm(*w, X, Y, M, workspace, ws_bytes, as_stream(stream)));
 }
 
 }  // extern "C"

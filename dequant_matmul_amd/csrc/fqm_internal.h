@@ -86,8 +86,9 @@ bool lut6_gemv_mfma_supported(const fqm_weights& w, int batch);
 size_t lut6_gemv_mfma_workspace(const fqm_weights& w, int batch);
 hipError_t launch_lut6_gemv_mfma(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
                                  float* ws, hipStream_t s);
-hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M,
-                            hipStream_t s);
+size_t lut6_gemm_workspace(const fqm_weights& w, int64_t M);
+hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M, void* ws,
+                            size_t ws_bytes, hipStream_t s);
 hipError_t launch_fabq_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
                             int batch, hipStream_t s);
 // MDBF: workspace holds the bf16 hi/lo dense operands of both passes.

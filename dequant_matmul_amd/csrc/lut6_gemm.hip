@@ -41,6 +41,7 @@
 // workgroup b computes M tile b % mtiles, so with M = 8 * BM each XCD keeps
 // one X panel (BM x K bf16, 2.6 MB at K = 5120) in its own L2 while the W
 // panels stream through.
+#include <algorithm>
 #include <type_traits>
 
 #include "fqm_internal.h"
@@ -58,7 +59,6 @@ typedef __attribute__((address_space(3))) uint8_t lds8;
 typedef __attribute__((address_space(3))) uint16_t lds16;
 typedef __attribute__((address_space(3))) const uint16_t lds16c;
 typedef __attribute__((address_space(3))) const u32x4 lds128c;
-typedef __attribute__((address_space(1))) const void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
 
 constexpr int BM = 256, BN = 256, BK = 64;
@@ -118,12 +118,18 @@ __device__ __forceinline__ void barrier_after_loads() {
     asm volatile("" ::: "memory");
 }
 
+// Workgroup b computes tile (M tile tt % mtiles, N tile nt0 + tt / mtiles),
+// tt = b / ksplit, over K steps [t0, t1) of its split b % ksplit.  PARTIAL:
+// the fp32 tile (all BM x BN values) goes to part[b]; otherwise the bf16
+// outputs inside M x N go to Y.
+template <bool PARTIAL>
 __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* __restrict__ X,
                                                                const uint8_t* __restrict__ packed,
                                                                int64_t ld,
                                                                const uint16_t* __restrict__ lut,
-                                                               uint16_t* __restrict__ Y, int M,
-                                                               int N, int K, int mtiles) {
+                                                               uint16_t* __restrict__ Y, float* __restrict__ part,
+                                                               int M, int N, int K, int mtiles, int nt0,
+                                                               int ksplit) {
     // Separate LDS objects: the X tiles are written by direct global -> LDS
     // loads, and distinct objects let the compiler see that the table
     // gathers do not wait for those loads.
@@ -136,7 +142,8 @@ __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* _
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x;
-    const int mt = b % mtiles, nt = b / mtiles;
+    const int tt = b / ksplit, ks = b - tt * ksplit;
+    const int mt = tt % mtiles, nt = nt0 + tt / mtiles;
     const int m0 = mt * BM, n0 = nt * BN;
     const int wn = wave;  // W rows 32 wn .. 32 wn + 31 of the tile
     const int g = lane >> 5, j = lane & 31;
@@ -156,21 +163,29 @@ __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* _
     asm volatile("" : "+v"(cmask));  // in a VGPR: (v & mask) | base is one v_and_or_b32
 
     // ---- X: direct global -> LDS, 1 KB (8 rows) per wave instruction -----------
-    // Load u of wave w fills rows 8 (8u + w) .. + 7; lane l lands at byte 16 l
-    // of that kilobyte (row + l / 8, stored chunk l % 8) and fetches the
-    // logical chunk that the swizzle puts there, (l % 8) ^ ((row / 2) % 8).
-    const uint16_t* xsrc[XDMA];
+    // Buffer loads with an LDS destination from the tile's X panel (the
+    // compiler tracks these exactly; the flat-address form makes it wait for
+    // every LDS read while one is in flight).  Load u of wave w fills rows
+    // 8 (8u + w) .. + 7; lane l lands at byte 16 l of that kilobyte (row +
+    // l / 8, stored chunk l % 8) and fetches the logical chunk that the
+    // swizzle puts there, (l % 8) ^ ((row / 2) % 8).  Rows past M repeat row
+    // M - 1 (never stored).
+    // X as one buffer (the host keeps M * K * 2 below 2^31); the tile's first
+    // row goes into the scalar offset.
+    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, 0x7fffffff, 0x00020000);
+    const uint32_t xtile = (uint32_t)m0 * (uint32_t)K * 2u;
+    uint32_t xoff[XDMA];
 #pragma unroll
     for (int u = 0; u < XDMA; ++u) {
         const int row = 8 * (8 * u + wave) + (lane >> 3);
         const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        xsrc[u] = X + (int64_t)min(m0 + row, M - 1) * K + 8 * chunk;
+        xoff[u] = (uint32_t)(min(row, M - 1 - m0) * K + 8 * chunk) * 2u;
     }
     auto dma_x = [&](int buf, int t) {
 #pragma unroll
         for (int u = 0; u < XDMA; ++u)
-            __builtin_amdgcn_global_load_lds((gvoid*)(xsrc[u] + t * BK), (lvoid*)(XS[buf] + 1024 * (8 * u + wave)), 16,
-                                             0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (lvoid*)(XS[buf] + 1024 * (8 * u + wave)), 16, xoff[u],
+                                                     xtile + (uint32_t)t * (BK * 2), 0, 0);
     };
 
     // ---- codes: 24 bytes of row 32 wn + j per lane per step, CD steps ahead -------
@@ -196,17 +211,19 @@ __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* _
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-    const int steps = K / BK;  // >= 1
+    const int ksteps = K / BK;
+    const int t0 = (int)((int64_t)ks * ksteps / ksplit), t1 = (int)((int64_t)(ks + 1) * ksteps / ksplit);
+    const int steps = t1 - t0;  // >= 1
     __builtin_assume(steps > 0);
-    // ---- prologue: tables, X(0), codes of steps 0 .. CD - 1 ------------------------
-    dma_x(0, 0);
+    // ---- prologue: tables, X(t0), codes of steps t0 .. t0 + CD - 1 -----------------
+    dma_x(0, t0);
 #pragma unroll
-    for (int u = 0; u < CD; ++u) load_codes(u, min(u, steps - 1));
+    for (int u = 0; u < CD; ++u) load_codes(u, t0 + min(u, steps - 1));
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
     // ---- main loop -----------------------------------------------------------------
-    // Step t (X buffer B = t % 2, code slot S = t % (CD + 1)): request X(t+1),
+    // Step t0 + t (X buffer B = t % 2, code slot S = t % (CD + 1)): request X(t+1),
     // then the codes of step t + CD, then the four slices of step t (operand
     // reads, gathers, MFMAs).  Before the closing barrier publishes X(t+1) the
     // wave waits until at most the two code loads of this step are in flight
@@ -216,9 +233,9 @@ __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* _
     auto step = [&](auto bufc, auto slotc, auto lastc, int t) {
         constexpr int B = decltype(bufc)::value, S = decltype(slotc)::value;
         constexpr bool LAST = decltype(lastc)::value;
-        dma_x(B ^ 1, min(t + 1, steps - 1));
+        dma_x(B ^ 1, t0 + min(t + 1, steps - 1));
         __builtin_amdgcn_sched_barrier(0);
-        load_codes((S + CD) % (CD + 1), min(t + CD, steps - 1));
+        load_codes((S + CD) % (CD + 1), t0 + min(t + CD, steps - 1));
         __builtin_amdgcn_sched_barrier(0);  // the loads go out first, in this order
         auto slice = [&](auto qc) {
             constexpr int q = decltype(qc)::value;
@@ -263,29 +280,129 @@ __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* _
     if (t + 2 < steps) step(Buf<0>{}, Buf<2>{}, Last{}, t + 2);
 
     // D layout of a 32x32 block: lane l, item r -> row (r % 4) + 8 * (r / 4) + 4 * (l / 32), column l % 32.
-    const int n = n0 + 32 * wn + j;
+    if constexpr (PARTIAL) {
+        float* pt = part + (size_t)b * (BM * BN) + 32 * wn + j;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = m0 + 32 * i + (r & 3) + 8 * (r >> 2) + 4 * g;
-            if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16(acc[i][r]);
-        }
+            for (int r = 0; r < 16; ++r) pt[(32 * i + (r & 3) + 8 * (r >> 2) + 4 * g) * BN] = acc[i][r];
+    } else {
+        const int n = n0 + 32 * wn + j;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + 32 * i + (r & 3) + 8 * (r >> 2) + 4 * g;
+                if (m < M && n < N) Y[(int64_t)m * N + n] = f32_to_bf16(acc[i][r]);
+            }
+    }
+}
+
+// Y for the split tiles: the ksplit fp32 partial tiles of tile tt summed in
+// split order (a fixed order), rounded once to bf16.  Thread: 4 consecutive
+// columns of one tile row.
+__global__ __launch_bounds__(256) void lut6_gemm_reduce(const float* __restrict__ part, uint16_t* __restrict__ Y,
+                                                        int M, int N, int mtiles, int nt0, int ksplit,
+                                                        int64_t groups) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (tile, row, column group)
+    if (e >= groups) return;
+    constexpr int G = BN / 4;
+    const int64_t tt = e / (BM * G);
+    const int rem = (int)(e - tt * (BM * G));
+    const int ml = rem / G, nl = 4 * (rem - ml * G);
+    const int mt = (int)(tt % mtiles), nt = nt0 + (int)(tt / mtiles);
+    const int m = mt * BM + ml, n = nt * BN + nl;
+    if (m >= M) return;
+    const float* p = part + (size_t)tt * ksplit * (BM * BN) + ml * BN + nl;
+    float4 sum = *reinterpret_cast<const float4*>(p);
+    for (int k = 1; k < ksplit; ++k) {
+        const float4 v = *reinterpret_cast<const float4*>(p + (size_t)k * (BM * BN));
+        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+    uint16_t* y = Y + (int64_t)m * N + n;
+    if (n + 0 < N) y[0] = f32_to_bf16(sum.x);
+    if (n + 1 < N) y[1] = f32_to_bf16(sum.y);
+    if (n + 2 < N) y[2] = f32_to_bf16(sum.z);
+    if (n + 3 < N) y[3] = f32_to_bf16(sum.w);
+}
+
+// Tile plan.  One workgroup per compute unit; whole rounds of tiles run as
+// one launch.  The N tiles left for a last, partial round are split along K
+// (ksplit parts of at least MIN_SPLIT_STEPS steps) so that they occupy every
+// compute unit, and their fp32 partial tiles are reduced afterwards.
+constexpr int MIN_SPLIT_STEPS = 8;
+
+struct GemmPlan {
+    int mtiles = 0, ntiles = 0;
+    int nt_main = 0;      // N tiles [0, nt_main) in the direct launch
+    int ksplit = 1;       // K parts of each remaining tile
+    int64_t tail = 0;     // remaining tiles ((ntiles - nt_main) * mtiles)
+    size_t ws_bytes = 0;  // tail * ksplit fp32 partial tiles
+};
+
+GemmPlan gemm_plan(int64_t rows, int64_t cols, int64_t M, int cus) {
+    GemmPlan p;
+    p.mtiles = (int)((M + BM - 1) / BM);
+    p.ntiles = (int)((rows + BN - 1) / BN);
+    p.nt_main = p.ntiles;
+    const int64_t tiles = (int64_t)p.mtiles * p.ntiles, slots = std::max(cus, 1);
+    if (tiles % slots == 0) return p;
+    const int nt_main = (int)((tiles / slots) * slots / p.mtiles);
+    const int64_t tail = (int64_t)(p.ntiles - nt_main) * p.mtiles;
+    const int ksplit = (int)std::min<int64_t>(slots / tail, cols / BK / MIN_SPLIT_STEPS);
+    if (ksplit < 2) return p;
+    p.nt_main = nt_main;
+    p.ksplit = ksplit;
+    p.tail = tail;
+    p.ws_bytes = (size_t)tail * ksplit * BM * BN * sizeof(float);
+    return p;
+}
+
+hipError_t device_cus(int* cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return e;
 }
 
 }  // namespace
 
-hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M,
-                            hipStream_t s) {
-    if (w.cols % BK || w.rows > 0x7fffffff || M > 0x7fffffff || w.cols > 0x7fffffff)
+size_t lut6_gemm_workspace(const fqm_weights& w, int64_t M) {
+    int cus = 0;
+    if (M <= 0 || device_cus(&cus) != hipSuccess) return 0;
+    return gemm_plan(w.rows, w.cols, M, cus).ws_bytes;
+}
+
+hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M, void* ws,
+                            size_t ws_bytes, hipStream_t s) {
+    if (w.cols % BK || w.rows > 0x7fffffff || M > 0x7fffffff || w.cols > 0x7fffffff ||
+        M * w.cols * 2 > 0x7fffffff)
         return hipErrorInvalidValue;
-    const int mtiles = (int)((M + BM - 1) / BM);
-    const int64_t ntiles = (w.rows + BN - 1) / BN;
-    if (ntiles * mtiles > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(lut6_gemm_kernel, dim3((unsigned)(ntiles * mtiles)), dim3(64 * NWAVE), 0, s,
-                       X, w.lut6.packed, w.lut6.ld, w.lut6.lut, Y, (int)M, (int)w.rows, (int)w.cols,
-                       mtiles);
-    return hipGetLastError();
+    int cus = 0;
+    hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    const GemmPlan p = gemm_plan(w.rows, w.cols, M, cus);
+    if ((int64_t)p.ntiles * p.mtiles > 0x7fffffff) return hipErrorInvalidValue;
+    if (p.ws_bytes > ws_bytes || (p.ws_bytes && !ws)) return hipErrorInvalidValue;
+    const int64_t main_tiles = (int64_t)p.nt_main * p.mtiles;
+    if (main_tiles > 0) {
+        hipLaunchKernelGGL(lut6_gemm_kernel<false>, dim3((unsigned)main_tiles), dim3(64 * NWAVE), 0, s, X,
+                           w.lut6.packed, w.lut6.ld, w.lut6.lut, Y, nullptr, (int)M, (int)w.rows, (int)w.cols,
+                           p.mtiles, 0, 1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (p.tail > 0) {
+        float* part = static_cast<float*>(ws);
+        hipLaunchKernelGGL(lut6_gemm_kernel<true>, dim3((unsigned)(p.tail * p.ksplit)), dim3(64 * NWAVE), 0, s, X,
+                           w.lut6.packed, w.lut6.ld, w.lut6.lut, Y, part, (int)M, (int)w.rows, (int)w.cols,
+                           p.mtiles, p.nt_main, p.ksplit);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t groups = p.tail * BM * (BN / 4);
+        hipLaunchKernelGGL(lut6_gemm_reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, part, Y,
+                           (int)M, (int)w.rows, p.mtiles, p.nt_main, p.ksplit, groups);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace fqm

@@ -198,12 +198,25 @@ size_t fqm_workspace_size(const fqm_weights* w, int32_t batch);
 fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
                     int32_t batch, void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace fqm_gemm needs for this LUT6 descriptor and M on
+ * the current device: 256 * 256 * 4 bytes per K part of each 256 x 256 output
+ * tile of a last, partial round of tiles (one round = one tile per compute
+ * unit), when such tiles are split along K; 0 when nothing is split.  A
+ * function of rows, cols, M and the device's compute-unit count.  Returns 0
+ * for an invalid or non-LUT6 descriptor. */
+size_t fqm_gemm_workspace_size(const fqm_weights* w, int64_t M);
+
 /* Y = X W^T for a LUT6 descriptor (prefill): X [M][cols] bf16, Y [M][rows]
- * bf16, both row-major.  W tiles are decoded to bf16 in on-chip memory (exact:
- * the levels are bf16) and contracted on the bf16 matrix cores with fp32
- * accumulation.  FABQ / MDBF descriptors return FQM_E_UNSUPPORTED. */
+ * bf16, both row-major; cols a multiple of 64 and M * cols * 2 < 2^31
+ * (FQM_E_SHAPE otherwise).  Each weight is gathered from its row's table
+ * (exact: the levels are bf16) straight into the operands of the bf16 matrix
+ * cores, fp32 accumulation.  workspace: device memory of at least
+ * fqm_gemm_workspace_size(w, M) bytes, 16-byte aligned (may be NULL when that
+ * is 0); its contents on entry do not matter and are clobbered.  Split tiles
+ * add their fp32 K parts in a fixed order, so results do not depend on timing.
+ * FABQ / MDBF descriptors return FQM_E_UNSUPPORTED. */
 fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_t M,
-                    void* stream);
+                    void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

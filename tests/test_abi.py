@@ -52,6 +52,10 @@ def gemv(lib, w, x=FAKE, y=FAKE, dt=0, batch=1, ws=None, wsb=0):
     return lib.fqm_gemv(ctypes.byref(w), x, y, dt, batch, ws, wsb, None)
 
 
+def gemm(lib, w, X=FAKE, Y=FAKE, M=4, ws=None, wsb=0):
+    return lib.fqm_gemm(ctypes.byref(w), X, Y, M, ws, wsb, None)
+
+
 def test_lut6_argument_errors(lib):
     assert lib.fqm_gemv(None, FAKE, FAKE, 0, 1, None, 0, None) == E["NULL"]
     assert gemv(lib, lut6(cols=100)) == E["SHAPE"]            # cols % 64
@@ -70,9 +74,15 @@ def test_lut6_argument_errors(lib):
     assert gemv(lib, lut6(rows=-1)) == E["SHAPE"]
     # empty work returns before any launch
     assert gemv(lib, lut6(rows=0, packed=None, lut=None)) == E["OK"]
-    assert lib.fqm_gemm(ctypes.byref(lut6()), FAKE, FAKE, 0, None) == E["OK"]
-    assert lib.fqm_gemm(ctypes.byref(lut6()), FAKE, FAKE, -1, None) == E["SHAPE"]
-    assert lib.fqm_gemm(ctypes.byref(lut6()), None, FAKE, 4, None) == E["NULL"]
+    assert gemm(lib, lut6(), M=0) == E["OK"]
+    assert gemm(lib, lut6(), M=-1) == E["SHAPE"]
+    assert gemm(lib, lut6(), X=None) == E["NULL"]
+    assert gemm(lib, lut6(), Y=FAKE + 2) == E["ALIGN"]
+    # X must stay below 2 GiB (buffer addressing): M * cols * 2 < 2^31
+    assert gemm(lib, lut6(cols=65536, ld=49152), M=16384) == E["SHAPE"]
+    assert lib.fqm_gemm_workspace_size(ctypes.byref(lut6()), 0) == 0
+    assert lib.fqm_gemm_workspace_size(ctypes.byref(lut6()), -3) == 0
+    assert lib.fqm_gemm_workspace_size(None, 4) == 0
 
 
 def test_lut6_workspace_rule(lib):
@@ -124,7 +134,8 @@ def test_fabq_argument_errors(lib):
     assert gemv(lib, w) == E["NULL"]
     w = fabq(n_hi=64)  # no binary rows: their pointers are not needed
     w.fabq.codebook = w.fabq.signs = None
-    assert lib.fqm_gemm(ctypes.byref(w), FAKE, FAKE, 1, None) == E["UNSUPPORTED"]
+    assert gemm(lib, w, M=1) == E["UNSUPPORTED"]
+    assert lib.fqm_gemm_workspace_size(ctypes.byref(w), 1) == 0
     assert lib.fqm_workspace_size(ctypes.byref(fabq()), 4) == 0
 
 
@@ -157,4 +168,4 @@ def test_mdbf_argument_errors_and_workspace(lib):
     assert gemv(lib, w) == E["SHAPE"]
     assert lib.fqm_workspace_size(ctypes.byref(mdbf(P=2)), 3) == 2 * 2 * 1 * 64 * (4096 + 2048)
     assert lib.fqm_dequant(ctypes.byref(mdbf()), FAKE, None) == E["UNSUPPORTED"]
-    assert lib.fqm_gemm(ctypes.byref(mdbf()), FAKE, FAKE, 1, None) == E["UNSUPPORTED"]
+    assert gemm(lib, mdbf(), M=1) == E["UNSUPPORTED"]

@@ -46,3 +46,53 @@ def test_gemm_matches_gemv_rows():
     y = fqm.gemv(w, X, out_dtype=torch.float32)
     # both follow the same definition; they differ only by summation order
     assert_close(to_f64(Y), to_f64(y), "bf16")
+
+
+
+def _plan_ws(rows, cols, M):
+    """Workspace rule of the tile plan: whole rounds of 256 x 256 tiles (one per
+    compute unit) run directly; the N tiles of a last partial round split K
+    into min(CUs // tail tiles, steps // 8) parts (when >= 2) of fp32 tiles."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mt, nt = -(-M // 256), -(-rows // 256)
+    tiles = mt * nt
+    if tiles % cus == 0:
+        return 0
+    nt_main = (tiles // cus) * cus // mt
+    tail = (nt - nt_main) * mt
+    ks = min(cus // tail, cols // 64 // 8)
+    return tail * ks * 256 * 256 * 4 if ks >= 2 else 0
+
+
+@pytest.mark.parametrize("rows,cols,M", [(520, 1088, 300), (17408, 5120, 2048), (300, 128, 50),
+                                         (5120, 17408, 77)])
+def test_gemm_workspace_rule(rows, cols, M):
+    w = lut6_weights(256, cols, 1)
+    w.desc.rows = rows  # the rule reads the shape only (no launch)
+    assert fqm.gemm_workspace_size(w, M) == _plan_ws(rows, cols, M)
+
+
+def test_gemm_missing_workspace_is_an_error():
+    rows, cols, M = 520, 1088, 64
+    w = lut6_weights(rows, cols, 9)
+    assert fqm.gemm_workspace_size(w, M) > 0
+    X = bf16_dev(synth.activations(M, cols, 1))
+    Y = torch.empty((M, rows), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fqm.FqmError) as err:
+        fqm.gemm(w, X, Y=Y, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert err.value.status == 5  # FQM_E_WORKSPACE
+
+
+@pytest.mark.parametrize("rows,cols,M", [(300, 128, 50), (700, 192, 257)])
+def test_gemm_unsplit_short_k(rows, cols, M):
+    """K too short to split (fewer than 16 steps of 64): every tile in the
+    direct launch, no workspace."""
+    inp, packed = lut6_case(rows, cols, 5)
+    w = lut6_weights(rows, cols, 5)
+    assert fqm.gemm_workspace_size(w, M) == 0
+    X = synth.activations(M, cols, 6)
+    buf, Y = guarded((M, rows), torch.bfloat16)
+    fqm.gemm(w, bf16_dev(X), Y=Y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(Y), oracle.lut6.gemm(packed, inp.lut, X, cols), "bf16", f"rows={rows}")
