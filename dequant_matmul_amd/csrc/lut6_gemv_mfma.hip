@@ -8,17 +8,25 @@
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulate) and the decode stays the
 // batch-independent part:
 //   - A workgroup owns 16 rows (one MFMA row block) and a range of 512-wide
-//     K chunks.  A wave instruction decodes two rows (32 lanes each; the two
-//     tables sit in opposite halves of the 64 banks): lane j loads the row's
-//     12-byte piece j (16 codes) and gathers its 16 weights from the row's
-//     128-byte table in LDS.
-//   - The decoded 16 x 512 bf16 block and the 16 x 512 x block (batch rows
-//     past the batch are not loaded; their output columns are not stored)
-//     sit in LDS, double-buffered, as 1024-byte rows whose 16-byte chunks
-//     are permuted and XOR-swizzled, so the decode writes, the x stores (x
-//     staged through registers with coalesced loads one chunk ahead) and
-//     both MFMA operand reads are free of bank conflicts.  Every wave multiplies a quarter of
-//     the chunk's 32-wide k slices.
+//     K chunks; wave w takes k [64 w, 64 w + 64) of every chunk.
+//   - Codes arrive with coalesced loads (a wave instruction reads 384
+//     contiguous bytes of each of two rows) four chunks ahead and pass
+//     through a small LDS buffer (16 rows x 384 bytes per chunk), because
+//     the operand layout wants 16 rows per wave instruction.
+//   - Weights are gathered straight into the MFMA row operand: lane
+//     (r = lane % 16, g = lane / 16) reads the 12-byte piece of row r holding
+//     codes [16 g, 16 g + 16) of the wave's 64 k, gathers the 16 bf16 values
+//     from row r's table and packs them into the operands of the wave's two
+//     32-wide k slices (slice s uses codes 16 g + 8 s + e; the x operand is
+//     read in the same k order).  W never passes through LDS as a tile.
+//   - Tables: each row's table is held four times, one copy per lane group
+//     g, entry e of (row r, copy g) at 256 e + 4 (16 g + r): the 64 lanes of a
+//     gather hit 64 distinct banks, whatever the codes.
+//   - x chunks (batch rows past the batch are not loaded; their output
+//     columns are not stored) sit in LDS, double-buffered, as 1024-byte rows
+//     with XOR-swizzled 16-byte chunks; x is staged through registers with
+//     coalesced loads one chunk ahead.  The gathers run one chunk ahead of
+//     their MFMAs.
 //   - The waves' 16 x 16 partial results are added in wave order; K is
 //     split over workgroups so that the grid covers the chip several times,
 //     the partials go to the workspace and a second kernel adds them in
@@ -35,6 +43,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds8;
+typedef __attribute__((address_space(3))) uint16_t lds16;
+typedef __attribute__((address_space(3))) uint32_t lds32;
 typedef __attribute__((address_space(3))) const uint16_t lds16c;
 typedef __attribute__((address_space(3))) u32x4 lds128;
 typedef __attribute__((address_space(3))) const u32x4 lds128c;
@@ -43,30 +53,30 @@ typedef __attribute__((address_space(3))) const float ldsf;
 
 constexpr int RB = 16;                         // rows per workgroup
 constexpr int NW = 8;                          // waves per workgroup
-constexpr int PPW = RB / 2 / NW;               // row pairs each wave decodes per chunk
 constexpr int CH = 512;                        // k per chunk
-constexpr int PC = 2;                          // code chunks requested ahead
-constexpr int TILE = RB * CH * 2;              // one decoded W block (16 KB); an x block is XROWS KB
+constexpr int CSLOTS = 4;                      // code register slots: chunks are loaded 4 steps ahead
+constexpr int CB_ROW = 400;                    // code buffer row stride (384 bytes + 16: conflict-free reads)
 constexpr int SLICES = CH / 32 / NW;           // k slices per wave per chunk
+constexpr int TAB_BYTES = 64 * 256;            // 16 rows x 4 copies x 64 entries, 4-byte slots
 constexpr int SPLIT_TARGET = 1024;             // aim for at least this many workgroups
+static_assert(SLICES == 2 && CH == 64 * NW, "a wave takes 64 k of a chunk: 16 codes per lane");
 
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t hi, uint32_t lo) {
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// Code j of a 12-byte piece, shifted so that its 6 bits sit at bits 1..6
-// (the byte offset of its table entry) with other bits still to be masked.
+// Table offset of code J of a 12-byte piece d0..d2: the code's 6 bits moved
+// to bits 8..13 (entry stride 256 bytes), other bits still to be masked.
 template <int J>
-__device__ __forceinline__ uint32_t code_x2(uint32_t d0, uint32_t d1, uint32_t d2) {
-    constexpr int bit = 6 * J;
-    if constexpr (bit == 0) return d0 << 1;
-    else if constexpr (bit + 6 <= 32) return d0 >> (bit - 1);
-    else if constexpr (bit < 32) return __builtin_amdgcn_alignbit(d1, d0, bit - 1);
-    else if constexpr (bit == 32) return d1 << 1;
-    else if constexpr (bit + 6 <= 64) return d1 >> (bit - 33);
-    else if constexpr (bit < 64) return __builtin_amdgcn_alignbit(d2, d1, bit - 33);
-    else if constexpr (bit == 64) return d2 << 1;
-    else return d2 >> (bit - 65);
+__device__ __forceinline__ uint32_t code_x256(uint32_t d0, uint32_t d1, uint32_t d2) {
+    constexpr int bit = 6 * J, w = bit >> 5, o = bit & 31;
+    const uint32_t d[3] = {d0, d1, d2};
+    if constexpr (o + 6 <= 32) {
+        if constexpr (o >= 8) return d[w] >> (o - 8);
+        else return d[w] << (8 - o);
+    } else {
+        return __builtin_amdgcn_alignbit(d[w + 1], d[w], o - 8);
+    }
 }
 
 // Byte offset of 16-byte chunk q (k = 8q .. 8q+7) of row r in a [16][512]
@@ -77,74 +87,68 @@ __device__ __forceinline__ uint32_t tpos(uint32_t r, uint32_t q) {
     return r * 1024u + 16u * (q ^ r ^ ((q >> 4) & 1u));
 }
 
-// W block layout: chunk q of row r at slot ((q / 2) | (q % 2) * 32) ^ r.  A
-// decode write instruction covers chunks 2j (or 2j + 1) of a row for 32
-// consecutive j, i.e. 32 consecutive slots; with the layout above (stride-2
-// chunks) those writes measured about 8 bank-conflict cycles per
-// instruction, with this one none, and the MFMA row-fragment reads (16 rows,
-// one chunk) stay conflict-free.
-__device__ __forceinline__ uint32_t wpos(uint32_t r, uint32_t q) {
-    return r * 1024u + 16u * (((q >> 1) | ((q & 1u) << 5)) ^ (r & 15u));
-}
-
 // XROWS: batch rows an x block holds (8 or 16, >= batch); XPT = XROWS / 8
-// 16-byte x pieces per thread per chunk.  With XROWS = 8 a workgroup uses
-// about 50 KB of LDS and three fit on a CU.
+// 16-byte x pieces per thread per chunk.
 template <int XROWS>
 __global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
     const uint8_t* __restrict__ packed, int64_t ld, const uint16_t* __restrict__ lut,
     const uint16_t* __restrict__ x, void* __restrict__ y, int y_f32, float* __restrict__ part,
     int rows, int cols, int batch, int nblocks, int cps) {
-    __shared__ __attribute__((aligned(1024))) uint8_t s_tab[RB * 128];  // low addresses: immediate offsets
-    __shared__ __attribute__((aligned(16))) uint8_t s_w0[TILE];
-    __shared__ __attribute__((aligned(16))) uint8_t s_w1[TILE];
+    __shared__ __attribute__((aligned(16))) uint8_t s_tab[TAB_BYTES];
     constexpr int XPT = XROWS / 8;
     __shared__ __attribute__((aligned(16))) uint8_t s_x0[XROWS * 1024];
     __shared__ __attribute__((aligned(16))) uint8_t s_x1[XROWS * 1024];
-    static_assert(NW * 64 * 16 <= TILE, "the reduction reuses a W buffer");
+    __shared__ __attribute__((aligned(16))) uint8_t s_c0[RB * CB_ROW];
+    __shared__ __attribute__((aligned(16))) uint8_t s_c1[RB * CB_ROW];
+    lds8* const CB[2] = {(lds8*)s_c0, (lds8*)s_c1};
     lds8* const TAB = (lds8*)s_tab;
-    lds8* const WS[2] = {(lds8*)s_w0, (lds8*)s_w1};
     lds8* const XS[2] = {(lds8*)s_x0, (lds8*)s_x1};
-    lds8* const RED = (lds8*)s_w0;  // after the K loop
+    lds8* const RED = (lds8*)s_tab;  // after the K loop
+    static_assert(NW * 64 * 16 <= TAB_BYTES, "the reduction reuses the tables");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = lane >> 5, j = lane & 31;
+    const int r16 = lane & 15, g = lane >> 4;
     const int blk = blockIdx.x % nblocks, ks = blockIdx.x / nblocks;
     const int n0 = blk * RB;
     const int nch = cols / CH;
     const int c0 = ks * cps, c1 = min(c0 + cps, nch);  // this workgroup's chunks [c0, c1)
     const int n = c1 - c0;
 
-    // row tables
-    if (tid < RB * 8) {
-        const int r = tid >> 3, part8 = tid & 7;
+    // row tables, four copies: thread t writes copy t / 128 of entries
+    // 8 (t % 8) .. + 7 of row (t / 8) % 16
+    {
+        const int r = (tid >> 3) & 15, part8 = tid & 7, cp = tid >> 7;
         const u32x4 v = *reinterpret_cast<const u32x4*>(lut + (int64_t)min(n0 + r, rows - 1) * 64 + part8 * 8);
-        *(lds128*)(TAB + 16 * tid) = v;
-    }
-
-    // this wave decodes rows 2 (wave + NW u) + h, u < PPW; lane j takes piece j
-    const uint8_t* prow[PPW];
-    uint32_t tabrow[PPW];  // table offsets, multiples of 128: (code & mask) | tabrow is one v_and_or_b32
+        lds8* dst = TAB + 256 * 8 * part8 + 4 * (16 * cp + r);
 #pragma unroll
-    for (int u = 0; u < PPW; ++u) {
-        const int r = 2 * (wave + NW * u) + h;
-        prow[u] = packed + (int64_t)min(n0 + r, rows - 1) * ld + (int64_t)384 * c0 + 12 * j;
-        tabrow[u] = (uint32_t)(128 * r);
+        for (int e = 0; e < 8; ++e) *(lds16*)(dst + 256 * e) = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
     }
-    uint32_t cr[PC + 1][PPW][3];
-    // codes of chunk c0 + c of the two rows (clamped to the last chunk) into
-    // register slot cs % (PC + 1) (cs: a compile-time number congruent to c)
+    static_assert(64 * NW == RB * 8 * 4, "one table item per thread");
+
+    // Global code loads: wave w, lane half h, lane j = lane % 32 loads the
+    // 12-byte piece j of row 2 w + h.  Chunk c goes to register slot
+    // c % CSLOTS, then to the code buffer.
+    const int crow = 2 * wave + (lane >> 5), cpiece = lane & 31;
+    const uint8_t* prow = packed + (int64_t)min(n0 + crow, rows - 1) * ld + (int64_t)384 * c0 + 12 * cpiece;
+    uint32_t cr[CSLOTS][3];
     auto load_codes = [&](int cs, int c) {
         const int cc = min(c, n - 1);
-#pragma unroll
-        for (int u = 0; u < PPW; ++u) {
-            const uint32_t* q = reinterpret_cast<const uint32_t*>(prow[u] + 384 * cc);
-            cr[cs % (PC + 1)][u][0] = __builtin_nontemporal_load(q);
-            cr[cs % (PC + 1)][u][1] = __builtin_nontemporal_load(q + 1);
-            cr[cs % (PC + 1)][u][2] = __builtin_nontemporal_load(q + 2);
-        }
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(prow + 384 * cc);
+        cr[cs % CSLOTS][0] = __builtin_nontemporal_load(q);
+        cr[cs % CSLOTS][1] = __builtin_nontemporal_load(q + 1);
+        cr[cs % CSLOTS][2] = __builtin_nontemporal_load(q + 2);
     };
+    auto store_codes = [&](int cs, int buf) {
+        lds8* d = CB[buf] + CB_ROW * crow + 12 * cpiece;
+        *(lds32*)d = cr[cs % CSLOTS][0];
+        *(lds32*)(d + 4) = cr[cs % CSLOTS][1];
+        *(lds32*)(d + 8) = cr[cs % CSLOTS][2];
+    };
+    // lane (r16, g): row n0 + r16, codes [64 wave + 16 g, + 16) of each chunk
+    const uint32_t cread = (uint32_t)(CB_ROW * r16 + 48 * wave + 12 * g);
+    const uint32_t tabrow = (uint32_t)(4 * (16 * g + r16));  // (code << 8) | tabrow
+
     // x block of chunk c0 + c: piece p = tid + 256 u is batch row p / 64,
     // 16-byte chunk p % 64 (pieces past the batch repeat the last one: same
     // bytes to the same address).  Loaded one chunk ahead into registers.
@@ -167,103 +171,86 @@ __global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
         for (int u = 0; u < XPT; ++u) *(lds128*)(XS[buf] + xdst[u]) = xw[set][u];
     };
 
-    uint32_t mask = 0x7Eu;
+    uint32_t mask = 0x3F00u;
     asm volatile("" : "+v"(mask));  // in a VGPR: (code & mask) | row is one v_and_or_b32
-    // Gather the weights of the chunk whose codes sit in register slot
-    // cs % (PC + 1); they are written to LDS one chunk later.
-    uint32_t g[PPW][16];
-    auto gather = [&](int cs) {
+    // Gather the 16 weights of the chunk whose codes sit in code buffer buf;
+    // they feed the MFMAs one chunk later.
+    uint32_t gv[16];
+    auto gather = [&](int buf) {
+        const lds8* q = CB[buf] + cread;
+        const uint32_t d0 = *(const lds32*)q, d1 = *(const lds32*)(q + 4), d2 = *(const lds32*)(q + 8);
+        uint32_t a[16];
+        a[0] = (code_x256<0>(d0, d1, d2) & mask) | tabrow;
+        a[1] = (code_x256<1>(d0, d1, d2) & mask) | tabrow;
+        a[2] = (code_x256<2>(d0, d1, d2) & mask) | tabrow;
+        a[3] = (code_x256<3>(d0, d1, d2) & mask) | tabrow;
+        a[4] = (code_x256<4>(d0, d1, d2) & mask) | tabrow;
+        a[5] = (code_x256<5>(d0, d1, d2) & mask) | tabrow;
+        a[6] = (code_x256<6>(d0, d1, d2) & mask) | tabrow;
+        a[7] = (code_x256<7>(d0, d1, d2) & mask) | tabrow;
+        a[8] = (code_x256<8>(d0, d1, d2) & mask) | tabrow;
+        a[9] = (code_x256<9>(d0, d1, d2) & mask) | tabrow;
+        a[10] = (code_x256<10>(d0, d1, d2) & mask) | tabrow;
+        a[11] = (code_x256<11>(d0, d1, d2) & mask) | tabrow;
+        a[12] = (code_x256<12>(d0, d1, d2) & mask) | tabrow;
+        a[13] = (code_x256<13>(d0, d1, d2) & mask) | tabrow;
+        a[14] = (code_x256<14>(d0, d1, d2) & mask) | tabrow;
+        a[15] = (code_x256<15>(d0, d1, d2) & mask) | tabrow;
 #pragma unroll
-        for (int u = 0; u < PPW; ++u) {
-            const uint32_t d0 = cr[cs % (PC + 1)][u][0], d1 = cr[cs % (PC + 1)][u][1], d2 = cr[cs % (PC + 1)][u][2];
-            const uint32_t tb = tabrow[u];
-            uint32_t a[16];
-            a[0] = (code_x2<0>(d0, d1, d2) & mask) | tb;
-            a[1] = (code_x2<1>(d0, d1, d2) & mask) | tb;
-            a[2] = (code_x2<2>(d0, d1, d2) & mask) | tb;
-            a[3] = (code_x2<3>(d0, d1, d2) & mask) | tb;
-            a[4] = (code_x2<4>(d0, d1, d2) & mask) | tb;
-            a[5] = (code_x2<5>(d0, d1, d2) & mask) | tb;
-            a[6] = (code_x2<6>(d0, d1, d2) & mask) | tb;
-            a[7] = (code_x2<7>(d0, d1, d2) & mask) | tb;
-            a[8] = (code_x2<8>(d0, d1, d2) & mask) | tb;
-            a[9] = (code_x2<9>(d0, d1, d2) & mask) | tb;
-            a[10] = (code_x2<10>(d0, d1, d2) & mask) | tb;
-            a[11] = (code_x2<11>(d0, d1, d2) & mask) | tb;
-            a[12] = (code_x2<12>(d0, d1, d2) & mask) | tb;
-            a[13] = (code_x2<13>(d0, d1, d2) & mask) | tb;
-            a[14] = (code_x2<14>(d0, d1, d2) & mask) | tb;
-            a[15] = (code_x2<15>(d0, d1, d2) & mask) | tb;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) g[u][e] = *(lds16c*)(TAB + a[e]);
-        }
+        for (int e = 0; e < 16; ++e) gv[e] = *(lds16c*)(TAB + a[e]);
     };
-    // Write the gathered weights as bf16 pairs into W buffer buf.
-    auto write_w = [&](int buf) {
+    // x operand of slice s: batch row lane % 16, 16-byte chunk 8 wave + 2 g + s
+    uint32_t xopos[SLICES];
 #pragma unroll
-        for (int u = 0; u < PPW; ++u) {
-            uint32_t wv[8];
-#pragma unroll
-            for (int p = 0; p < 8; ++p) wv[p] = perm_lo16(g[u][2 * p + 1], g[u][2 * p]);
-            const uint32_t r = (uint32_t)(2 * (wave + NW * u) + h);
-            *(lds128*)(WS[buf] + wpos(r, 2u * j)) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-            *(lds128*)(WS[buf] + wpos(r, 2u * j + 1u)) = u32x4{wv[4], wv[5], wv[6], wv[7]};
-        }
-    };
-    // operand offsets: row (W) or batch row (x) lane % 16, slice NW s + wave, chunk 4 slice + lane / 16
-    uint32_t wopos[SLICES], xopos[SLICES];
-#pragma unroll
-    for (int s2 = 0; s2 < SLICES; ++s2) {
-        const uint32_t q = (uint32_t)(4 * (NW * s2 + wave) + (lane >> 4));
-        wopos[s2] = wpos((uint32_t)(lane & 15), q);
-        xopos[s2] = tpos((uint32_t)(lane & 15 & (XROWS - 1)), q);  // columns >= XROWS are never stored
-    }
+    for (int s2 = 0; s2 < SLICES; ++s2)
+        xopos[s2] = tpos((uint32_t)(r16 & (XROWS - 1)), (uint32_t)(8 * wave + 2 * g + s2));  // columns >= XROWS are never stored
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
-    // ---- prologue: W(0) and x(0) in LDS, W(1) gathered, x(1) loaded --------------
+    // ---- prologue: x(0) and the codes of chunks 0, 1 in LDS, W(0) gathered ------
 #pragma unroll
-    for (int c = 0; c < PC + 1; ++c) load_codes(c, c);
+    for (int c = 0; c < CSLOTS; ++c) load_codes(c, c);
     load_x(0, 0);
+    store_codes(0, 0);
+    store_codes(1, 1);
     store_x(0, 0);
     load_x(1, 1);
-    __syncthreads();  // tables, x block 0
+    __syncthreads();  // tables, x block 0, code buffers
     gather(0);
-    write_w(0);
-    gather(1);
-    load_codes(PC + 1, PC + 1);
-    __syncthreads();
+    __syncthreads();  // code buffer 0 is rewritten in chunk 0
 
-    // Chunk c: read its MFMA operands first; then write W(c+1) (gathered one
-    // chunk earlier), store x(c+1) (loaded one chunk earlier), gather W(c+2),
-    // request x(c+2) and the codes of c + PC + 2; then the MFMAs of c.  Past
-    // the end the chunk index is clamped; the extra work lands in buffers that
-    // are never read.  The loop is unrolled by 6 so that every register slot
-    // (codes: c % 3, x: c % 2) and buffer (c % 2) is a compile-time index.
+    // Chunk c: read its x operands and pack its weights (gathered one chunk
+    // earlier) into the row operands; then store x(c+1) (loaded one chunk
+    // earlier), gather W(c+1) (codes in the buffer since the previous chunk),
+    // store the codes of c+2 (loaded two chunks earlier), request x(c+2) and
+    // the codes of c+4; then the MFMAs of c.  Past the end the chunk index is
+    // clamped; the extra work lands in buffers that are never read.  The loop
+    // is unrolled by 4 so that every register slot (codes: c % 4, x: c % 2)
+    // and buffer (c % 2) is a compile-time index.
     auto step = [&](auto cm, int c) {
-        constexpr int C6 = decltype(cm)::value;
-        constexpr int B = C6 & 1;
+        constexpr int C4 = decltype(cm)::value;
+        constexpr int B = C4 & 1;
         bf16x8 af[SLICES], bf[SLICES];
 #pragma unroll
         for (int s2 = 0; s2 < SLICES; ++s2) {
-            af[s2] = __builtin_bit_cast(bf16x8, *(lds128c*)(WS[B] + wopos[s2]));
             bf[s2] = __builtin_bit_cast(bf16x8, *(lds128c*)(XS[B] + xopos[s2]));
+            af[s2] = __builtin_bit_cast(
+                bf16x8, u32x4{perm_lo16(gv[8 * s2 + 1], gv[8 * s2]), perm_lo16(gv[8 * s2 + 3], gv[8 * s2 + 2]),
+                              perm_lo16(gv[8 * s2 + 5], gv[8 * s2 + 4]), perm_lo16(gv[8 * s2 + 7], gv[8 * s2 + 6])});
         }
-        write_w(B ^ 1);
         store_x(B ^ 1, B ^ 1);
-        gather(C6 + 2);
+        gather(B ^ 1);
+        store_codes(C4 + 2, B);
         load_x(B, c + 2);
-        load_codes(C6 + 2 + PC, c + 2 + PC);
+        load_codes(C4 + CSLOTS, c + CSLOTS);
 #pragma unroll
         for (int s2 = 0; s2 < SLICES; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s2], bf[s2], acc, 0, 0, 0);
         __syncthreads();
     };
-    for (int c = 0; c < n; c += 6) {
+    for (int c = 0; c < n; c += 4) {
         step(std::integral_constant<int, 0>{}, c);
         if (c + 1 < n) step(std::integral_constant<int, 1>{}, c + 1);
         if (c + 2 < n) step(std::integral_constant<int, 2>{}, c + 2);
         if (c + 3 < n) step(std::integral_constant<int, 3>{}, c + 3);
-        if (c + 4 < n) step(std::integral_constant<int, 4>{}, c + 4);
-        if (c + 5 < n) step(std::integral_constant<int, 5>{}, c + 5);
     }
 
     // D layout of a 16x16 block: lane l, item i -> row 4 (l / 16) + i, column l % 16.
