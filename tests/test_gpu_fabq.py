@@ -47,7 +47,7 @@ def test_gemv_layer(bs, batch, out):
     assert_close(to_f64(y), oracle.fabq.gemv(p, x, 5120, 5120, bs, inp.n_hi), out, f"bs{bs} b{batch}")
 
 
-@pytest.mark.parametrize("batch", [1, 3, 16])
+@pytest.mark.parametrize("batch", [1, 3, 4, 16])
 def test_gemv_ragged_rows(batch):
     inp, p = case(101, 1536, 51, 256)
     x = synth.activations(batch, 1536, 51)
@@ -55,10 +55,13 @@ def test_gemv_ragged_rows(batch):
     assert_close(to_f64(y), oracle.fabq.gemv(p, x, 101, 1536, 256, inp.n_hi), "f32")
 
 
-def test_all_int4_and_all_binary_layers():
+@pytest.mark.parametrize("batch", [2, 5])
+def test_all_int4_and_all_binary_layers(batch):
+    """Batch 2 takes the VALU kernel, batch 5 the matrix-core one (row blocks
+    of one kind only)."""
     for frac in (1.0, 0.0):
         inp = synth.fabq_input(64, 1024, 52, blocksize=64, hi_frac=frac)
         p = oracle.fabq.pack(inp)
-        x = synth.activations(2, 1024, 52)
+        x = synth.activations(batch, 1024, 52)
         y = fqm.gemv(weights(inp), bf16_dev(x), out_dtype=torch.float32)
         assert_close(to_f64(y), oracle.fabq.gemv(p, x, 64, 1024, 64, inp.n_hi), "f32", f"hi={frac}")
