@@ -115,9 +115,9 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
 // sum: binary rows add s_b * (sum of +-x) over the wave's slices of the
 // block (linear, so the waves' parts add up to the block's); int4 rows add
 // the plain sum and take the row scale at the end.  The codebook term
-// c[idx_b] * (sum of x over the wave's slices of block b) comes from the x
-// operand the lane holds anyway (8 values per slice), added across the four
-// lanes that share a batch row.  The per-block scales and centroids of the 16 rows are staged in LDS
+// c[idx_b] * (sum of x over the wave's slices of block b) takes its sum of x
+// from a second MFMA per slice with an all-ones row operand (the matrix
+// cores are otherwise idle; no vector instructions per slice).  The per-block scales and centroids of the 16 rows are staged in LDS
 // first, so a flush reads LDS only.  The waves' results are added in
 // wave order.  A row block that is all binary (or all int4) decodes only its
 // own kind; a mixed one decodes both and selects per lane.
@@ -223,20 +223,18 @@ __global__ __launch_bounds__(64 * kMW) void fabq_gemv_mfma_kernel(fqm_fabq f, co
     __syncthreads();  // tables
 
     f32x4_t total = {0.f, 0.f, 0.f, 0.f}, acc = {0.f, 0.f, 0.f, 0.f};
-    float xs = 0.f;  // this lane's part of the block's sum of x
+    f32x4_t accx = {0.f, 0.f, 0.f, 0.f};  // every row: the sum of x over the block's slices so far
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
     auto flush = [&](int blk) {
-        // the wave's part of the block's sum of x for batch row lane % 16:
-        // add the four lanes g = 0..3
-        float xb = xs + __shfl_xor(xs, 16, 64);
-        xb += __shfl_xor(xb, 32, 64);
+        const float xb = accx[0];  // the wave's part of the block's sum of x, batch row lane % 16
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * g + i;
             const float cv = s_cb[s_ix[r * kMaxNB + blk]];
             total[i] = fmaf(s_sc[r * kMaxNB + blk], acc[i], fmaf(cv, xb, total[i]));
             acc[i] = 0.f;
+            accx[i] = 0.f;
         }
-        xs = 0.f;
     };
     // kind of the row block: 0 all binary, 1 all int4, 2 mixed (uniform)
     const int kind = r0 >= f.n_hi ? 0 : (min(r0 + 16, rows) <= f.n_hi ? 1 : 2);
@@ -264,10 +262,7 @@ __global__ __launch_bounds__(64 * kMW) void fabq_gemv_mfma_kernel(fqm_fabq f, co
                 av = __builtin_bit_cast(bf16x8_t, a_int4 ? ai : as);
             }
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, xv[q][u]), acc, 0, 0, 0);
-            float sx = 0.f;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) sx += bf16lo(xv[q][u][d]) + bf16hi(xv[q][u][d]);
-            xs += sx;
+            accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8_t, xv[q][u]), accx, 0, 0, 0);
         }
     };
     for (int base = t0; base < t1; base += 2 * kGS) {
