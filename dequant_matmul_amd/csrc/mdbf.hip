@@ -23,9 +23,9 @@
 // block, 256-wide K block and 16-wide k slice, the 64 lanes' 16-byte MFMA
 // operand pieces are contiguous, so every operand load is one coalesced 1 KB
 // wave read.
-// A workgroup owns 32 rows and a batch slice; its 8 waves split K and their
-// partial sums are added in a fixed order in LDS, so results do not depend
-// on timing.  Columns past the logical width hold zeros in D1/D2, so the sign
+// A workgroup owns 32 rows and a batch slice; its waves (16 in pass 1, 8 in
+// pass 2) split K and their partial sums are added in a fixed order in LDS,
+// so results do not depend on timing.  Columns past the logical width hold zeros in D1/D2, so the sign
 // bits read there (padding, or a clamped re-read) contribute nothing.
 #include <algorithm>
 
@@ -172,7 +172,7 @@ __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int
 }
 
 // Sum of the NW waves' partial blocks in a fixed tree order (waves w and
-// w + h for h = 4, 2, 1) into red[nb][row][col] (LDS).  D layout of a 32x32
+// w + h for h = NW / 2, ..., 2, 1) into red[nb][row][col] (LDS).  D layout of a 32x32
 // block: lane l, item q -> row (q % 4) + 8 (q / 4) + 4 (l / 32), column l % 32.
 template <int NB, int NW>
 __device__ __forceinline__ void reduce_waves(f32x16 (&acc)[NB], float* buf, float* red) {
