@@ -24,6 +24,20 @@ def test_gemm_ragged(M):
     assert_close(to_f64(Y), oracle.lut6.gemm(packed, inp.lut, X, cols), "bf16", f"M={M}")
 
 
+def test_gemm_prefill_shape_every_output():
+    """The prefill configuration (X 2048 x 5120, the up layer 17408 x 5120):
+    all 35.7 M outputs against the fp64 product (one BLAS matmul on the host)."""
+    rows, cols, seed, M = 17408, 5120, 2, 2048
+    inp, packed = lut6_case(rows, cols, seed)
+    w = lut6_weights(rows, cols, seed)
+    X = synth.activations(M, cols, 4)
+    Y = fqm.gemm(w, bf16_dev(X))
+    W = oracle.lut6.decode(inp.codes, inp.lut)
+    yo = oracle.numerics.bf16_to_f64(X) @ W.T
+    del W
+    assert_close(to_f64(Y), yo, "bf16", f"M={M}")
+
+
 @pytest.mark.parametrize("M", [2047, 2048])
 def test_gemm_prefill_shape_sampled(M):
     rows, cols, seed = 17408, 5120, 2
