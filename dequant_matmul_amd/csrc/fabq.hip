@@ -18,14 +18,69 @@ namespace {
 
 constexpr int kWaves = 4;
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Eight bf16 +-1.0 from one sign byte: bit e set -> +1.0, clear -> -1.0.
+__device__ __forceinline__ bf16x8_t signs_to_bf16(uint32_t byte) {
+    const uint32_t nb = ~byte;
+    u32x4_t v;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t t = (nb >> (2 * d)) & 3u;  // sign bits of elements 2d, 2d + 1
+        v[d] = 0x3F803F80u | (((t | (t << 15)) & 0x10001u) << 15);
+    }
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+
+// The 32 signs of one sign dword as 16 bf16 pairs of +-1.0 (element 2j in
+// the low half of pair j, 2j+1 in the high half; bit set -> +1.0): the two
+// 16-bit halves of a dword holding two copies of the relevant half of ~d are
+// shifted by different amounts at once, which puts the sign of element 2j at
+// bit 15 and that of 2j+1 at bit 31.
+__device__ __forceinline__ void signs32_to_bf16(uint32_t d, uint32_t ones, uint32_t (&v)[16]) {
+    const uint32_t nd = ~d;
+    const uint32_t lo = __builtin_amdgcn_perm(nd, nd, 0x01000100u);  // (nd[15:0], nd[15:0])
+    const uint32_t hi = __builtin_amdgcn_perm(nd, nd, 0x03020302u);  // (nd[31:16], nd[31:16])
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const u16x2_t sh = {(uint16_t)(15 - 2 * (j & 7)), (uint16_t)(14 - 2 * (j & 7))};
+        const u16x2_t t = __builtin_bit_cast(u16x2_t, j < 8 ? lo : hi) << sh;
+        v[j] = (__builtin_bit_cast(uint32_t, t) & 0x80008000u) | ones;  // ones = bf16 (1, 1) in a register
+    }
+}
+
+// a.lo * b.lo + a.hi * b.hi + c for bf16 pairs, fp32 accumulate
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                          false);
+}
+
+// Vector-ALU kernel (batch 1..3), one stored row per wave.  Every lane runs
+// the same number of steps (indices past the row are clamped and their
+// results dropped by a select), so each group of U steps issues all its loads
+// before the first use; the row's output slot, int4 scale and the codebook
+// (one centroid per lane, looked up across lanes) are requested up front.
 template <int B>
 __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16_t* __restrict__ x,
                                                         void* __restrict__ y, int y_f32,
                                                         int64_t rows, int64_t cols) {
+    constexpr int UI = B == 1 ? 5 : 1;  // int4 steps per group (64 dwords of 8 fields each)
+    constexpr int UB = B == 1 ? 3 : 1;  // binary steps per group (64 dwords of 32 signs each)
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int64_t i = (int64_t)blockIdx.x * kWaves + wave;  // stored row
-    if (i >= rows) return;
+    const int64_t i_u = (int64_t)blockIdx.x * kWaves + wave;  // stored row
+    if (i_u >= rows) return;
+    const int64_t i = i_u;
+    const bool has_bin = f.n_hi < rows;
+    // unconditional loads (x stands in for an array the matrix does not have)
+    const uint32_t cbits = *(reinterpret_cast<const uint32_t*>(has_bin ? f.codebook : x) + (lane & 7));
+    const int32_t out_row = f.row_of[i];
+    const uint16_t hbits = *(f.n_hi > 0 ? f.s_hi + min(i, (int64_t)f.n_hi - 1) : x);
 
     float acc[B];
 #pragma unroll
@@ -35,65 +90,100 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
         // int4 row: one dword = 8 nibbles = 8 columns per lane step.
         const uint32_t* q = reinterpret_cast<const uint32_t*>(f.q4 + i * f.ld_q4);
         const int64_t nw = cols / 8;
-        for (int64_t p = lane; p < nw; p += 64) {
-            const uint32_t d = q[p];
-            float wq[8];
+        for (int64_t p0 = 0; p0 < nw; p0 += 64 * UI) {
+            uint32_t d[UI];
+            uint4 xv[UI][B];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) wq[j] = (float)((int32_t)(d << (28 - 4 * j)) >> 28);
+            for (int u = 0; u < UI; ++u) {
+                const int64_t p = min(p0 + 64 * u + lane, nw - 1);
+                d[u] = q[p];
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const uint4 xv = *reinterpret_cast<const uint4*>(x + (int64_t)b * cols + 8 * p);
-                const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-                float a = acc[b];
+                for (int b = 0; b < B; ++b) xv[u][b] = *reinterpret_cast<const uint4*>(x + (int64_t)b * cols + 8 * p);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    a = fmaf(wq[2 * j], bf16lo(xs[j]), a);
-                    a = fmaf(wq[2 * j + 1], bf16hi(xs[j]), a);
+            for (int u = 0; u < UI; ++u) {
+                const bool ok = p0 + 64 * u + lane < nw;
+                float wq[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) wq[jj] = (float)((int32_t)(d[u] << (28 - 4 * jj)) >> 28);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const uint32_t xs[4] = {xv[u][b].x, xv[u][b].y, xv[u][b].z, xv[u][b].w};
+                    float a = acc[b];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        a = fmaf(wq[2 * jj], bf16lo(xs[jj]), a);
+                        a = fmaf(wq[2 * jj + 1], bf16hi(xs[jj]), a);
+                    }
+                    acc[b] = ok ? a : acc[b];
                 }
-                acc[b] = a;
             }
         }
-        const float s = fp16_to_f32(f.s_hi[i]);
+        const float s = fp16_to_f32(hbits);
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[b] *= s;
     } else {
         // binary row: one dword = 32 sign bits; a block (>= 64 columns) holds whole dwords.
+        // centroids 2 (lane % 8) and 2 (lane % 8) + 1 (fp16 pairs), read across lanes where used
+        uint32_t ones = 0x3F803F80u;  // bf16 (1, 1), held in a register
+        asm volatile("" : "+v"(ones));
         const int64_t j = i - f.n_hi;
         const uint32_t* sg = reinterpret_cast<const uint32_t*>(f.signs + j * f.ld_signs);
         const int64_t nb = cols / f.blocksize;
         const uint16_t* sb = f.s_blk + j * nb;
         const uint8_t* ib = f.idx + j * f.ld_idx;
-        const int words_per_block = f.blocksize / 32;
-        const int64_t nw = cols / 32;
-        for (int64_t p = lane; p < nw; p += 64) {
-            const uint32_t d = sg[p];
-            const int64_t blk = p / words_per_block;
-            const float s = fp16_to_f32(sb[blk]);
-            const uint32_t id = (ib[blk >> 1] >> ((blk & 1) * 4)) & 15u;
-            const float c = fp16_to_f32(f.codebook[id]);
+        const int wshift = __builtin_ctz((unsigned)f.blocksize) - 5;  // log2(sign dwords per block)
+        const int nw = (int)(cols / 32);
+        for (int p0 = 0; p0 < nw; p0 += 64 * UB) {
+            uint32_t d[UB];
+            uint16_t sbits[UB];
+            uint8_t ibits[UB];
+            int bodd[UB];
+            uint4 xv[UB][B][4];
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const uint4* xp = reinterpret_cast<const uint4*>(x + (int64_t)b * cols + 32 * p);
-                float ps = 0.f, xsum = 0.f;
+            for (int u = 0; u < UB; ++u) {
+                const int p = min(p0 + 64 * u + lane, nw - 1);
+                const int blk = p >> wshift;
+                d[u] = sg[p];
+                sbits[u] = sb[blk];
+                ibits[u] = ib[blk >> 1];
+                bodd[u] = blk & 1;
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const uint4 xv = xp[h];
-                    const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+                for (int b = 0; b < B; ++b)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int bit = 8 * h + 2 * t;
-                        const float x0 = bf16lo(xs[t]), x1 = bf16hi(xs[t]);
-                        // +-x by flipping the sign bit where the sign bit of W is 0
-                        ps += __uint_as_float(__float_as_uint(x0) ^ ((~d >> bit) & 1u) << 31);
-                        ps += __uint_as_float(__float_as_uint(x1) ^ ((~d >> (bit + 1)) & 1u) << 31);
-                        xsum += x0 + x1;
+                    for (int h = 0; h < 4; ++h)
+                        xv[u][b][h] = reinterpret_cast<const uint4*>(x + (int64_t)b * cols + 32 * p)[h];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const bool ok = p0 + 64 * u + lane < nw;
+                const float s = fp16_to_f32(sbits[u]);
+                const int id = (ibits[u] >> (4 * bodd[u])) & 15;
+                const uint32_t cpair = (uint32_t)__shfl((int)cbits, id >> 1);
+                const float c = fp16_to_f32((uint16_t)(cpair >> (16 * (id & 1))));
+                // the 32 signs as bf16 +-1.0 pairs: products with x are exact
+                uint32_t sv[16];
+                signs32_to_bf16(d[u], ones, sv);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    float ps = 0.f, xsum = 0.f;
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        const uint32_t xs[4] = {xv[u][b][h].x, xv[u][b][h].y, xv[u][b][h].z, xv[u][b][h].w};
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            ps = dot2_bf16(sv[4 * h + t], xs[t], ps);
+                            xsum = dot2_bf16(ones, xs[t], xsum);
+                        }
                     }
+                    const float a = fmaf(s, ps, fmaf(c, xsum, acc[b]));
+                    acc[b] = ok ? a : acc[b];
                 }
-                acc[b] = fmaf(s, ps, fmaf(c, xsum, acc[b]));
             }
         }
     }
-    const int64_t out_row = f.row_of[i];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const float v = wave_sum(acc[b]);
@@ -125,26 +215,10 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
 // are filled, and each group's loads go out before the previous group's
 // products; no global load depends on another.
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMW = 8;        // waves per workgroup
 constexpr int kGS = 8;        // slices whose loads a wave issues together
 constexpr int kMaxNB = 256;   // blocks per row the LDS tables hold (larger: VALU kernel)
-
-// Eight bf16 +-1.0 from one sign byte: bit e set -> +1.0, clear -> -1.0.
-__device__ __forceinline__ bf16x8_t signs_to_bf16(uint32_t byte) {
-    const uint32_t nb = ~byte;
-    u32x4_t v;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const uint32_t t = (nb >> (2 * d)) & 3u;  // sign bits of elements 2d, 2d + 1
-        v[d] = 0x3F803F80u | (((t | (t << 15)) & 0x10001u) << 15);
-    }
-    return __builtin_bit_cast(bf16x8_t, v);
-}
 
 // Eight bf16 from eight 4-bit two's complement fields (field e at bits 4e), exact.
 __device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t d) {
@@ -158,7 +232,7 @@ __device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t d) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-__global__ __launch_bounds__(64 * kMW) void fabq_gemv_mfma_kernel(fqm_fabq f, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(4))) void fabq_gemv_mfma_kernel(fqm_fabq f, const uint16_t* __restrict__ x,
                                                                   void* __restrict__ y, int y_f32, int rows,
                                                                   int cols, int batch) {
     __shared__ float s_sc[16 * kMaxNB];     // [row][blk]: s_b (binary) or 1 (int4)
@@ -188,25 +262,48 @@ __global__ __launch_bounds__(64 * kMW) void fabq_gemv_mfma_kernel(fqm_fabq f, co
     const int ns = cols / 32;
     const int t0 = (wave * ns) / kMW, t1 = ((wave + 1) * ns) / kMW;  // this wave's slices
     // loads of the group of slices starting at base into register set q
-    // (indices past the wave's last slice repeat it; never used)
+    // (indices past the wave's last slice repeat it, or slice 0 for a wave
+    // without slices; never used)
     uint32_t wq[2][kGS];
     u32x4_t xv[2][kGS];
     auto load_group = [&](int q, int base) {
 #pragma unroll
         for (int u = 0; u < kGS; ++u) {
-            const int t = min(base + u, t1 - 1);
+            const int t = max(min(base + u, t1 - 1), 0);
             wq[q][u] = *reinterpret_cast<const uint32_t*>(arow + astep * t);
             xv[q][u] = *reinterpret_cast<const u32x4_t*>(xrow + 32 * t);
         }
     };
-    if (t0 < t1) load_group(0, t0);
+    // Per-block scales and indices of the 16 rows (rows past the end repeat
+    // the last): table item e = tid + 64 kMW p goes to [row][blk].  The raw
+    // fields of the first pass are requested before the first group of
+    // weights and stored after it, so the two latencies overlap; their loads
+    // are unconditional (clamped index; x stands in for the binary-row arrays
+    // when there are no binary rows, and the values are then not used).
+    const int ne = 16 * nblk;
+    const bool has_bin = f.n_hi < rows;
+    const int e0 = min(tid, ne - 1);
+    const int er = e0 / nblk, eb = e0 - er * nblk;
+    const int esr = min(r0 + er, rows - 1);
+    const int64_t ejb = max(esr - f.n_hi, 0);
+    const uint16_t* ps = has_bin ? f.s_blk + ejb * nblk + eb : x;
+    const uint8_t* pi = has_bin ? f.idx + ejb * f.ld_idx + (eb >> 1) : reinterpret_cast<const uint8_t*>(x);
+    const uint16_t* pcb = has_bin ? f.codebook + (tid & 15) : x;
+    const uint16_t sraw = *ps, craw = *pcb;
+    const uint8_t iraw = *pi;
+    __builtin_amdgcn_sched_barrier(0);
+    load_group(0, t0);  // unconditional, so the waits below count exactly
     // the output row and int4 row scale this thread stores at the end
     const int srow = min(r0 + ((tid >> 4) & 15), rows - 1);
     const int32_t out_row = f.row_of[srow];
-    const float hi_scale = srow < f.n_hi ? fp16_to_f32(f.s_hi[srow]) : 1.f;
+    const uint16_t hraw = *(f.n_hi > 0 ? f.s_hi + min(srow, f.n_hi - 1) : x);  // used for int4 rows only
 
-    // per-block scales and indices of the 16 rows (rows past the end repeat the last)
-    for (int e = tid; e < 16 * nblk; e += 64 * kMW) {
+    if (tid < ne) {
+        const bool bin = esr >= f.n_hi;
+        s_sc[er * kMaxNB + eb] = bin ? fp16_to_f32(sraw) : 1.f;
+        s_ix[er * kMaxNB + eb] = bin ? (uint8_t)((iraw >> ((eb & 1) * 4)) & 15u) : (uint8_t)16;
+    }
+    for (int e = tid + 64 * kMW; e < ne; e += 64 * kMW) {  // blocks shorter than 5120 / 32 columns
         const int r = e / nblk, blk = e - r * nblk;
         const int sr = min(r0 + r, rows - 1);
         float sc = 1.f;
@@ -219,7 +316,7 @@ __global__ __launch_bounds__(64 * kMW) void fabq_gemv_mfma_kernel(fqm_fabq f, co
         s_sc[r * kMaxNB + blk] = sc;
         s_ix[r * kMaxNB + blk] = (uint8_t)ix;
     }
-    if (tid < 17) s_cb[tid] = (tid < 16 && f.n_hi < rows) ? fp16_to_f32(f.codebook[tid]) : 0.f;
+    if (tid < 17) s_cb[tid] = (tid < 16 && has_bin) ? fp16_to_f32(craw) : 0.f;
     __syncthreads();  // tables
 
     f32x4_t total = {0.f, 0.f, 0.f, 0.f}, acc = {0.f, 0.f, 0.f, 0.f};
@@ -282,7 +379,7 @@ __global__ __launch_bounds__(64 * kMW) void fabq_gemv_mfma_kernel(fqm_fabq f, co
         for (int w = 0; w < kMW; ++w) v += s_red[w * 64 + l][i];
         const int sr = r0 + row;
         if (sr < rows && col < batch) {
-            v *= hi_scale;
+            v *= srow < f.n_hi ? fp16_to_f32(hraw) : 1.f;
             const int64_t o = (int64_t)col * rows + out_row;
             if (y_f32)
                 reinterpret_cast<float*>(y)[o] = v;

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64 * WPG) void lut6_gemv_rows(const uint8_t* __rest
         const int k = min(tid + u * 64 * WPG, NX - 1);
         s_x[((k >> 7) << 7) | ((k & 1) << 6) | ((k >> 1) & 63)] = xs[u];  // clamped duplicates store equal values
     }
-    if (lane < 32) s_tab[wv][lane] = tv;
+    s_tab[wv][lane & 31] = tv;  // unconditional (lanes 32-63 repeat 0-31), so the load stays ahead of the codes
     __syncthreads();
 
     const uint32_t base = (uint32_t)(uintptr_t)(lds_u8*)s_tab + 128u * wv;  // multiple of 128

@@ -116,14 +116,10 @@ __global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
     const int n = c1 - c0;
 
     // row tables, four copies: thread t writes copy t / 128 of entries
-    // 8 (t % 8) .. + 7 of row (t / 8) % 16
-    {
-        const int r = (tid >> 3) & 15, part8 = tid & 7, cp = tid >> 7;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(lut + (int64_t)min(n0 + r, rows - 1) * 64 + part8 * 8);
-        lds8* dst = TAB + 256 * 8 * part8 + 4 * (16 * cp + r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *(lds16*)(dst + 256 * e) = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-    }
+    // 8 (t % 8) .. + 7 of row (t / 8) % 16 (loaded here, stored to LDS once
+    // the first code and x loads are out, so that their latencies overlap)
+    const int tr = (tid >> 3) & 15, tpart = tid & 7, tcp = tid >> 7;
+    const u32x4 tv = *reinterpret_cast<const u32x4*>(lut + (int64_t)min(n0 + tr, rows - 1) * 64 + tpart * 8);
     static_assert(64 * NW == RB * 8 * 4, "one table item per thread");
 
     // Global code loads: wave w, lane half h, lane j = lane % 32 loads the
@@ -210,6 +206,11 @@ __global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < CSLOTS; ++c) load_codes(c, c);
     load_x(0, 0);
+    {
+        lds8* dst = TAB + 256 * 8 * tpart + 4 * (16 * tcp + tr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *(lds16*)(dst + 256 * e) = (uint16_t)(tv[e >> 1] >> (16 * (e & 1)));
+    }
     store_codes(0, 0);
     store_codes(1, 1);
     store_x(0, 0);

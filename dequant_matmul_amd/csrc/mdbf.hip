@@ -114,9 +114,10 @@ __global__ __launch_bounds__(256) void mdbf_prep(fqm_mdbf md, const uint16_t* __
     rem -= (int64_t)b * l * m_pad;
     const int k = (int)(rem / m_pad);
     const int64_t i = rem - (int64_t)k * m_pad;
-    const fqm_mdbf_path path = p == 0 ? md.path[0] : md.path[1];
+    // the two paths' pointers are selected as values (p varies per thread)
+    const uint16_t* bamp = p == 0 ? md.path[0].B_amp : md.path[1].B_amp;
     uint16_t h[3] = {0, 0, 0};
-    if (i < m) split3_bf16(fp16_to_f32(path.B_amp[i * l + k]) * bf16_to_f32(x[(int64_t)b * m + i]), h);
+    if (i < m) split3_bf16(fp16_to_f32(bamp[i * l + k]) * bf16_to_f32(x[(int64_t)b * m + i]), h);
     const int bs = batch_slice(l);
     const int sg = b / bs, bl = b - sg * bs;
     uint16_t* dp = D1 + (int64_t)p * d1_path;
@@ -226,9 +227,12 @@ __global__ __launch_bounds__(64 * NW1) void mdbf_pass1(fqm_mdbf md, const uint16
     const int64_t j0 = (int64_t)blockIdx.x * 32;
     // the epilogue's envelope values, fetched before the long sign products
     // (rows j0 .. j0 + 31 of the [r][l] arrays are one contiguous run)
+    // (unconditional loads at a clamped index, so that no wait lands here)
     const int64_t qo = j0 * l + threadIdx.x;
     const bool qin = threadIdx.x < 32 * l && qo < r * l;
-    const uint16_t qv_h = qin ? path.Q_V[qo] : 0, qu_h = qin ? path.Q_U[qo] : 0;
+    const int64_t qoc = min(qo, r * l - 1);
+    const uint16_t qv_l = path.Q_V[qoc], qu_l = path.Q_U[qoc];
+    const uint16_t qv_h = qin ? qv_l : 0, qu_h = qin ? qu_l : 0;
     const uint16_t* Dp = D1 + (int64_t)p * d1_path;
     const int wave = threadIdx.x >> 6;
     const int nblk = (int)(m_pad / KB);
@@ -286,12 +290,16 @@ __global__ __launch_bounds__(64 * NW2) void mdbf_pass2(fqm_mdbf md, const uint16
     const int b0 = blockIdx.y * bs, nb_rows = min(bs, batch - b0);
     const int64_t i0 = (int64_t)blockIdx.x * 32;
     // the epilogue's envelope values, fetched before the long sign products
+    // (unconditional loads at a clamped index, path 0 standing in for a
+    // missing path 1, so that no wait lands here)
     uint16_t amp_h[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int64_t ao = i0 * l + threadIdx.x;
         const bool ain = p < md.P && threadIdx.x < 32 * l && ao < n * l;
-        amp_h[p] = ain ? md.path[p].A_amp[ao] : 0;
+        const uint16_t* ap = p < md.P ? md.path[p].A_amp : md.path[0].A_amp;
+        const uint16_t a_l = ap[min(ao, n * l - 1)];
+        amp_h[p] = ain ? a_l : 0;
     }
     const int wave = threadIdx.x >> 6;
     const int nblk = (int)(r_pad / KB);
