@@ -55,10 +55,11 @@ def test_gemv_ragged_rows(batch):
     assert_close(to_f64(y), oracle.fabq.gemv(p, x, 101, 1536, 256, inp.n_hi), "f32")
 
 
-@pytest.mark.parametrize("batch", [2, 5])
+@pytest.mark.parametrize("batch", [1, 2, 5])
 def test_all_int4_and_all_binary_layers(batch):
-    """Batch 2 takes the VALU kernel, batch 5 the matrix-core one (row blocks
-    of one kind only)."""
+    """Batches 1 and 2 take the VALU kernel (batch 1 with its grouped loads),
+    batch 5 the matrix-core one (row blocks of one kind only; a layer without
+    binary rows has no block scales, indices or codebook to read)."""
     for frac in (1.0, 0.0):
         inp = synth.fabq_input(64, 1024, 52, blocksize=64, hi_frac=frac)
         p = oracle.fabq.pack(inp)
