@@ -17,6 +17,10 @@ row's K calls are captured into a HIP graph that is replayed between two HIP
 events recorded on the launch stream; a row's time is the average call
 duration in that stream (no per-call Python overhead between kernels).
 
+``dense_reference`` (context, not a row of the path) times the same products
+on dense bf16 weights of the same shapes through torch (the vendor BLAS), with
+the weights rotated the same way; ``--no-dense`` skips it.
+
 ``--profile ROW`` runs only ROW (for rocprofv3); ``--copy-calib MB`` runs a
 plain device copy of that size (the reference point for the HBM counters).
 """
@@ -51,6 +55,8 @@ def parse():
     ap.add_argument("--profile", default=None, help="run only this row (for rocprofv3)")
     ap.add_argument("--copy-calib", type=float, default=0.0, help="MB of a plain device copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense bf16 torch reference (context, not a row of the path)")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed calls one by one instead of replaying a HIP graph")
     return ap.parse_args()
@@ -253,6 +259,9 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(lut6_inputs, rows, res, fqm, bf16, dev)
+    dense = None
+    if not args.no_dense:
+        dense = dense_reference(res, args.rotate_gb, dev)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -270,6 +279,7 @@ def main():
         "prefill_frac_of_bf16_peak": round(res["prefill"]["frac_mfma"], 4) if "prefill" in res else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "dense_reference": dense,
         "rows": {k: {kk: (round(v, 3) if isinstance(v, float) else v) for kk, v in d.items()}
                  for k, d in res.items()},
         "setup_s": round(t_gen, 1), "timed_wall_s": round(wall, 3),
@@ -295,6 +305,53 @@ def kernel_source_sha():
     for f in ("lut6_gemv.hip", "fqm_internal.h"):
         h.update(open(os.path.join(ROOT, "dequant_matmul_amd", "csrc", f), "rb").read())
     return h.hexdigest()
+
+
+def dense_reference(res, rotate_gb, dev):
+    """Context, not a row of the path: the same products on dense bf16 weights
+    through torch (hipBLASLt / rocBLAS), weights rotating over device copies
+    like the rows, timed with HIP events around eager calls."""
+    import torch
+    import synth
+    C = synth.CONFIGS
+    out = {"kind": "torch bf16 matmul / linear on dense bf16 weights of the same shapes "
+                   "(vendor BLAS), weights rotated over device copies; context only"}
+    gen = torch.Generator(device=dev).manual_seed(0)
+
+    def timed(fn, n):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    for name in ("up", "down"):
+        N, K = C[f"lut6_{name}"]["rows"], C[f"lut6_{name}"]["cols"]
+        copies = max(2, int(np.ceil(rotate_gb * 1e9 / (N * K * 2))))
+        ws = [torch.randn(N, K, device=dev, dtype=torch.bfloat16, generator=gen) for _ in range(copies)]
+        x1 = torch.randn(1, K, device=dev, dtype=torch.bfloat16, generator=gen)
+        us = timed(lambda i: torch.nn.functional.linear(x1, ws[i % copies]), 100)
+        out[f"{name}_b1_us"] = round(us, 2)
+        out[f"{name}_b1_gbs"] = round(N * K * 2 / us * 1e-3, 1)
+        if name == "up" and "prefill" in res:
+            M = C["prefill"]["M"]
+            X = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=gen)
+            us = timed(lambda i: torch.matmul(X, ws[i % copies].t()), 20)
+            out["prefill_us"] = round(us, 1)
+            out["prefill_tflops"] = round(2 * M * N * K / us * 1e-6, 1)
+            del X
+        del ws
+        torch.cuda.empty_cache()
+    if "lut6_up_b1" in res and "lut6_down_b1" in res:
+        pair = res["lut6_up_b1"]["us_per_call"] + res["lut6_down_b1"]["us_per_call"]
+        out["b1_pair_speedup_of_lut6"] = round((out["up_b1_us"] + out["down_b1_us"]) / pair, 2)
+    if "prefill" in res and "prefill_us" in out:
+        out["prefill_speedup_of_lut6"] = round(out["prefill_us"] / res["prefill"]["us_per_call"], 3)
+    return out
 
 
 def cpu_baseline(lut6_inputs, rows, res, fqm, bf16, dev):

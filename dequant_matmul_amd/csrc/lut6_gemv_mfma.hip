@@ -61,6 +61,15 @@ constexpr int TAB_BYTES = 64 * 256;            // 16 rows x 4 copies x 64 entrie
 constexpr int SPLIT_TARGET = 1024;             // aim for at least this many workgroups
 static_assert(SLICES == 2 && CH == 64 * NW, "a wave takes 64 k of a chunk: 16 codes per lane");
 
+// Workgroup barrier that waits for nothing: the caller has made its LDS
+// stores complete already (the LDS reads still in flight are gathers from
+// the tables, which no wave rewrites inside the loop).
+__device__ __forceinline__ void barrier_no_wait() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint32_t perm_lo16(uint32_t hi, uint32_t lo) {
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
@@ -216,36 +225,41 @@ __global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
     store_x(0, 0);
     load_x(1, 1);
     __syncthreads();  // tables, x block 0, code buffers
-    gather(0);
-    __syncthreads();  // code buffer 0 is rewritten in chunk 0
+    gather(0);        // its code reads finish before the gathers go out
+    barrier_no_wait();  // code buffer 0 is rewritten in chunk 0
 
-    // Chunk c: read its x operands and pack its weights (gathered one chunk
-    // earlier) into the row operands; then store x(c+1) (loaded one chunk
-    // earlier), gather W(c+1) (codes in the buffer since the previous chunk),
-    // store the codes of c+2 (loaded two chunks earlier), request x(c+2) and
-    // the codes of c+4; then the MFMAs of c.  Past the end the chunk index is
-    // clamped; the extra work lands in buffers that are never read.  The loop
-    // is unrolled by 4 so that every register slot (codes: c % 4, x: c % 2)
-    // and buffer (c % 2) is a compile-time index.
+    // Chunk c: read its x operands, store x(c+1) (loaded one chunk earlier)
+    // and the codes of c+2 (loaded two chunks earlier), pack the weights
+    // gathered one chunk earlier into the row operands, request x(c+2) and
+    // the codes of c+4; wait for this chunk's LDS reads and stores; gather
+    // W(c+1) (codes in the buffer since the previous chunk); then the MFMAs
+    // of c and a barrier that does not wait for the gathers (their results
+    // are used one chunk later).  Past the end the chunk index is clamped;
+    // the extra work lands in buffers that are never read.  The loop is
+    // unrolled by 4 so that every register slot (codes: c % 4, x: c % 2) and
+    // buffer (c % 2) is a compile-time index.
     auto step = [&](auto cm, int c) {
         constexpr int C4 = decltype(cm)::value;
         constexpr int B = C4 & 1;
         bf16x8 af[SLICES], bf[SLICES];
 #pragma unroll
-        for (int s2 = 0; s2 < SLICES; ++s2) {
-            bf[s2] = __builtin_bit_cast(bf16x8, *(lds128c*)(XS[B] + xopos[s2]));
+        for (int s2 = 0; s2 < SLICES; ++s2) bf[s2] = __builtin_bit_cast(bf16x8, *(lds128c*)(XS[B] + xopos[s2]));
+        store_x(B ^ 1, B ^ 1);
+        store_codes(C4 + 2, B);
+#pragma unroll
+        for (int s2 = 0; s2 < SLICES; ++s2)
             af[s2] = __builtin_bit_cast(
                 bf16x8, u32x4{perm_lo16(gv[8 * s2 + 1], gv[8 * s2]), perm_lo16(gv[8 * s2 + 3], gv[8 * s2 + 2]),
                               perm_lo16(gv[8 * s2 + 5], gv[8 * s2 + 4]), perm_lo16(gv[8 * s2 + 7], gv[8 * s2 + 6])});
-        }
-        store_x(B ^ 1, B ^ 1);
-        gather(B ^ 1);
-        store_codes(C4 + 2, B);
         load_x(B, c + 2);
         load_codes(C4 + CSLOTS, c + CSLOTS);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only: this chunk's LDS reads and stores are done
+        asm volatile("" ::: "memory");
+        gather(B ^ 1);
 #pragma unroll
         for (int s2 = 0; s2 < SLICES; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s2], bf[s2], acc, 0, 0, 0);
-        __syncthreads();
+        barrier_no_wait();
     };
     for (int c = 0; c < n; c += 4) {
         step(std::integral_constant<int, 0>{}, c);
@@ -254,6 +268,7 @@ __global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
         if (c + 3 < n) step(std::integral_constant<int, 3>{}, c + 3);
     }
 
+    __syncthreads();  // every wave's last gathers have read the tables, which RED overwrites
     // D layout of a 16x16 block: lane l, item i -> row 4 (l / 16) + i, column l % 16.
     *(ldsf4*)(RED + 16 * (64 * wave + lane)) = acc;
     __syncthreads();
