@@ -260,35 +260,30 @@ hipError_t launch_b(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
     return hipGetLastError();
 }
 
-// Batch-1 variants by cells per row (cols / 1024): rows of at most eight
-// chunks use 4-wave workgroups, longer rows 10-wave workgroups (x for a
-// 17408-column row is 34 KB of LDS, so a CU holds four such groups); codes
-// are requested four chunks ahead.  Other widths take the generic kernel.
+// Batch-1 variants by cells per row (cols / 1024), 1 to kMaxCells: rows of at
+// most 8 cells use 4-wave workgroups, longer rows 10-wave workgroups (x for a
+// 17408-column row is 34 KB of LDS, so a CU holds four such groups); codes are
+// requested four cells ahead.  Other widths take the generic kernel.
+constexpr int kMaxCells = 31;  // x (2 KB per cell) and the tables stay under 64 KB of LDS
+
 bool rows_supported(const fqm_weights& w) {
-    if (w.cols <= 0 || (w.cols & 1023) || w.rows <= 0 || w.rows > 0x7fffffff) return false;
-    switch (w.cols >> 10) {
-        case 1: case 2: case 3: case 4: case 5: case 6: case 8: case 12: case 16: case 17: case 20:
-            return true;
-        default:
-            return false;
+    return w.cols > 0 && (w.cols & 1023) == 0 && (w.cols >> 10) <= kMaxCells && w.rows > 0 &&
+           w.rows <= 0x7fffffff;
+}
+
+template <int CPR>
+hipError_t launch_cells(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
+    if constexpr (CPR > kMaxCells) {
+        return hipErrorInvalidValue;
+    } else {
+        if ((w.cols >> 10) != CPR) return launch_cells<CPR + 1>(w, x, y, y_f32, s);
+        if constexpr (CPR <= 8) return launch_rows<CPR, 1, 4, 4>(w, x, y, y_f32, s);
+        else return launch_rows<CPR, 1, 10, 4>(w, x, y, y_f32, s);
     }
 }
 
 hipError_t launch_b1(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
-    switch (w.cols >> 10) {
-        case 1: return launch_rows<1, 1, 4, 4>(w, x, y, y_f32, s);
-        case 2: return launch_rows<2, 1, 4, 4>(w, x, y, y_f32, s);
-        case 3: return launch_rows<3, 1, 4, 4>(w, x, y, y_f32, s);
-        case 4: return launch_rows<4, 1, 4, 4>(w, x, y, y_f32, s);
-        case 5: return launch_rows<5, 1, 4, 4>(w, x, y, y_f32, s);
-        case 6: return launch_rows<6, 1, 4, 4>(w, x, y, y_f32, s);
-        case 8: return launch_rows<8, 1, 4, 4>(w, x, y, y_f32, s);
-        case 12: return launch_rows<12, 1, 10, 4>(w, x, y, y_f32, s);
-        case 16: return launch_rows<16, 1, 10, 4>(w, x, y, y_f32, s);
-        case 17: return launch_rows<17, 1, 10, 4>(w, x, y, y_f32, s);
-        case 20: return launch_rows<20, 1, 10, 4>(w, x, y, y_f32, s);
-        default: return hipErrorInvalidValue;
-    }
+    return launch_cells<1>(w, x, y, y_f32, s);
 }
 
 }  // namespace

@@ -134,7 +134,19 @@ def test_gemv_zero_cols_and_padded_rows():
 # one 1024-weight chunk per row, rows not a multiple of the workgroup size,
 # 16 and 17 chunks per row (the 10-wave workgroup variants), and a row count
 # that leaves a partial last workgroup.
-B1_SHAPES = [(77, 1024, 9), (1000, 3072, 8), (513, 2048, 12), (600, 16384, 10), (5200, 17408, 13)]
+B1_SHAPES = [(77, 1024, 9), (1000, 3072, 8), (513, 2048, 12), (600, 16384, 10), (5200, 17408, 13),
+             (130, 7168, 14), (301, 11264, 15), (97, 31744, 16)]  # 7, 11 and 31 cells: the widest
+
+
+def test_gemv_b1_past_the_widest_cells():
+    """32 cells (32768 columns) and a width that is not a whole number of
+    cells take the generic batch-1 kernel."""
+    for rows, cols, seed in ((65, 32768, 17), (70, 3136, 18)):
+        inp, packed = lut6_case(rows, cols, seed)
+        w = lut6_weights(rows, cols, seed)
+        x = synth.activations(1, cols, seed)
+        y = fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32)
+        assert_close(to_f64(y), oracle.lut6.gemv(packed, inp.lut, x, cols), "f32", f"{rows}x{cols}")
 
 
 @pytest.mark.parametrize("rows,cols,seed", B1_SHAPES)
