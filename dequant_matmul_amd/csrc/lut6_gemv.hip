@@ -104,18 +104,19 @@ __device__ __forceinline__ uint32_t code_x2(uint32_t d0, uint32_t d1, uint32_t d
 // Batch 1, cols a multiple of 1024.  A row is CPR chunks of 1024 weights; in
 // chunk c lane i owns the 12-byte piece i (16 codes, bytes [768c + 12i, +12)
 // of the row: one fully coalesced 768-byte load per chunk) and the matching
-// 16 x values (32 bytes, read from L2).  Each row is split over S waves
-// (wave s takes chunks [s*CPR/S, (s+1)*CPR/S)); a workgroup holds WPG waves,
-// i.e. WPG/S rows.  Codes are requested PC chunks ahead and x PX chunks
-// ahead, every load unconditional within the unrolled chunk loop, so the
-// compiler's waits are exact.  A wave's row table sits in its own LDS slot
-// at a compile-time offset, so a code becomes a gather address in two VALU
-// ops (shift, mask) and all 64 lanes of a gather read one 128-byte table
-// (distinct banks or a shared dword).  Two gathered bf16 are paired
-// (v_perm_b32) and meet the x pair in v_dot2_f32_bf16 (fp32 accumulate).
-// Each wave reduces its partial row sum once with DPP; with S > 1 the S
-// partials are added in wave order through LDS, so the result does not
-// depend on timing.
+// 16 x values (32 bytes), read from the x block the workgroup stages in LDS
+// once.  Each row is split over S waves (wave s takes chunks
+// [s*CPR/S, (s+1)*CPR/S)); a workgroup holds WPG waves, i.e. WPG/S rows.
+// Codes are requested PC chunks ahead, every load unconditional within the
+// unrolled chunk loop, so the compiler's waits are exact.  A wave's row table
+// sits in its own 128-byte LDS slot (a multiple of 128, held in a scalar
+// register), so a code becomes a gather address in two VALU ops (shift, then
+// mask and OR of the slot in one v_and_or_b32) and all 64 lanes of a gather
+// read one 128-byte table (distinct banks or a shared dword).  Two gathered
+// bf16 are paired (v_perm_b32) and meet the x pair in v_dot2_f32_bf16 (fp32
+// accumulate).  Each wave reduces its partial row sum once with DPP; with
+// S > 1 the S partials are added in wave order through LDS, so the result
+// does not depend on timing.
 // ---------------------------------------------------------------------------
 template <int CPR, int S, int WPG, int PC>
 __global__ __launch_bounds__(64 * WPG) void lut6_gemv_rows(const uint8_t* __restrict__ packed,
