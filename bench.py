@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--profile", default=None, help="run only this row (for rocprofv3)")
     ap.add_argument("--copy-calib", type=float, default=0.0, help="MB of a plain device copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--msweep", action="store_true",
+                    help="time the LUT6 GEMM (and the GEMV, M <= 16) on the up layer for M = 1 .. 2048 "
+                         "and print one JSON line (the GEMV/GEMM crossover), instead of the bench line")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense bf16 torch reference (context, not a row of the path)")
     ap.add_argument("--no-graph", action="store_true",
@@ -89,6 +92,10 @@ def main():
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if args.msweep:
+        print(json.dumps(msweep(fqm, synth, bf16, dev, args.rotate_gb)))
+        return
 
     def n_copies(w):
         return max(2, int(np.ceil(args.rotate_gb * 1e9 / w.nbytes())))
@@ -305,6 +312,52 @@ def kernel_source_sha():
     for f in ("lut6_gemv.hip", "fqm_internal.h"):
         h.update(open(os.path.join(ROOT, "dequant_matmul_amd", "csrc", f), "rb").read())
     return h.hexdigest()
+
+
+def msweep(fqm, synth, bf16, dev, rotate_gb, K_CALLS=20):
+    """Per-call time of the LUT6 GEMM for M = 1 .. 2048 on the up layer
+    (17408 x 5120), and of the GEMV for M <= 16, each as a graph of K_CALLS
+    calls with the weights rotating over device copies."""
+    import torch
+    cfg = synth.CONFIGS["lut6_up"]
+    inp = synth.lut6_input(cfg["rows"], cfg["cols"], cfg["seed"])
+    w0 = fqm.Lut6Weights.from_codes(inp.codes, inp.lut, device=dev)
+    ws = [w0] + [w0.clone() for _ in range(max(2, int(np.ceil(rotate_gb * 1e9 / w0.nbytes()))) - 1)]
+    N, K = cfg["rows"], cfg["cols"]
+
+    def timed(fn):
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K_CALLS):
+                fn(i + 1)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K_CALLS
+
+    out = []
+    for M in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048):
+        X = bf16(synth.activations(M, K, 7))
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        gws = fqm.gemm_workspace_size(w0, M)
+        gwt = torch.empty(gws, dtype=torch.uint8, device=dev) if gws else None
+        row = dict(M=M, gemm_us=round(timed(lambda i: fqm.gemm(ws[i % len(ws)], X, Y=Y, workspace=gwt)), 2))
+        if M <= 16:
+            vws = fqm.workspace_size(w0, M)
+            vwt = torch.empty(vws, dtype=torch.uint8, device=dev) if vws else None
+            row["gemv_us"] = round(timed(lambda i: fqm.gemv(ws[i % len(ws)], X, y=Y, workspace=vwt)), 2)
+        best = min(v for k, v in row.items() if k.endswith("_us"))
+        row["tflops_best"] = round(2 * M * N * K / best * 1e-6, 1)
+        row["weight_gbs_best"] = round(w0.nbytes() / best * 1e-3, 1)
+        out.append(row)
+    return {"msweep": out, "layer": f"LUT6 up {N}x{K}", "calls_per_graph": K_CALLS,
+            "weight_rotation_gb": rotate_gb}
 
 
 def dense_reference(res, rotate_gb, dev):

@@ -176,9 +176,18 @@ fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_
     return FQM_E_FORMAT;
 }
 
+// Up to 16 rows of X go to the GEMV kernels when they have a tuned kernel
+// for the shape: the prefill tiles are 256 rows tall, so below that the
+// matrix cores would mostly multiply padding (measured on the 17408 x 5120
+// layer: 14-31 us through the GEMV path against 68-71 us as a GEMM).
+static bool gemm_as_gemv(const fqm_weights& w, int64_t M) {
+    return M >= 1 && M <= 16 && fqm::lut6_gemv_fast_path(w, (int)M);
+}
+
 size_t fqm_gemm_workspace_size(const fqm_weights* w, int64_t M) {
     if (check_weights(w) != FQM_OK || w->format != FQM_LUT6 || M <= 0 || w->rows == 0) return 0;
     if (w->cols % 64 || M * w->cols * 2 > INT32_MAX) return 0;
+    if (gemm_as_gemv(*w, M)) return fqm::lut6_gemv_mfma_workspace(*w, (int)M);
     return fqm::lut6_gemm_workspace(*w, M);
 }
 
@@ -196,6 +205,8 @@ fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_
     const size_t need = fqm_gemm_workspace_size(w, M);
     if (need && (!workspace || ws_bytes < need)) return FQM_E_WORKSPACE;
     if (need && !aligned16(workspace)) return FQM_E_ALIGN;
+    if (gemm_as_gemv(*w, M))  // Y[M][rows] bf16 is the GEMV's y[batch][rows]
+        return hip_status(launch_lut6_gemv(*w, X, Y, 0, (int)M, static_cast<float*>(workspace), as_stream(stream)));
     return hip_status(launch_lut6_gemm(*w, X, Y, M, workspace, ws_bytes, as_stream(stream)));
 }
 

@@ -83,6 +83,9 @@ hipError_t launch_lut6_gemv(const fqm_weights& w, const uint16_t* x, void* y, in
 // Batch 2..16 on the matrix cores (cols a multiple of 1024); K may be split
 // over workgroups, with fp32 partial sums in the caller's workspace.
 bool lut6_gemv_mfma_supported(const fqm_weights& w, int batch);
+// true when launch_lut6_gemv takes a tuned kernel for this shape and batch
+// (the cell kernel at batch 1, the matrix-core kernel at 2..16)
+bool lut6_gemv_fast_path(const fqm_weights& w, int batch);
 size_t lut6_gemv_mfma_workspace(const fqm_weights& w, int batch);
 hipError_t launch_lut6_gemv_mfma(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
                                  float* ws, hipStream_t s);

@@ -78,6 +78,35 @@ def _plan_ws(rows, cols, M):
     return tail * ks * 256 * 256 * 4 if ks >= 2 else 0
 
 
+@pytest.mark.parametrize("M", [1, 2, 8, 16])
+@pytest.mark.parametrize("rows,cols", [(520, 2048), (300, 17408)])
+def test_gemm_small_m_runs_the_gemv_kernels(rows, cols, M):
+    """Up to 16 rows on a shape the GEMV kernels cover: the same workspace and
+    the same bits as fqm_gemv, and the oracle's product."""
+    inp, packed = lut6_case(rows, cols, 21)
+    w = lut6_weights(rows, cols, 21)
+    assert fqm.gemm_workspace_size(w, M) == fqm.workspace_size(w, M)
+    X = synth.activations(M, cols, 22)
+    buf, Y = guarded((M, rows), torch.bfloat16)
+    fqm.gemm(w, bf16_dev(X), Y=Y)
+    y = fqm.gemv(w, bf16_dev(X))
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert torch.equal(Y.view(torch.int16), y.view(torch.int16))
+    assert_close(to_f64(Y), oracle.lut6.gemm(packed, inp.lut, X, cols), "bf16", f"M={M}")
+
+
+def test_gemm_small_m_missing_workspace_is_an_error():
+    rows, cols, M = 300, 17408, 8  # the GEMV kernel splits K here: fp32 partials in the workspace
+    w = lut6_weights(rows, cols, 21)
+    assert fqm.gemm_workspace_size(w, M) > 0
+    X = bf16_dev(synth.activations(M, cols, 1))
+    Y = torch.empty((M, rows), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fqm.FqmError) as err:
+        fqm.gemm(w, X, Y=Y, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert err.value.status == 5  # FQM_E_WORKSPACE
+
+
 @pytest.mark.parametrize("rows,cols,M", [(520, 1088, 300), (17408, 5120, 2048), (300, 128, 50),
                                          (5120, 17408, 77)])
 def test_gemm_workspace_rule(rows, cols, M):
