@@ -61,14 +61,21 @@ typedef __attribute__((address_space(3))) const uint16_t lds16c;
 typedef __attribute__((address_space(3))) const u32x4 lds128c;
 typedef __attribute__((address_space(3))) void lvoid;
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int NWAVE = 8;                       // 8 waves along N, 256 x 32 outputs each
-constexpr int MB = BM / 32;                    // 32-row blocks of X per wave
-constexpr int XT_BYTES = BM * BK * 2;          // one X tile, 128-byte rows
+// Tile heights: BM rows of X per workgroup (256 for prefill; 64 for small M,
+// where a 256-row tile would mostly multiply padding).
+constexpr int BM_BIG = 256, BM_SMALL = 64;
+constexpr int BN = 256, BK = 64;
+constexpr int NWAVE = 8;                       // 8 waves along N, BM x 32 outputs each
 constexpr int TAB_BYTES = BN * 128;            // BN row tables, bank-sliced
-constexpr int XDMA = XT_BYTES / 1024 / NWAVE;  // 1 KB direct-to-LDS X loads per wave per step
 constexpr int CD = 3;                          // codes are requested CD steps ahead
-static_assert(XDMA == 4 && BN == 32 * NWAVE && CD == 3, "tile constants (the loop is unrolled by CD + 1)");
+static_assert(BN == 32 * NWAVE && CD == 3, "tile constants (the loop is unrolled by CD + 1)");
+template <int BM>
+struct TileShape {
+    static constexpr int MB = BM / 32;                    // 32-row blocks of X per wave
+    static constexpr int XT_BYTES = BM * BK * 2;          // one X tile, 128-byte rows
+    static constexpr int XDMA = XT_BYTES / 1024 / NWAVE;  // 1 KB direct-to-LDS X loads per wave per step
+    static_assert(XDMA >= 1 && BM % 64 == 0, "every wave loads whole kilobytes of the X tile");
+};
 
 template <int BUF>
 using Buf = std::integral_constant<int, BUF>;
@@ -122,14 +129,15 @@ __device__ __forceinline__ void barrier_after_loads() {
 // tt = b / ksplit, over K steps [t0, t1) of its split b % ksplit.  PARTIAL:
 // the fp32 tile (all BM x BN values) goes to part[b]; otherwise the bf16
 // outputs inside M x N go to Y.
-template <bool PARTIAL>
-__global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* __restrict__ X,
+template <bool PARTIAL, int BM>
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
                                                                const uint8_t* __restrict__ packed,
                                                                int64_t ld,
                                                                const uint16_t* __restrict__ lut,
                                                                uint16_t* __restrict__ Y, float* __restrict__ part,
                                                                int M, int N, int K, int mtiles, int nt0,
                                                                int ksplit) {
+    constexpr int MB = TileShape<BM>::MB, XT_BYTES = TileShape<BM>::XT_BYTES, XDMA = TileShape<BM>::XDMA;
     // Separate LDS objects: the X tiles are written by direct global -> LDS
     // loads, and distinct objects let the compiler see that the table
     // gathers do not wait for those loads.
@@ -298,9 +306,27 @@ __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(const uint16_t* _
     }
 }
 
+#define FQM_GEMM_ARGS                                                                                    \
+    const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed, int64_t ld,                      \
+        const uint16_t *__restrict__ lut, uint16_t *__restrict__ Y, float *__restrict__ part, int M, int N, \
+        int K, int mtiles, int nt0, int ksplit
+template <bool PARTIAL>
+__global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(FQM_GEMM_ARGS) {
+    gemm_tile<PARTIAL, BM_BIG>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
+}
+// 64-row tiles: 48 KB of LDS and at most 96 VGPRs (five waves per SIMD), so
+// two workgroups share a CU
+template <bool PARTIAL>
+__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(5))) void lut6_gemm_small_kernel(
+    FQM_GEMM_ARGS) {
+    gemm_tile<PARTIAL, BM_SMALL>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
+}
+#undef FQM_GEMM_ARGS
+
 // Y for the split tiles: the ksplit fp32 partial tiles of tile tt summed in
 // split order (a fixed order), rounded once to bf16.  Thread: 4 consecutive
 // columns of one tile row.
+template <int BM>
 __global__ __launch_bounds__(256) void lut6_gemm_reduce(const float* __restrict__ part, uint16_t* __restrict__ Y,
                                                         int M, int N, int mtiles, int nt0, int ksplit,
                                                         int64_t groups) {
@@ -326,13 +352,19 @@ __global__ __launch_bounds__(256) void lut6_gemm_reduce(const float* __restrict_
     if (n + 3 < N) y[3] = f32_to_bf16(sum.w);
 }
 
-// Tile plan.  One workgroup per compute unit; whole rounds of tiles run as
-// one launch.  The N tiles left for a last, partial round are split along K
-// (ksplit parts of at least MIN_SPLIT_STEPS steps) so that they occupy every
-// compute unit, and their fp32 partial tiles are reduced afterwards.
+// Tile plan.  Whole rounds of tiles (one per resident workgroup: one per
+// compute unit for 256-row tiles, two for 64-row tiles)
+// run as one launch.  The N tiles left for a last, partial round are split
+// along K (ksplit parts of at least MIN_SPLIT_STEPS steps; at most
+// MAX_SPLIT_SMALL parts for 64-row tiles, whose fp32 partials would
+// otherwise outweigh the weights) so that they occupy the chip, and their
+// fp32 partial tiles are reduced afterwards.
 constexpr int MIN_SPLIT_STEPS = 8;
+constexpr int MAX_SPLIT_SMALL = 4;
+constexpr int64_t SMALL_M_MAX = 64;  // M up to this takes 64-row tiles (measured: faster up to 64 rows, slower at 128 and 256)
 
 struct GemmPlan {
+    int bm = BM_BIG;      // tile height
     int mtiles = 0, ntiles = 0;
     int nt_main = 0;      // N tiles [0, nt_main) in the direct launch
     int ksplit = 1;       // K parts of each remaining tile
@@ -342,20 +374,52 @@ struct GemmPlan {
 
 GemmPlan gemm_plan(int64_t rows, int64_t cols, int64_t M, int cus) {
     GemmPlan p;
-    p.mtiles = (int)((M + BM - 1) / BM);
+    const bool small = M <= SMALL_M_MAX;
+    p.bm = small ? BM_SMALL : BM_BIG;
+    p.mtiles = (int)((M + p.bm - 1) / p.bm);
     p.ntiles = (int)((rows + BN - 1) / BN);
     p.nt_main = p.ntiles;
-    const int64_t tiles = (int64_t)p.mtiles * p.ntiles, slots = std::max(cus, 1);
+    const int64_t tiles = (int64_t)p.mtiles * p.ntiles, slots = (int64_t)std::max(cus, 1) * (small ? 2 : 1);
     if (tiles % slots == 0) return p;
     const int nt_main = (int)((tiles / slots) * slots / p.mtiles);
     const int64_t tail = (int64_t)(p.ntiles - nt_main) * p.mtiles;
-    const int ksplit = (int)std::min<int64_t>(slots / tail, cols / BK / MIN_SPLIT_STEPS);
+    int64_t ksplit = std::min<int64_t>(slots / tail, cols / BK / MIN_SPLIT_STEPS);
+    if (small) ksplit = std::min<int64_t>(ksplit, MAX_SPLIT_SMALL);
     if (ksplit < 2) return p;
     p.nt_main = nt_main;
-    p.ksplit = ksplit;
+    p.ksplit = (int)ksplit;
     p.tail = tail;
-    p.ws_bytes = (size_t)tail * ksplit * BM * BN * sizeof(float);
+    p.ws_bytes = (size_t)tail * ksplit * p.bm * BN * sizeof(float);
     return p;
+}
+
+template <int BM>
+hipError_t launch_plan(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M, void* ws,
+                       const GemmPlan& p, hipStream_t s) {
+    hipError_t e;
+    const int64_t main_tiles = (int64_t)p.nt_main * p.mtiles;
+    auto kernel = [](bool partial) {
+        if constexpr (BM == BM_SMALL) return partial ? lut6_gemm_small_kernel<true> : lut6_gemm_small_kernel<false>;
+        else return partial ? lut6_gemm_kernel<true> : lut6_gemm_kernel<false>;
+    };
+    if (main_tiles > 0) {
+        hipLaunchKernelGGL(kernel(false), dim3((unsigned)main_tiles), dim3(64 * NWAVE), 0, s, X,
+                           w.lut6.packed, w.lut6.ld, w.lut6.lut, Y, nullptr, (int)M, (int)w.rows, (int)w.cols,
+                           p.mtiles, 0, 1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (p.tail > 0) {
+        float* part = static_cast<float*>(ws);
+        hipLaunchKernelGGL(kernel(true), dim3((unsigned)(p.tail * p.ksplit)), dim3(64 * NWAVE), 0, s,
+                           X, w.lut6.packed, w.lut6.ld, w.lut6.lut, Y, part, (int)M, (int)w.rows, (int)w.cols,
+                           p.mtiles, p.nt_main, p.ksplit);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t groups = p.tail * BM * (BN / 4);
+        hipLaunchKernelGGL(lut6_gemm_reduce<BM>, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, part, Y,
+                           (int)M, (int)w.rows, p.mtiles, p.nt_main, p.ksplit, groups);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t device_cus(int* cus) {
@@ -384,25 +448,7 @@ hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y
     const GemmPlan p = gemm_plan(w.rows, w.cols, M, cus);
     if ((int64_t)p.ntiles * p.mtiles > 0x7fffffff) return hipErrorInvalidValue;
     if (p.ws_bytes > ws_bytes || (p.ws_bytes && !ws)) return hipErrorInvalidValue;
-    const int64_t main_tiles = (int64_t)p.nt_main * p.mtiles;
-    if (main_tiles > 0) {
-        hipLaunchKernelGGL(lut6_gemm_kernel<false>, dim3((unsigned)main_tiles), dim3(64 * NWAVE), 0, s, X,
-                           w.lut6.packed, w.lut6.ld, w.lut6.lut, Y, nullptr, (int)M, (int)w.rows, (int)w.cols,
-                           p.mtiles, 0, 1);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if (p.tail > 0) {
-        float* part = static_cast<float*>(ws);
-        hipLaunchKernelGGL(lut6_gemm_kernel<true>, dim3((unsigned)(p.tail * p.ksplit)), dim3(64 * NWAVE), 0, s, X,
-                           w.lut6.packed, w.lut6.ld, w.lut6.lut, Y, part, (int)M, (int)w.rows, (int)w.cols,
-                           p.mtiles, p.nt_main, p.ksplit);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int64_t groups = p.tail * BM * (BN / 4);
-        hipLaunchKernelGGL(lut6_gemm_reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, part, Y,
-                           (int)M, (int)w.rows, p.mtiles, p.nt_main, p.ksplit, groups);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return p.bm == BM_SMALL ? launch_plan<BM_SMALL>(w, X, Y, M, ws, p, s) : launch_plan<BM_BIG>(w, X, Y, M, ws, p, s);
 }
 
 }  // namespace fqm

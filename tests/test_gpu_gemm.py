@@ -11,7 +11,7 @@ from gpu_common import DEV, assert_close, bf16_dev, canaries_intact, guarded, lu
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M", [1, 17, 128, 300])
+@pytest.mark.parametrize("M", [1, 17, 64, 128, 255, 256, 257, 300])
 def test_gemm_ragged(M):
     rows, cols, seed = 520, 1088, 9
     inp, packed = lut6_case(rows, cols, seed)
@@ -38,7 +38,7 @@ def test_gemm_prefill_shape_every_output():
     assert_close(to_f64(Y), yo, "bf16", f"M={M}")
 
 
-@pytest.mark.parametrize("M", [2047, 2048])
+@pytest.mark.parametrize("M", [100, 256, 2047, 2048])
 def test_gemm_prefill_shape_sampled(M):
     rows, cols, seed = 17408, 5120, 2
     inp, packed = lut6_case(rows, cols, seed)
@@ -64,18 +64,25 @@ def test_gemm_matches_gemv_rows():
 
 
 def _plan_ws(rows, cols, M):
-    """Workspace rule of the tile plan: whole rounds of 256 x 256 tiles (one per
-    compute unit) run directly; the N tiles of a last partial round split K
-    into min(CUs // tail tiles, steps // 8) parts (when >= 2) of fp32 tiles."""
+    """Workspace rule of the tile plan: tiles are 256 rows of X tall (64 when
+    M <= 64) and 256 columns wide; whole rounds of tiles (one per compute unit,
+    two per compute unit for 64-row tiles) run directly; the N tiles of a
+    last partial round split K into min(slots // tail tiles, steps // 8) parts
+    (at most 4 for 64-row tiles; split only when >= 2) of fp32 tiles."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    mt, nt = -(-M // 256), -(-rows // 256)
+    small = M <= 64
+    bm = 64 if small else 256
+    mt, nt = -(-M // bm), -(-rows // 256)
     tiles = mt * nt
-    if tiles % cus == 0:
+    slots = cus * (2 if small else 1)
+    if tiles % slots == 0:
         return 0
-    nt_main = (tiles // cus) * cus // mt
+    nt_main = (tiles // slots) * slots // mt
     tail = (nt - nt_main) * mt
-    ks = min(cus // tail, cols // 64 // 8)
-    return tail * ks * 256 * 256 * 4 if ks >= 2 else 0
+    ks = min(slots // tail, cols // 64 // 8)
+    if small:
+        ks = min(ks, 4)
+    return tail * ks * bm * 256 * 4 if ks >= 2 else 0
 
 
 @pytest.mark.parametrize("M", [1, 2, 8, 16])
@@ -108,7 +115,7 @@ def test_gemm_small_m_missing_workspace_is_an_error():
 
 
 @pytest.mark.parametrize("rows,cols,M", [(520, 1088, 300), (17408, 5120, 2048), (300, 128, 50),
-                                         (5120, 17408, 77)])
+                                         (5120, 17408, 77), (17408, 5120, 64), (5120, 17408, 33)])
 def test_gemm_workspace_rule(rows, cols, M):
     w = lut6_weights(256, cols, 1)
     w.desc.rows = rows  # the rule reads the shape only (no launch)
