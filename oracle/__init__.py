@@ -14,6 +14,8 @@ library matrix product:
           "What BenQ stores": decode is the row-wise gather of the code into
           that row's 64-entry table; the table holds 32 negative levels in
           ascending order, then 32 positive).
+  lut4  - the same with 4-bit codes and 16-entry tables (the 8-tier row of
+          the card's "Why equal-width shells" placement table).
   fabq  - binary core with int4 rows, per-block scales and a residual
           codebook ("FABQ-RC" README "Key Ideas" and model card
           "How It Works" / "Quantization Details").
@@ -24,4 +26,4 @@ Pins that tie each part to something other than itself live in
 ``tests/test_oracle_*.py``.  Parity status per function is stated in each
 module header.
 """
-from . import numerics, bits, lut6, fabq, mdbf, compare  # noqa: F401
+from . import numerics, bits, lut6, lut4, fabq, mdbf, compare  # noqa: F401

@@ -40,6 +40,8 @@ __all__ = [
     "activations",
     "Lut6Input",
     "lut6_input",
+    "Lut4Input",
+    "lut4_input",
     "FabqInput",
     "fabq_input",
     "fabq_quantize",
@@ -140,6 +142,40 @@ def _nearest_shell(w, delta, lutv, chunk_rows: int = 1024):
         pick = np.argmin(dist, axis=0)
         out[r0:r0 + chunk_rows] = np.take_along_axis(cand, pick[None], axis=0)[0]
     return out
+
+
+# ---------------------------------------------------------------------------
+# per-row LUT, 4-bit codes (the 8-tier shell placement)
+# ---------------------------------------------------------------------------
+@dataclass
+class Lut4Input:
+    codes: np.ndarray  # uint8 [rows][cols], 0..15
+    lut: np.ndarray    # uint16 bf16 bits [rows][16], ascending by value
+    rows: int
+    cols: int
+    seed: int
+
+
+def lut4_input(rows: int, cols: int, seed: int) -> Lut4Input:
+    """Gaussian rows, 8 equal-width shells per sign, nearest-level codes.
+
+    As lut6_input with 8 tiers: sigma_r log-uniform on [0.005, 0.05],
+    w ~ N(0, sigma_r^2); D_r = max_k |w_rk| / 8, levels (t + 1/2) D_r for
+    t = 0..7; the table is the 16 signed levels ascending, rounded fp64 ->
+    fp32 -> bf16; a weight's code is the index of the nearest bf16 level
+    (fp64 distance, ties to the lower index).  16 levels: the exact argmin.
+    """
+    rng = np.random.default_rng([seed, 4])
+    sigma = np.exp(rng.uniform(math.log(0.005), math.log(0.05), size=rows))
+    w = rng.standard_normal((rows, cols)) * sigma[:, None]
+    delta = np.abs(w).max(axis=1) / 8.0
+    pos = (np.arange(8, dtype=np.float64) + 0.5)[None, :] * delta[:, None]
+    lut = bf16_bits_from_f64(np.concatenate([-pos[:, ::-1], pos], axis=1))
+    lutv = _bf16_bits_to_f64(lut)
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    for r0 in range(0, rows, 512):
+        codes[r0:r0 + 512] = _nearest_full(w[r0:r0 + 512], lutv[r0:r0 + 512])
+    return Lut4Input(codes=codes, lut=lut, rows=rows, cols=cols, seed=seed)
 
 
 # ---------------------------------------------------------------------------
@@ -283,6 +319,8 @@ CONFIGS = {
     "tiny_lut6": dict(rows=256, cols=512, seed=1, batches=(1,), y="f32"),
     "lut6_up": dict(rows=17408, cols=5120, seed=2, batches=(1, 8), y="bf16"),
     "lut6_down": dict(rows=5120, cols=17408, seed=3, batches=(1, 8), y="bf16"),
+    "lut4_up": dict(rows=17408, cols=5120, seed=7, batches=(1,), y="bf16"),
+    "lut4_down": dict(rows=5120, cols=17408, seed=8, batches=(1,), y="bf16"),
     "prefill": dict(M=2048, weights="lut6_up", seed=4),
     "fabq": dict(rows=5120, cols=5120, seed=5, batches=(1, 8)),
     "mdbf": dict(n=4096, m=4096, r=2000, l=2, P=1, seed=6, batches=(1, 16)),
