@@ -23,12 +23,12 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfqm.so")
 
-FQM_LUT6, FQM_FABQ, FQM_MDBF = 1, 2, 3
+FQM_LUT6, FQM_FABQ, FQM_MDBF, FQM_LUT4 = 1, 2, 3, 4
 FQM_BF16, FQM_F32 = 0, 1
 
 __all__ = [
     "FqmError", "FqmNotBuilt", "load", "version", "status_str", "pack_bits", "pack",
-    "unpack", "dequant", "workspace_size", "gemv", "gemm_workspace_size", "gemm", "Lut6Weights", "FabqWeights",
+    "unpack", "dequant", "workspace_size", "gemv", "gemm_workspace_size", "gemm", "Lut6Weights", "Lut4Weights", "FabqWeights",
     "MdbfWeights", "SYMBOLS",
 ]
 
@@ -73,9 +73,13 @@ class _Mdbf(ctypes.Structure):
     _fields_ = [("r", c_int32), ("l", c_int32), ("P", c_int32), ("path", _MdbfPath * 2)]
 
 
+class _Lut4(ctypes.Structure):
+    _fields_ = [("packed", c_void_p), ("lut", c_void_p), ("ld", c_int64)]
+
+
 class _Weights(ctypes.Structure):
     _fields_ = [("format", c_int32), ("rows", c_int64), ("cols", c_int64), ("lut6", _Lut6),
-                ("fabq", _Fabq), ("mdbf", _Mdbf)]
+                ("fabq", _Fabq), ("mdbf", _Mdbf), ("lut4", _Lut4)]
 
 
 _lib = None
@@ -232,6 +236,34 @@ class Lut6Weights(_WeightsBase):
     def nbytes(self) -> int:
         """Algorithmic bytes: packed codes (unpadded) + tables."""
         return self.rows * self.cols * 3 // 4 + self.rows * 128
+
+
+class Lut4Weights(_WeightsBase):
+    """Per-row LUT 4-bit weights: packed [rows][ld] uint8 (two codes per byte),
+    lut [rows][16] bf16."""
+    fmt = FQM_LUT4
+
+    def __init__(self, packed: torch.Tensor, lut: torch.Tensor, rows: int, cols: int):
+        super().__init__(rows, cols)
+        self.packed, self.lut = packed, lut
+        self.desc.lut4.packed = self._hold(packed)
+        self.desc.lut4.lut = self._hold(lut)
+        self.desc.lut4.ld = packed.shape[1] if packed.dim() == 2 else 0
+
+    @classmethod
+    def from_codes(cls, codes, lut_bits, device="cuda", ld: int | None = None):
+        codes_d = _dev(codes, torch.uint8, device)
+        lut_d = _dev(lut_bits, torch.int16, device).view(torch.bfloat16)
+        rows, cols = codes_d.shape
+        packed = pack_bits(codes_d, 4, ld=ld)
+        return cls(packed, lut_d, rows, cols)
+
+    def clone(self):
+        return Lut4Weights(self.packed.clone(), self.lut.clone(), self.rows, self.cols)
+
+    def nbytes(self) -> int:
+        """Algorithmic bytes: packed codes (unpadded) + tables."""
+        return self.rows * self.cols // 2 + self.rows * 32
 
 
 class FabqWeights(_WeightsBase):

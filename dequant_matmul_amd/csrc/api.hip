@@ -30,6 +30,16 @@ fqm_status check_weights(const fqm_weights* w) {
             if (f.ld & 15) return FQM_E_ALIGN;
             return FQM_OK;
         }
+        case FQM_LUT4: {
+            const fqm_lut4& f = w->lut4;
+            if (w->cols % 64) return FQM_E_SHAPE;
+            if (w->rows == 0) return FQM_OK;
+            if (!f.packed || !f.lut) return FQM_E_NULL;
+            if (!aligned16(f.packed) || !aligned16(f.lut)) return FQM_E_ALIGN;
+            if (f.ld < w->cols / 2) return FQM_E_SHAPE;
+            if (f.ld & 15) return FQM_E_ALIGN;
+            return FQM_OK;
+        }
         case FQM_FABQ: {
             const fqm_fabq& f = w->fabq;
             const int bs = f.blocksize;
@@ -135,6 +145,7 @@ fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream) {
     if (!W) return FQM_E_NULL;
     if (!aligned16(W)) return FQM_E_ALIGN;
     if (w->format == FQM_LUT6) return hip_status(launch_dequant_lut6(*w, W, as_stream(stream)));
+    if (w->format == FQM_LUT4) return hip_status(launch_dequant_lut4(*w, W, as_stream(stream)));
     return hip_status(launch_dequant_fabq(*w, W, as_stream(stream)));
 }
 
@@ -164,6 +175,7 @@ fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_
             return hip_status(
                 launch_lut6_gemv(*w, x, y, y_f32, batch, static_cast<float*>(workspace), s));
         }
+        case FQM_LUT4: return hip_status(launch_lut4_gemv(*w, x, y, y_f32, batch, s));
         case FQM_FABQ: return hip_status(launch_fabq_gemv(*w, x, y, y_f32, batch, s));
         case FQM_MDBF: {
             const size_t need = fqm_workspace_size(w, batch);

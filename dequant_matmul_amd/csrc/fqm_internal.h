@@ -76,6 +76,9 @@ hipError_t launch_pack_bits(const uint8_t* vals, uint8_t* out, int64_t rows, int
 hipError_t launch_unpack6(const uint8_t* packed, uint8_t* codes, int64_t rows, int64_t cols,
                           int64_t ld, hipStream_t s);
 hipError_t launch_dequant_lut6(const fqm_weights& w, uint16_t* W, hipStream_t s);
+hipError_t launch_dequant_lut4(const fqm_weights& w, uint16_t* W, hipStream_t s);
+hipError_t launch_lut4_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
+                            hipStream_t s);
 hipError_t launch_dequant_fabq(const fqm_weights& w, uint16_t* W, hipStream_t s);
 
 hipError_t launch_lut6_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,

@@ -14,6 +14,11 @@
  *             gather of codes into the tables, and the card's kernel fuses
  *             that gather into the matrix product.  Codes are packed four per
  *             three bytes, the packing its usage note says the format needs.
+ *   FQM_LUT4  the same card, "Why equal-width shells": its 8-tier, 4-bit
+ *             placement read as the 6-bit format is - one 4-bit code (1 sign
+ *             + 3 tier bits) per weight indexing the row's table of 16 signed
+ *             bf16 levels (8 negative ascending, then 8 positive); codes two
+ *             per byte.
  *   FQM_FABQ  "FABQ-RC" README "Key Ideas" and the FABQ-RC model card
  *             "How It Works" / "Quantization Details": the top 5 % of output
  *             rows as int4 with an fp16 row scale, the rest binary +-1 with an
@@ -69,7 +74,7 @@
 extern "C" {
 #endif
 
-#define FQM_VERSION 1
+#define FQM_VERSION 2
 
 typedef enum fqm_status {
     FQM_OK = 0,
@@ -82,7 +87,7 @@ typedef enum fqm_status {
     FQM_E_HIP = 7          /* a HIP launch failed */
 } fqm_status;
 
-enum fqm_format { FQM_LUT6 = 1, FQM_FABQ = 2, FQM_MDBF = 3 };
+enum fqm_format { FQM_LUT6 = 1, FQM_FABQ = 2, FQM_MDBF = 3, FQM_LUT4 = 4 };
 enum fqm_dtype { FQM_BF16 = 0, FQM_F32 = 1 };
 
 /* Per-row LUT, 6-bit codes (rows = N outputs, cols = K inputs).
@@ -92,6 +97,14 @@ typedef struct fqm_lut6 {
     const uint16_t* lut;    /* [rows][64] bf16, entry j is the level of code j */
     int64_t ld;             /* bytes per packed row, >= cols*3/4 */
 } fqm_lut6;
+
+/* Per-row LUT, 4-bit codes (rows = N outputs, cols = K inputs).
+ * cols must be a multiple of 64. */
+typedef struct fqm_lut4 {
+    const uint8_t* packed;  /* [rows][ld] bytes, 4-bit fields (code 2j in the low nibble of byte j) */
+    const uint16_t* lut;    /* [rows][16] bf16, entry j is the level of code j */
+    int64_t ld;             /* bytes per packed row, >= cols/2 */
+} fqm_lut4;
 
 /* FABQ-RC-style core (rows = N, cols = K).  Stored row i (0 <= i < rows)
  * produces output row row_of[i]; stored rows 0..n_hi-1 are int4 rows, stored
@@ -140,6 +153,7 @@ typedef struct fqm_weights {
     fqm_lut6 lut6;
     fqm_fabq fabq;
     fqm_mdbf mdbf;
+    fqm_lut4 lut4;              /* last, so the earlier members keep their offsets */
 } fqm_weights;
 
 /* Library version (FQM_VERSION). */
@@ -171,7 +185,7 @@ fqm_status fqm_unpack(const uint8_t* packed, uint8_t* codes, int64_t rows, int64
                       int64_t ld, void* stream);
 
 /* Test helper: write the decoded weights W [rows][cols] as bf16, row-major,
- * row index = output row.  LUT6: W[r][k] = lut[r][code] (an exact copy).
+ * row index = output row.  LUT6 and LUT4: W[r][k] = lut[r][code] (an exact copy).
  * FABQ: the exact value of q*s or s_b*(+-1) + c[idx] rounded once to bf16
  * (nearest even).  MDBF: FQM_E_UNSUPPORTED (W is a product of factors). */
 fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
@@ -192,8 +206,8 @@ size_t fqm_workspace_size(const fqm_weights* w, int32_t batch);
  * FQM_BF16) or fp32 (FQM_F32).  workspace: device memory of at least
  * fqm_workspace_size(w, batch) bytes (may be NULL when that is 0); its
  * contents on entry do not matter and are clobbered.
- * LUT6 follows the BenQ card's decode (a gather into the row's table) fused
- * into the product; FABQ and MDBF follow the decode stated with each format
+ * LUT6 and LUT4 follow the BenQ card's decode (a gather into the row's table)
+ * fused into the product; FABQ and MDBF follow the decode stated with each format
  * above; every decoded weight stays in fp32 (never rounded to bf16). */
 fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
                     int32_t batch, void* workspace, size_t ws_bytes, void* stream);
@@ -220,7 +234,7 @@ size_t fqm_gemm_workspace_size(const fqm_weights* w, int64_t M);
  * Up to 16 rows of X on a shape the GEMV kernels cover run those kernels (the
  * same product as fqm_gemv with batch = M and bf16 output; the 256-row tiles
  * would mostly multiply padding there).
- * FABQ / MDBF descriptors return FQM_E_UNSUPPORTED. */
+ * LUT4 / FABQ / MDBF descriptors return FQM_E_UNSUPPORTED. */
 fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_t M,
                     void* workspace, size_t ws_bytes, void* stream);
 

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert decl == set(fqm.SYMBOLS)
     for name in decl:
         assert hasattr(lib, name), name
-    assert lib.fqm_version() == 1
+    assert lib.fqm_version() == 2
 
 
 def test_status_strings(lib):
@@ -83,6 +83,33 @@ def test_lut6_argument_errors(lib):
     assert lib.fqm_gemm_workspace_size(ctypes.byref(lut6()), 0) == 0
     assert lib.fqm_gemm_workspace_size(ctypes.byref(lut6()), -3) == 0
     assert lib.fqm_gemm_workspace_size(None, 4) == 0
+
+
+def lut4(rows=64, cols=128, ld=64, packed=FAKE, lut=FAKE):
+    w = fqm._Weights()
+    w.format, w.rows, w.cols = fqm.FQM_LUT4, rows, cols
+    w.lut4.packed, w.lut4.lut, w.lut4.ld = packed, lut, ld
+    return w
+
+
+def test_lut4_argument_errors(lib):
+    assert gemv(lib, lut4(cols=96)) == E["SHAPE"]             # cols % 64
+    assert gemv(lib, lut4(ld=48)) == E["SHAPE"]               # ld < cols/2
+    assert gemv(lib, lut4(ld=72)) == E["ALIGN"]               # ld % 16
+    assert gemv(lib, lut4(packed=FAKE + 4)) == E["ALIGN"]
+    assert gemv(lib, lut4(lut=None)) == E["NULL"]
+    assert gemv(lib, lut4(), batch=17) == E["SHAPE"]
+    assert gemv(lib, lut4(rows=0, packed=None, lut=None)) == E["OK"]
+    assert gemm(lib, lut4()) == E["UNSUPPORTED"]              # no LUT4 GEMM
+    assert lib.fqm_workspace_size(ctypes.byref(lut4()), 8) == 0
+    assert lib.fqm_gemm_workspace_size(ctypes.byref(lut4()), 8) == 0
+
+
+def test_descriptor_layout_matches_the_header():
+    """The LUT4 member sits after the others, so their offsets are unchanged."""
+    W = fqm._Weights
+    assert W.lut4.offset > W.mdbf.offset > W.fabq.offset > W.lut6.offset
+    assert ctypes.sizeof(fqm._Lut4) == 24
 
 
 def test_lut6_workspace_rule(lib):

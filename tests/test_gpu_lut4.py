@@ -1,0 +1,86 @@
+"""GPU parity for the per-row LUT 4-bit GEMV (16-entry tables, two codes per byte)."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_matmul_amd as fqm
+import oracle
+import synth
+from gpu_common import DEV, assert_close, bf16_dev, canaries_intact, guarded, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=None)
+def case(rows, cols, seed):
+    inp = synth.lut4_input(rows, cols, seed)
+    return inp, oracle.lut4.pack_codes(inp.codes)
+
+
+def weights(rows, cols, seed):
+    inp, _ = case(rows, cols, seed)
+    return fqm.Lut4Weights.from_codes(inp.codes, inp.lut, device=DEV)
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(130, 1024, 1), (77, 3136, 2), (5120, 5120, 3)])
+def test_pack_and_dequant_are_bit_exact(rows, cols, seed):
+    inp, packed = case(rows, cols, seed)
+    w = weights(rows, cols, seed)
+    assert np.array_equal(w.packed[:, :cols // 2].cpu().numpy(), packed)
+    W = fqm.dequant(w).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(W, inp.lut[np.arange(rows)[:, None], inp.codes])
+
+
+# 1, 11 and 31 whole 1024-column cells (the cell kernel), the full layers
+CELL_SHAPES = [(77, 1024, 4), (301, 11264, 5), (97, 31744, 6), (17408, 5120, 7), (5120, 17408, 8)]
+
+
+@pytest.mark.parametrize("rows,cols,seed", CELL_SHAPES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemv_b1_cells(rows, cols, seed, out):
+    inp, packed = case(rows, cols, seed)
+    w = weights(rows, cols, seed)
+    x = synth.activations(1, cols, seed)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    buf, y = guarded((1, rows), dt)
+    fqm.gemv(w, bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.lut4.gemv(packed, inp.lut, x, cols), out, f"{rows}x{cols} {out}")
+
+
+@pytest.mark.parametrize("batch", [1, 2, 5, 8, 16])
+def test_gemv_generic_widths_and_batches(batch):
+    """Widths that are not whole cells (and every batch above 1) take the
+    generic kernel."""
+    for rows, cols, seed in ((70, 1088, 9), (33, 4160, 10)):
+        inp, packed = case(rows, cols, seed)
+        w = weights(rows, cols, seed)
+        x = synth.activations(batch, cols, seed)
+        buf, y = guarded((batch, rows), torch.float32)
+        fqm.gemv(w, bf16_dev(x), y=y)
+        torch.cuda.synchronize()
+        assert canaries_intact(buf)
+        assert_close(to_f64(y), oracle.lut4.gemv(packed, inp.lut, x, cols), "f32", f"{rows}x{cols} b{batch}")
+
+
+def test_gemv_b8_full_layer():
+    inp, packed = case(17408, 5120, 7)
+    w = weights(17408, 5120, 7)
+    x = synth.activations(8, 5120, 11)
+    y = fqm.gemv(w, bf16_dev(x))
+    assert_close(to_f64(y), oracle.lut4.gemv(packed, inp.lut, x, 5120), "bf16", "b8")
+
+
+def test_gemv_mirror_negates():
+    """Mirror-symmetric tables: codes c -> 15 - c give -y (fp32 output; the
+    kernel's fp32 sums need not negate bit for bit, so within rounding)."""
+    inp, packed = case(300, 2048, 12)
+    x = bf16_dev(synth.activations(1, 2048, 12))
+    w = fqm.Lut4Weights.from_codes(inp.codes, inp.lut, device=DEV)
+    wm = fqm.Lut4Weights.from_codes(15 - inp.codes, inp.lut, device=DEV)
+    y = to_f64(fqm.gemv(w, x, out_dtype=torch.float32))
+    ym = to_f64(fqm.gemv(wm, x, out_dtype=torch.float32))
+    assert np.allclose(ym, -y, rtol=1e-5, atol=1e-6 * np.abs(y).max())
