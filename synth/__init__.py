@@ -125,18 +125,20 @@ def _nearest_full(w, lutv):
 def _nearest_shell(w, delta, lutv, chunk_rows: int = 1024):
     """Shell index, then a +-1 neighbour check against the bf16 levels.
 
-    bf16 rounding moves a level by at most 2^-9 of its value (< 0.07 D), so the
-    nearest rounded level is the shell's own level or an adjacent one.
+    bf16 rounding moves a level by at most 2^-9 of its value (< 0.07 D with
+    32 tiers, < 0.015 D with 8), so the nearest rounded level is the shell's
+    own level or an adjacent one.  The tier count T is half the table width.
     """
     rows, cols = w.shape
+    T = lutv.shape[1] // 2
     out = np.empty((rows, cols), dtype=np.uint8)
     for r0 in range(0, rows, chunk_rows):
         ws = w[r0:r0 + chunk_rows]
         lv = lutv[r0:r0 + chunk_rows]
         dl = delta[r0:r0 + chunk_rows, None]
-        tier = np.minimum(np.floor(np.abs(ws) / dl), 31).astype(np.int64)
-        c0 = np.where(ws >= 0, 32 + tier, 31 - tier)
-        cand = np.stack([np.clip(c0 - 1, 0, 63), c0, np.clip(c0 + 1, 0, 63)], axis=0)
+        tier = np.minimum(np.floor(np.abs(ws) / dl), T - 1).astype(np.int64)
+        c0 = np.where(ws >= 0, T + tier, T - 1 - tier)
+        cand = np.stack([np.clip(c0 - 1, 0, 2 * T - 1), c0, np.clip(c0 + 1, 0, 2 * T - 1)], axis=0)
         vals = np.take_along_axis(np.broadcast_to(lv[None], (3,) + lv.shape), cand, axis=2)
         dist = np.abs(ws[None] - vals)
         pick = np.argmin(dist, axis=0)
@@ -156,14 +158,15 @@ class Lut4Input:
     seed: int
 
 
-def lut4_input(rows: int, cols: int, seed: int) -> Lut4Input:
+def lut4_input(rows: int, cols: int, seed: int, *, exact_argmin: bool = False) -> Lut4Input:
     """Gaussian rows, 8 equal-width shells per sign, nearest-level codes.
 
     As lut6_input with 8 tiers: sigma_r log-uniform on [0.005, 0.05],
     w ~ N(0, sigma_r^2); D_r = max_k |w_rk| / 8, levels (t + 1/2) D_r for
     t = 0..7; the table is the 16 signed levels ascending, rounded fp64 ->
     fp32 -> bf16; a weight's code is the index of the nearest bf16 level
-    (fp64 distance, ties to the lower index).  16 levels: the exact argmin.
+    (fp64 distance, ties to the lower index), found by the shell shortcut
+    unless ``exact_argmin``.
     """
     rng = np.random.default_rng([seed, 4])
     sigma = np.exp(rng.uniform(math.log(0.005), math.log(0.05), size=rows))
@@ -172,9 +175,12 @@ def lut4_input(rows: int, cols: int, seed: int) -> Lut4Input:
     pos = (np.arange(8, dtype=np.float64) + 0.5)[None, :] * delta[:, None]
     lut = bf16_bits_from_f64(np.concatenate([-pos[:, ::-1], pos], axis=1))
     lutv = _bf16_bits_to_f64(lut)
-    codes = np.empty((rows, cols), dtype=np.uint8)
-    for r0 in range(0, rows, 512):
-        codes[r0:r0 + 512] = _nearest_full(w[r0:r0 + 512], lutv[r0:r0 + 512])
+    if exact_argmin:
+        codes = np.empty((rows, cols), dtype=np.uint8)
+        for r0 in range(0, rows, 512):
+            codes[r0:r0 + 512] = _nearest_full(w[r0:r0 + 512], lutv[r0:r0 + 512])
+    else:
+        codes = _nearest_shell(w, delta, lutv)
     return Lut4Input(codes=codes, lut=lut, rows=rows, cols=cols, seed=seed)
 
 

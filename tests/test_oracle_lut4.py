@@ -88,3 +88,9 @@ def test_gemv_one_hot_constant_and_mirror():
 
 def test_bits_per_weight():
     assert lut4.bpw(5120) == 4.0 + 256.0 / 5120
+
+
+def test_generator_shell_shortcut_equals_full_argmin():
+    a = synth.lut4_input(256, 1024, seed=5)
+    b = synth.lut4_input(256, 1024, seed=5, exact_argmin=True)
+    assert np.array_equal(a.codes, b.codes)
