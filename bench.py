@@ -6,6 +6,7 @@ synthetic input already resident in HBM:
   lut6_up_b1, lut6_down_b1   LUT6 GEMV, batch 1 (W 17408x5120 and 5120x17408)
   lut6_up_b8, lut6_down_b8   LUT6 GEMV, batch 8
   prefill                    LUT6 GEMM, X 2048x5120 times the up weights
+  lut4_up_b1, lut4_down_b1   LUT4 GEMV, batch 1, the same two shapes
   fabq_b1, fabq_b8           FABQ-RC-style GEMV, 5120x5120, the layer's drawn blocksize
   mdbf_b1, mdbf_b16          MDBF GEMV, n = m = 4096, r = 2000, l = 2, P = 1
 
@@ -146,6 +147,22 @@ def main():
             fn=lambda s, ws=ws, X=X, Y=Y, gws=gws: fqm.gemm(ws[(s + 1) % len(ws)], X, Y=Y, workspace=gws),
             bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * K,
             bound="mfma", kernel="lut6_gemm (with its K-split last round and reduction)")
+
+    # ---- LUT4 weights (up, down shapes), batch 1 ----------------------------------
+    for name in ("up", "down"):
+        cfg = C[f"lut4_{name}"]
+        key = f"lut4_{name}_b1"
+        if not wanted(key):
+            continue
+        inp = synth.lut4_input(cfg["rows"], cfg["cols"], cfg["seed"])
+        q0 = fqm.Lut4Weights.from_codes(inp.codes, inp.lut, device=dev)
+        qcopies = [q0] + [q0.clone() for _ in range(n_copies(q0) - 1)]
+        x = bf16(synth.activations(1, cfg["cols"], cfg["seed"]))
+        y = torch.empty((1, cfg["rows"]), dtype=torch.bfloat16, device=dev)
+        rows[key] = dict(fn=lambda s, ws=qcopies, x=x, y=y: fqm.gemv(ws[s % len(ws)], x, y=y),
+                         bytes=q0.nbytes() + x.numel() * 2 + y.numel() * 2,
+                         flops=2 * cfg["rows"] * cfg["cols"], bound="hbm",
+                         kernel="lut4_gemv_cells, batch 1")
 
     # ---- FABQ (5120^2, the layer's drawn blocksize) ------------------------------
     fabq_bs = None
