@@ -7,6 +7,7 @@ synthetic input already resident in HBM:
   lut6_up_b8, lut6_down_b8   LUT6 GEMV, batch 8
   prefill                    LUT6 GEMM, X 2048x5120 times the up weights
   lut4_up_b1, lut4_down_b1   LUT4 GEMV, batch 1, the same two shapes
+  lut4_up_b8, lut4_down_b8   LUT4 GEMV, batch 8
   fabq_b1, fabq_b8           FABQ-RC-style GEMV, 5120x5120, the layer's drawn blocksize
   mdbf_b1, mdbf_b16          MDBF GEMV, n = m = 4096, r = 2000, l = 2, P = 1
 
@@ -148,21 +149,29 @@ def main():
             bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * K,
             bound="mfma", kernel="lut6_gemm (with its K-split last round and reduction)")
 
-    # ---- LUT4 weights (up, down shapes), batch 1 ----------------------------------
+    # ---- LUT4 weights (up, down shapes), batch 1 and 8 ---------------------------
     for name in ("up", "down"):
         cfg = C[f"lut4_{name}"]
-        key = f"lut4_{name}_b1"
-        if not wanted(key):
+        keys = [f"lut4_{name}_b{b}" for b in cfg["batches"]]
+        if not wanted(*keys):
             continue
         inp = synth.lut4_input(cfg["rows"], cfg["cols"], cfg["seed"])
         q0 = fqm.Lut4Weights.from_codes(inp.codes, inp.lut, device=dev)
         qcopies = [q0] + [q0.clone() for _ in range(n_copies(q0) - 1)]
-        x = bf16(synth.activations(1, cfg["cols"], cfg["seed"]))
-        y = torch.empty((1, cfg["rows"]), dtype=torch.bfloat16, device=dev)
-        rows[key] = dict(fn=lambda s, ws=qcopies, x=x, y=y: fqm.gemv(ws[s % len(ws)], x, y=y),
-                         bytes=q0.nbytes() + x.numel() * 2 + y.numel() * 2,
-                         flops=2 * cfg["rows"] * cfg["cols"], bound="hbm",
-                         kernel="lut4_gemv_cells, batch 1")
+        for b, key in zip(cfg["batches"], keys):
+            if not wanted(key):
+                continue
+            x = bf16(synth.activations(b, cfg["cols"], cfg["seed"]))
+            y = torch.empty((b, cfg["rows"]), dtype=torch.bfloat16, device=dev)
+            off = 0 if b == 1 else len(qcopies) // 2
+            ws_bytes = fqm.workspace_size(q0, b)
+            wsp = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+            rows[key] = dict(
+                fn=(lambda s, ws=qcopies, x=x, y=y, off=off, wsp=wsp:
+                    fqm.gemv(ws[(s + off) % len(ws)], x, y=y, workspace=wsp)),
+                bytes=q0.nbytes() + x.numel() * 2 + y.numel() * 2,
+                flops=2 * b * cfg["rows"] * cfg["cols"], bound="hbm",
+                kernel="lut4_gemv_cells, batch 1" if b == 1 else f"lut4_gemv_mfma_kernel, batch {b}")
 
     # ---- FABQ (5120^2, the layer's drawn blocksize) ------------------------------
     fabq_bs = None

@@ -151,7 +151,7 @@ fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream) {
 
 size_t fqm_workspace_size(const fqm_weights* w, int32_t batch) {
     if (check_weights(w) != FQM_OK || batch < 1 || batch > 16) return 0;
-    if (w->format == FQM_LUT6) return fqm::lut6_gemv_mfma_workspace(*w, batch);
+    if (w->format == FQM_LUT6 || w->format == FQM_LUT4) return fqm::lut_gemv_mfma_workspace(*w, batch);
     if (w->format != FQM_MDBF) return 0;
     return fqm::mdbf_workspace_bytes(*w, batch);
 }
@@ -175,7 +175,13 @@ fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_
             return hip_status(
                 launch_lut6_gemv(*w, x, y, y_f32, batch, static_cast<float*>(workspace), s));
         }
-        case FQM_LUT4: return hip_status(launch_lut4_gemv(*w, x, y, y_f32, batch, s));
+        case FQM_LUT4: {
+            const size_t need = fqm_workspace_size(w, batch);
+            if (need && (!workspace || ws_bytes < need)) return FQM_E_WORKSPACE;
+            if (need && !aligned16(workspace)) return FQM_E_ALIGN;
+            return hip_status(
+                launch_lut4_gemv(*w, x, y, y_f32, batch, static_cast<float*>(workspace), s));
+        }
         case FQM_FABQ: return hip_status(launch_fabq_gemv(*w, x, y, y_f32, batch, s));
         case FQM_MDBF: {
             const size_t need = fqm_workspace_size(w, batch);
@@ -199,7 +205,7 @@ static bool gemm_as_gemv(const fqm_weights& w, int64_t M) {
 size_t fqm_gemm_workspace_size(const fqm_weights* w, int64_t M) {
     if (check_weights(w) != FQM_OK || w->format != FQM_LUT6 || M <= 0 || w->rows == 0) return 0;
     if (w->cols % 64 || M * w->cols * 2 > INT32_MAX) return 0;
-    if (gemm_as_gemv(*w, M)) return fqm::lut6_gemv_mfma_workspace(*w, (int)M);
+    if (gemm_as_gemv(*w, M)) return fqm::lut_gemv_mfma_workspace(*w, (int)M);
     return fqm::lut6_gemm_workspace(*w, M);
 }
 

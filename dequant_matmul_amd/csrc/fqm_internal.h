@@ -78,20 +78,22 @@ hipError_t launch_unpack6(const uint8_t* packed, uint8_t* codes, int64_t rows, i
 hipError_t launch_dequant_lut6(const fqm_weights& w, uint16_t* W, hipStream_t s);
 hipError_t launch_dequant_lut4(const fqm_weights& w, uint16_t* W, hipStream_t s);
 hipError_t launch_lut4_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
-                            hipStream_t s);
+                            float* ws, hipStream_t s);
 hipError_t launch_dequant_fabq(const fqm_weights& w, uint16_t* W, hipStream_t s);
 
 hipError_t launch_lut6_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
                             int batch, float* ws, hipStream_t s);
-// Batch 2..16 on the matrix cores (cols a multiple of 1024); K may be split
-// over workgroups, with fp32 partial sums in the caller's workspace.
-bool lut6_gemv_mfma_supported(const fqm_weights& w, int batch);
+// Batch 2..16 of either LUT format (6- or 4-bit codes) on the matrix cores
+// (cols a multiple of 512); K may be split over workgroups, with fp32 partial
+// sums in the caller's workspace.  Support and workspace depend on the shape
+// and batch only.
+bool lut_gemv_mfma_supported(const fqm_weights& w, int batch);
 // true when launch_lut6_gemv takes a tuned kernel for this shape and batch
 // (the cell kernel at batch 1, the matrix-core kernel at 2..16)
 bool lut6_gemv_fast_path(const fqm_weights& w, int batch);
-size_t lut6_gemv_mfma_workspace(const fqm_weights& w, int batch);
-hipError_t launch_lut6_gemv_mfma(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
-                                 float* ws, hipStream_t s);
+size_t lut_gemv_mfma_workspace(const fqm_weights& w, int batch);
+hipError_t launch_lut_gemv_mfma(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
+                                float* ws, hipStream_t s);
 size_t lut6_gemm_workspace(const fqm_weights& w, int64_t M);
 hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M, void* ws,
                             size_t ws_bytes, hipStream_t s);

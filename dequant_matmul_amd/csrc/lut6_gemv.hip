@@ -290,13 +290,13 @@ hipError_t launch_b1(const fqm_weights& w, const uint16_t* x, void* y, int y_f32
 }  // namespace
 
 bool lut6_gemv_fast_path(const fqm_weights& w, int batch) {
-    return batch == 1 ? rows_supported(w) : lut6_gemv_mfma_supported(w, batch);
+    return batch == 1 ? rows_supported(w) : lut_gemv_mfma_supported(w, batch);
 }
 
 hipError_t launch_lut6_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
                             int batch, float* ws, hipStream_t s) {
     if (batch == 1 && rows_supported(w)) return launch_b1(w, x, y, y_f32, s);
-    if (lut6_gemv_mfma_supported(w, batch)) return launch_lut6_gemv_mfma(w, x, y, y_f32, batch, ws, s);
+    if (lut_gemv_mfma_supported(w, batch)) return launch_lut_gemv_mfma(w, x, y, y_f32, batch, ws, s);
     switch (batch) {
         case 1: return launch_b<1>(w, x, y, y_f32, s);
         case 2: return launch_b<2>(w, x, y, y_f32, s);

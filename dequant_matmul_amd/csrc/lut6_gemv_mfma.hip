@@ -1,7 +1,10 @@
-// Per-row LUT 6-bit GEMV for batch 2..16: y[b][r] = sum_k lut[r][code[r][k]] * x[b][k].
+// Per-row LUT GEMV for batch 2..16: y[b][r] = sum_k lut[r][code[r][k]] * x[b][k],
+// 6-bit codes (64-entry tables, 4 codes per 3 bytes) or 4-bit codes (16-entry
+// tables, 2 codes per byte).
 //
 // Source: "Qwen3.8-27B - BenQ 6-bit", "What BenQ stores": a weight is its
-// row's table entry selected by the 6-bit code, gathered inside the matmul.
+// row's table entry selected by the 6-bit code, gathered inside the matmul;
+// "Why equal-width shells" places 8 tiers in 4 bits, read the same way.
 //
 // With more than one activation row the multiply-adds per weight grow with
 // the batch, so the contraction runs on the matrix cores
@@ -10,11 +13,11 @@
 //   - A workgroup owns 16 rows (one MFMA row block) and a range of 512-wide
 //     K chunks; wave w takes k [64 w, 64 w + 64) of every chunk.
 //   - Codes arrive with coalesced loads (a wave instruction reads 384
-//     contiguous bytes of each of two rows) four chunks ahead and pass
-//     through a small LDS buffer (16 rows x 384 bytes per chunk), because
-//     the operand layout wants 16 rows per wave instruction.
+//     (6-bit) or 256 (4-bit) contiguous bytes of each of two rows) four
+//     chunks ahead and pass through a small LDS buffer (16 rows x one chunk),
+//     because the operand layout wants 16 rows per wave instruction.
 //   - Weights are gathered straight into the MFMA row operand: lane
-//     (r = lane % 16, g = lane / 16) reads the 12-byte piece of row r holding
+//     (r = lane % 16, g = lane / 16) reads the 12- (8-) byte piece of row r holding
 //     codes [16 g, 16 g + 16) of the wave's 64 k, gathers the 16 bf16 values
 //     from row r's table and packs them into the operands of the wave's two
 //     32-wide k slices (slice s uses codes 16 g + 8 s + e; the x operand is
@@ -55,9 +58,7 @@ constexpr int RB = 16;                         // rows per workgroup
 constexpr int NW = 8;                          // waves per workgroup
 constexpr int CH = 512;                        // k per chunk
 constexpr int CSLOTS = 4;                      // code register slots: chunks are loaded 4 steps ahead
-constexpr int CB_ROW = 400;                    // code buffer row stride (384 bytes + 16: conflict-free reads)
 constexpr int SLICES = CH / 32 / NW;           // k slices per wave per chunk
-constexpr int TAB_BYTES = 64 * 256;            // 16 rows x 4 copies x 64 entries, 4-byte slots
 constexpr int SPLIT_TARGET = 1024;             // aim for at least this many workgroups
 static_assert(SLICES == 2 && CH == 64 * NW, "a wave takes 64 k of a chunk: 16 codes per lane");
 
@@ -74,13 +75,26 @@ __device__ __forceinline__ uint32_t perm_lo16(uint32_t hi, uint32_t lo) {
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// Table offset of code J of a 12-byte piece d0..d2: the code's 6 bits moved
-// to bits 8..13 (entry stride 256 bytes), other bits still to be masked.
-template <int J>
-__device__ __forceinline__ uint32_t code_x256(uint32_t d0, uint32_t d1, uint32_t d2) {
-    constexpr int bit = 6 * J, w = bit >> 5, o = bit & 31;
-    const uint32_t d[3] = {d0, d1, d2};
-    if constexpr (o + 6 <= 32) {
+// Per code width: piece bytes (16 codes), table entries, code buffer row
+// stride (a chunk's bytes + 16, so that a read of 16 rows starts in 16
+// different bank groups), table bytes (4 copies x 16 rows x
+// entries, 4-byte slots; at least what the final reduction reuses).
+template <int BITS>
+struct LutFmt {
+    static constexpr int PB = 2 * BITS;
+    static constexpr int ND = PB / 4;
+    static constexpr int ENTRIES = 1 << BITS;
+    static constexpr int CHB = CH * BITS / 8;
+    static constexpr int CB_ROW = CHB + 16;
+    static constexpr int TAB_BYTES = std::max(ENTRIES * 256, NW * 64 * 16);
+};
+
+// Table offset of code J of a piece d[0..ND): the code's bits moved to bits
+// 8.. (entry stride 256 bytes), other bits still to be masked.
+template <int BITS, int J>
+__device__ __forceinline__ uint32_t code_x256(const uint32_t* d) {
+    constexpr int bit = BITS * J, w = bit >> 5, o = bit & 31;
+    if constexpr (o + BITS <= 32) {
         if constexpr (o >= 8) return d[w] >> (o - 8);
         else return d[w] << (8 - o);
     } else {
@@ -98,11 +112,13 @@ __device__ __forceinline__ uint32_t tpos(uint32_t r, uint32_t q) {
 
 // XROWS: batch rows an x block holds (8 or 16, >= batch); XPT = XROWS / 8
 // 16-byte x pieces per thread per chunk.
-template <int XROWS>
-__global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
+template <int BITS, int XROWS>
+__device__ __forceinline__ void gemv_mfma_body(
     const uint8_t* __restrict__ packed, int64_t ld, const uint16_t* __restrict__ lut,
     const uint16_t* __restrict__ x, void* __restrict__ y, int y_f32, float* __restrict__ part,
     int rows, int cols, int batch, int nblocks, int cps) {
+    using F = LutFmt<BITS>;
+    constexpr int PB = F::PB, ND = F::ND, CHB = F::CHB, CB_ROW = F::CB_ROW, TAB_BYTES = F::TAB_BYTES;
     __shared__ __attribute__((aligned(16))) uint8_t s_tab[TAB_BYTES];
     constexpr int XPT = XROWS / 8;
     __shared__ __attribute__((aligned(16))) uint8_t s_x0[XROWS * 1024];
@@ -125,33 +141,38 @@ __global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
     const int n = c1 - c0;
 
     // row tables, four copies: thread t writes copy t / 128 of entries
-    // 8 (t % 8) .. + 7 of row (t / 8) % 16 (loaded here, stored to LDS once
-    // the first code and x loads are out, so that their latencies overlap)
+    // EPT (t % 8) .. + EPT - 1 of row (t / 8) % 16 (loaded here, stored to LDS
+    // once the first code and x loads are out, so that their latencies overlap)
+    constexpr int EPT = F::ENTRIES / 8;  // entries per thread: 8 (6-bit) or 2 (4-bit)
     const int tr = (tid >> 3) & 15, tpart = tid & 7, tcp = tid >> 7;
-    const u32x4 tv = *reinterpret_cast<const u32x4*>(lut + (int64_t)min(n0 + tr, rows - 1) * 64 + tpart * 8);
+    uint32_t tv[EPT / 2];
+    {
+        const uint32_t* tsrc =
+            reinterpret_cast<const uint32_t*>(lut + (int64_t)min(n0 + tr, rows - 1) * F::ENTRIES + tpart * EPT);
+#pragma unroll
+        for (int i = 0; i < EPT / 2; ++i) tv[i] = tsrc[i];
+    }
     static_assert(64 * NW == RB * 8 * 4, "one table item per thread");
 
     // Global code loads: wave w, lane half h, lane j = lane % 32 loads the
-    // 12-byte piece j of row 2 w + h.  Chunk c goes to register slot
-    // c % CSLOTS, then to the code buffer.
+    // piece j of row 2 w + h.  Chunk c goes to register slot c % CSLOTS, then
+    // to the code buffer.
     const int crow = 2 * wave + (lane >> 5), cpiece = lane & 31;
-    const uint8_t* prow = packed + (int64_t)min(n0 + crow, rows - 1) * ld + (int64_t)384 * c0 + 12 * cpiece;
-    uint32_t cr[CSLOTS][3];
+    const uint8_t* prow = packed + (int64_t)min(n0 + crow, rows - 1) * ld + (int64_t)CHB * c0 + PB * cpiece;
+    uint32_t cr[CSLOTS][ND];
     auto load_codes = [&](int cs, int c) {
         const int cc = min(c, n - 1);
-        const uint32_t* q = reinterpret_cast<const uint32_t*>(prow + 384 * cc);
-        cr[cs % CSLOTS][0] = __builtin_nontemporal_load(q);
-        cr[cs % CSLOTS][1] = __builtin_nontemporal_load(q + 1);
-        cr[cs % CSLOTS][2] = __builtin_nontemporal_load(q + 2);
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(prow + CHB * cc);
+#pragma unroll
+        for (int i = 0; i < ND; ++i) cr[cs % CSLOTS][i] = __builtin_nontemporal_load(q + i);
     };
     auto store_codes = [&](int cs, int buf) {
-        lds8* d = CB[buf] + CB_ROW * crow + 12 * cpiece;
-        *(lds32*)d = cr[cs % CSLOTS][0];
-        *(lds32*)(d + 4) = cr[cs % CSLOTS][1];
-        *(lds32*)(d + 8) = cr[cs % CSLOTS][2];
+        lds8* d = CB[buf] + CB_ROW * crow + PB * cpiece;
+#pragma unroll
+        for (int i = 0; i < ND; ++i) *(lds32*)(d + 4 * i) = cr[cs % CSLOTS][i];
     };
     // lane (r16, g): row n0 + r16, codes [64 wave + 16 g, + 16) of each chunk
-    const uint32_t cread = (uint32_t)(CB_ROW * r16 + 48 * wave + 12 * g);
+    const uint32_t cread = (uint32_t)(CB_ROW * r16 + 4 * PB * wave + PB * g);
     const uint32_t tabrow = (uint32_t)(4 * (16 * g + r16));  // (code << 8) | tabrow
 
     // x block of chunk c0 + c: piece p = tid + 256 u is batch row p / 64,
@@ -176,31 +197,33 @@ __global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
         for (int u = 0; u < XPT; ++u) *(lds128*)(XS[buf] + xdst[u]) = xw[set][u];
     };
 
-    uint32_t mask = 0x3F00u;
+    uint32_t mask = (uint32_t)(F::ENTRIES - 1) << 8;
     asm volatile("" : "+v"(mask));  // in a VGPR: (code & mask) | row is one v_and_or_b32
     // Gather the 16 weights of the chunk whose codes sit in code buffer buf;
     // they feed the MFMAs one chunk later.
     uint32_t gv[16];
     auto gather = [&](int buf) {
         const lds8* q = CB[buf] + cread;
-        const uint32_t d0 = *(const lds32*)q, d1 = *(const lds32*)(q + 4), d2 = *(const lds32*)(q + 8);
+        uint32_t d[ND];
+#pragma unroll
+        for (int i = 0; i < ND; ++i) d[i] = *(const lds32*)(q + 4 * i);
         uint32_t a[16];
-        a[0] = (code_x256<0>(d0, d1, d2) & mask) | tabrow;
-        a[1] = (code_x256<1>(d0, d1, d2) & mask) | tabrow;
-        a[2] = (code_x256<2>(d0, d1, d2) & mask) | tabrow;
-        a[3] = (code_x256<3>(d0, d1, d2) & mask) | tabrow;
-        a[4] = (code_x256<4>(d0, d1, d2) & mask) | tabrow;
-        a[5] = (code_x256<5>(d0, d1, d2) & mask) | tabrow;
-        a[6] = (code_x256<6>(d0, d1, d2) & mask) | tabrow;
-        a[7] = (code_x256<7>(d0, d1, d2) & mask) | tabrow;
-        a[8] = (code_x256<8>(d0, d1, d2) & mask) | tabrow;
-        a[9] = (code_x256<9>(d0, d1, d2) & mask) | tabrow;
-        a[10] = (code_x256<10>(d0, d1, d2) & mask) | tabrow;
-        a[11] = (code_x256<11>(d0, d1, d2) & mask) | tabrow;
-        a[12] = (code_x256<12>(d0, d1, d2) & mask) | tabrow;
-        a[13] = (code_x256<13>(d0, d1, d2) & mask) | tabrow;
-        a[14] = (code_x256<14>(d0, d1, d2) & mask) | tabrow;
-        a[15] = (code_x256<15>(d0, d1, d2) & mask) | tabrow;
+        a[0] = (code_x256<BITS, 0>(d) & mask) | tabrow;
+        a[1] = (code_x256<BITS, 1>(d) & mask) | tabrow;
+        a[2] = (code_x256<BITS, 2>(d) & mask) | tabrow;
+        a[3] = (code_x256<BITS, 3>(d) & mask) | tabrow;
+        a[4] = (code_x256<BITS, 4>(d) & mask) | tabrow;
+        a[5] = (code_x256<BITS, 5>(d) & mask) | tabrow;
+        a[6] = (code_x256<BITS, 6>(d) & mask) | tabrow;
+        a[7] = (code_x256<BITS, 7>(d) & mask) | tabrow;
+        a[8] = (code_x256<BITS, 8>(d) & mask) | tabrow;
+        a[9] = (code_x256<BITS, 9>(d) & mask) | tabrow;
+        a[10] = (code_x256<BITS, 10>(d) & mask) | tabrow;
+        a[11] = (code_x256<BITS, 11>(d) & mask) | tabrow;
+        a[12] = (code_x256<BITS, 12>(d) & mask) | tabrow;
+        a[13] = (code_x256<BITS, 13>(d) & mask) | tabrow;
+        a[14] = (code_x256<BITS, 14>(d) & mask) | tabrow;
+        a[15] = (code_x256<BITS, 15>(d) & mask) | tabrow;
 #pragma unroll
         for (int e = 0; e < 16; ++e) gv[e] = *(lds16c*)(TAB + a[e]);
     };
@@ -216,9 +239,9 @@ __global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
     for (int c = 0; c < CSLOTS; ++c) load_codes(c, c);
     load_x(0, 0);
     {
-        lds8* dst = TAB + 256 * 8 * tpart + 4 * (16 * tcp + tr);
+        lds8* dst = TAB + 256 * EPT * tpart + 4 * (16 * tcp + tr);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *(lds16*)(dst + 256 * e) = (uint16_t)(tv[e >> 1] >> (16 * (e & 1)));
+        for (int e = 0; e < EPT; ++e) *(lds16*)(dst + 256 * e) = (uint16_t)(tv[e >> 1] >> (16 * (e & 1)));
     }
     store_codes(0, 0);
     store_codes(1, 1);
@@ -290,6 +313,22 @@ __global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(
     }
 }
 
+#define GEMV_MFMA_ARGS                                                                                     \
+    const uint8_t *__restrict__ packed, int64_t ld, const uint16_t *__restrict__ lut,                       \
+        const uint16_t *__restrict__ x, void *__restrict__ y, int y_f32, float *__restrict__ part, int rows, \
+        int cols, int batch, int nblocks, int cps
+
+template <int XROWS>
+__global__ __launch_bounds__(64 * NW) void lut6_gemv_mfma_kernel(GEMV_MFMA_ARGS) {
+    gemv_mfma_body<6, XROWS>(packed, ld, lut, x, y, y_f32, part, rows, cols, batch, nblocks, cps);
+}
+
+template <int XROWS>
+__global__ __launch_bounds__(64 * NW) void lut4_gemv_mfma_kernel(GEMV_MFMA_ARGS) {
+    gemv_mfma_body<4, XROWS>(packed, ld, lut, x, y, y_f32, part, rows, cols, batch, nblocks, cps);
+}
+#undef GEMV_MFMA_ARGS
+
 // y[b][r] = sum over splits s (in order) of part[s][b][r]
 __global__ __launch_bounds__(256) void lut6_gemv_split_sum(const float* __restrict__ part, void* __restrict__ y,
                                                            int y_f32, int64_t n, int nsplit) {
@@ -307,7 +346,7 @@ __global__ __launch_bounds__(256) void lut6_gemv_split_sum(const float* __restri
 
 // K split: enough workgroups to cover the chip several times over (two
 // resident per CU), with the chunks spread evenly over the splits.
-void lut6_mfma_split(const fqm_weights& w, int64_t* nblocks, int* nsplit, int* cps) {
+void lut_mfma_split(const fqm_weights& w, int64_t* nblocks, int* nsplit, int* cps) {
     const int64_t nb = (w.rows + RB - 1) / RB;
     const int nch = (int)(w.cols / CH);
     const int want = (int)std::min<int64_t>(nch, std::max<int64_t>(1, (SPLIT_TARGET + nb - 1) / nb));
@@ -317,34 +356,46 @@ void lut6_mfma_split(const fqm_weights& w, int64_t* nblocks, int* nsplit, int* c
     *nsplit = (nch + per - 1) / per;
 }
 
-bool lut6_gemv_mfma_supported(const fqm_weights& w, int batch) {
+bool lut_gemv_mfma_supported(const fqm_weights& w, int batch) {
     return batch >= 2 && batch <= 16 && w.cols > 0 && w.cols % CH == 0 && w.cols <= 0x7fffffff &&
            w.rows > 0 && w.rows <= 0x7fffffff;
 }
 
-size_t lut6_gemv_mfma_workspace(const fqm_weights& w, int batch) {
-    if (!lut6_gemv_mfma_supported(w, batch)) return 0;
+size_t lut_gemv_mfma_workspace(const fqm_weights& w, int batch) {
+    if (!lut_gemv_mfma_supported(w, batch)) return 0;
     int64_t nb;
     int ns, cps;
-    lut6_mfma_split(w, &nb, &ns, &cps);
+    lut_mfma_split(w, &nb, &ns, &cps);
     return ns > 1 ? (size_t)ns * (size_t)batch * (size_t)w.rows * sizeof(float) : 0;
 }
 
-hipError_t launch_lut6_gemv_mfma(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
-                                 float* ws, hipStream_t s) {
+hipError_t launch_lut_gemv_mfma(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
+                                float* ws, hipStream_t s) {
+    if (w.format != FQM_LUT6 && w.format != FQM_LUT4) return hipErrorInvalidValue;
     int64_t nb;
     int ns, cps;
-    lut6_mfma_split(w, &nb, &ns, &cps);
+    lut_mfma_split(w, &nb, &ns, &cps);
     if (nb * ns > 0x7fffffff) return hipErrorInvalidValue;
     float* part = ns > 1 ? ws : nullptr;
     if (ns > 1 && !ws) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(nb * ns)), block(64 * NW);
-    if (batch <= 8)
-        hipLaunchKernelGGL(lut6_gemv_mfma_kernel<8>, grid, block, 0, s, w.lut6.packed, w.lut6.ld, w.lut6.lut, x, y,
-                           y_f32, part, (int)w.rows, (int)w.cols, batch, (int)nb, cps);
+    const bool six = w.format == FQM_LUT6;
+    const uint8_t* packed = six ? w.lut6.packed : w.lut4.packed;
+    const int64_t ld = six ? w.lut6.ld : w.lut4.ld;
+    const uint16_t* lut = six ? w.lut6.lut : w.lut4.lut;
+    const int r = (int)w.rows, c = (int)w.cols, n = (int)nb;
+    if (six && batch <= 8)
+        hipLaunchKernelGGL(lut6_gemv_mfma_kernel<8>, grid, block, 0, s, packed, ld, lut, x, y, y_f32, part, r, c,
+                           batch, n, cps);
+    else if (six)
+        hipLaunchKernelGGL(lut6_gemv_mfma_kernel<16>, grid, block, 0, s, packed, ld, lut, x, y, y_f32, part, r, c,
+                           batch, n, cps);
+    else if (batch <= 8)
+        hipLaunchKernelGGL(lut4_gemv_mfma_kernel<8>, grid, block, 0, s, packed, ld, lut, x, y, y_f32, part, r, c,
+                           batch, n, cps);
     else
-        hipLaunchKernelGGL(lut6_gemv_mfma_kernel<16>, grid, block, 0, s, w.lut6.packed, w.lut6.ld, w.lut6.lut, x, y,
-                           y_f32, part, (int)w.rows, (int)w.cols, batch, (int)nb, cps);
+        hipLaunchKernelGGL(lut4_gemv_mfma_kernel<16>, grid, block, 0, s, packed, ld, lut, x, y, y_f32, part, r, c,
+                           batch, n, cps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     const int64_t total = (int64_t)batch * w.rows;

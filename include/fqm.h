@@ -194,10 +194,11 @@ fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
  * MDBF 128*P*S*(roundup(m,256) + roundup(r,256)) with S = ceil(batch / bs),
  * bs = 1 if 3*l >= 64 else floor(64 / (3*l)) (the dense operands of both
  * passes: each fp32 value as three bf16 parts, 64 columns per batch slice of
- * bs rows); LUT6 with batch >= 2 and
- * cols a multiple of 512 splits K over workgroups unless rows > 16368, and
- * then needs S*batch*rows*4 (S fp32 partial sums per output, S <= cols / 512,
- * a function of rows and cols only), else 0; 0 for FABQ.
+ * bs rows); LUT6 and LUT4 with batch >= 2 and
+ * cols a multiple of 512 split K over workgroups unless rows > 16368, and
+ * then need S*batch*rows*4 (S fp32 partial sums per output, S <= cols / 512,
+ * a function of rows and cols only, the same for both formats), else 0;
+ * 0 for FABQ.
  * Returns 0 for an invalid descriptor. */
 size_t fqm_workspace_size(const fqm_weights* w, int32_t batch);
 

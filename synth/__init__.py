@@ -325,8 +325,8 @@ CONFIGS = {
     "tiny_lut6": dict(rows=256, cols=512, seed=1, batches=(1,), y="f32"),
     "lut6_up": dict(rows=17408, cols=5120, seed=2, batches=(1, 8), y="bf16"),
     "lut6_down": dict(rows=5120, cols=17408, seed=3, batches=(1, 8), y="bf16"),
-    "lut4_up": dict(rows=17408, cols=5120, seed=7, batches=(1,), y="bf16"),
-    "lut4_down": dict(rows=5120, cols=17408, seed=8, batches=(1,), y="bf16"),
+    "lut4_up": dict(rows=17408, cols=5120, seed=7, batches=(1, 8), y="bf16"),
+    "lut4_down": dict(rows=5120, cols=17408, seed=8, batches=(1, 8), y="bf16"),
     "prefill": dict(M=2048, weights="lut6_up", seed=4),
     "fabq": dict(rows=5120, cols=5120, seed=5, batches=(1, 8)),
     "mdbf": dict(n=4096, m=4096, r=2000, l=2, P=1, seed=6, batches=(1, 16)),

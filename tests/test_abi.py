@@ -105,6 +105,22 @@ def test_lut4_argument_errors(lib):
     assert lib.fqm_gemm_workspace_size(ctypes.byref(lut4()), 8) == 0
 
 
+def test_lut4_batch_workspace_follows_the_lut6_rule(lib):
+    """Batches 2..16 of both LUT formats share the matrix-core kernel's K
+    split, so the workspace depends on the shape and batch only."""
+    for rows, cols, batch in ((5120, 17408, 8), (5120, 17408, 16), (17408, 5120, 8), (300, 4096, 2),
+                              (5120, 17408, 1), (64, 1088, 4)):
+        a = lib.fqm_workspace_size(ctypes.byref(lut4(rows, cols, ld=cols // 2)), batch)
+        b = lib.fqm_workspace_size(ctypes.byref(lut6(rows, cols, ld=cols * 3 // 4)), batch)
+        assert a == b, (rows, cols, batch)
+    need = lib.fqm_workspace_size(ctypes.byref(lut4(5120, 17408, ld=8704)), 8)
+    assert need > 0
+    w = lut4(5120, 17408, ld=8704)
+    assert gemv(lib, w, batch=8) == E["WORKSPACE"]
+    assert gemv(lib, w, batch=8, ws=FAKE, wsb=need - 16) == E["WORKSPACE"]
+    assert gemv(lib, w, batch=8, ws=FAKE + 8, wsb=need + 16) == E["ALIGN"]
+
+
 def test_descriptor_layout_matches_the_header():
     """The LUT4 member sits after the others, so their offsets are unchanged."""
     W = fqm._Weights

@@ -66,12 +66,34 @@ def test_gemv_generic_widths_and_batches(batch):
         assert_close(to_f64(y), oracle.lut4.gemv(packed, inp.lut, x, cols), "f32", f"{rows}x{cols} b{batch}")
 
 
-def test_gemv_b8_full_layer():
-    inp, packed = case(17408, 5120, 7)
-    w = weights(17408, 5120, 7)
-    x = synth.activations(8, 5120, 11)
+@pytest.mark.parametrize("batch", [2, 3, 8, 9, 16])
+@pytest.mark.parametrize("rows,cols,seed", [(70, 1536, 13), (301, 4096, 14), (16, 512, 15)])
+def test_gemv_matrix_cores(batch, rows, cols, seed):
+    """cols a multiple of 512, batch 2..16: the matrix-core kernel (ragged
+    16-row blocks, batch rows past the batch in an 8- or 16-row x block)."""
+    inp, packed = case(rows, cols, seed)
+    w = weights(rows, cols, seed)
+    x = synth.activations(batch, cols, seed)
+    buf, y = guarded((batch, rows), torch.float32)
+    fqm.gemv(w, bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.lut4.gemv(packed, inp.lut, x, cols), "f32", f"{rows}x{cols} b{batch}")
+
+
+@pytest.mark.parametrize("rows,cols,seed,batch", [(17408, 5120, 7, 8), (5120, 17408, 8, 8), (5120, 17408, 8, 16)])
+def test_gemv_matrix_cores_full_layers(rows, cols, seed, batch):
+    """The full layers; the down layer splits K over workgroups (fp32
+    partials in the workspace, added in split order)."""
+    inp, packed = case(rows, cols, seed)
+    w = weights(rows, cols, seed)
+    assert (fqm.workspace_size(w, batch) > 0) == (rows == 5120)
+    x = synth.activations(batch, cols, 11)
     y = fqm.gemv(w, bf16_dev(x))
-    assert_close(to_f64(y), oracle.lut4.gemv(packed, inp.lut, x, 5120), "bf16", "b8")
+    ref = oracle.lut4.gemv(packed, inp.lut, x, cols)
+    assert_close(to_f64(y), ref, "bf16", f"b{batch}")
+    y2 = fqm.gemv(w, bf16_dev(x))
+    assert torch.equal(y, y2)  # fixed-order sums: bitwise repeatable
 
 
 def test_gemv_mirror_negates():
