@@ -8,6 +8,7 @@ synthetic input already resident in HBM:
   prefill                    LUT6 GEMM, X 2048x5120 times the up weights
   lut4_up_b1, lut4_down_b1   LUT4 GEMV, batch 1, the same two shapes
   lut4_up_b8, lut4_down_b8   LUT4 GEMV, batch 8
+  lut4_prefill               LUT4 GEMM, X 2048x5120 times the LUT4 up weights
   fabq_b1, fabq_b8           FABQ-RC-style GEMV, 5120x5120, the layer's drawn blocksize
   mdbf_b1, mdbf_b16          MDBF GEMV, n = m = 4096, r = 2000, l = 2, P = 1
 
@@ -149,15 +150,17 @@ def main():
             bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * K,
             bound="mfma", kernel="lut6_gemm (with its K-split last round and reduction)")
 
-    # ---- LUT4 weights (up, down shapes), batch 1 and 8 ---------------------------
+    # ---- LUT4 weights (up, down shapes), batch 1 and 8, prefill on the up layer --
+    lut4 = {}
     for name in ("up", "down"):
         cfg = C[f"lut4_{name}"]
         keys = [f"lut4_{name}_b{b}" for b in cfg["batches"]]
-        if not wanted(*keys):
+        if not wanted(*keys, "lut4_prefill" if name == "up" else "-"):
             continue
         inp = synth.lut4_input(cfg["rows"], cfg["cols"], cfg["seed"])
         q0 = fqm.Lut4Weights.from_codes(inp.codes, inp.lut, device=dev)
         qcopies = [q0] + [q0.clone() for _ in range(n_copies(q0) - 1)]
+        lut4[name] = qcopies
         for b, key in zip(cfg["batches"], keys):
             if not wanted(key):
                 continue
@@ -172,6 +175,18 @@ def main():
                 bytes=q0.nbytes() + x.numel() * 2 + y.numel() * 2,
                 flops=2 * b * cfg["rows"] * cfg["cols"], bound="hbm",
                 kernel="lut4_gemv_cells, batch 1" if b == 1 else f"lut4_gemv_mfma_kernel, batch {b}")
+    if wanted("lut4_prefill"):
+        M = C["prefill"]["M"]
+        ws = lut4["up"]
+        X = bf16(synth.activations(M, C["lut4_up"]["cols"], C["prefill"]["seed"]))
+        Y = torch.empty((M, C["lut4_up"]["rows"]), dtype=torch.bfloat16, device=dev)
+        Nn, K = C["lut4_up"]["rows"], C["lut4_up"]["cols"]
+        gws_bytes = fqm.gemm_workspace_size(ws[0], M)
+        gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev) if gws_bytes else None
+        rows["lut4_prefill"] = dict(
+            fn=lambda s, ws=ws, X=X, Y=Y, gws=gws: fqm.gemm(ws[(s + 1) % len(ws)], X, Y=Y, workspace=gws),
+            bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * K,
+            bound="mfma", kernel="lut4_gemm (with its K-split last round and reduction)")
 
     # ---- FABQ (5120^2, the layer's drawn blocksize) ------------------------------
     fabq_bs = None

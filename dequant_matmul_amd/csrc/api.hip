@@ -199,21 +199,24 @@ fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_
 // matrix cores would mostly multiply padding (measured on the 17408 x 5120
 // layer: 14-31 us through the GEMV path against 68-71 us as a GEMM).
 static bool gemm_as_gemv(const fqm_weights& w, int64_t M) {
-    return M >= 1 && M <= 16 && fqm::lut6_gemv_fast_path(w, (int)M);
+    if (M < 1 || M > 16) return false;
+    return w.format == FQM_LUT4 ? fqm::lut4_gemv_fast_path(w, (int)M) : fqm::lut6_gemv_fast_path(w, (int)M);
 }
 
+static bool lut_format(const fqm_weights& w) { return w.format == FQM_LUT6 || w.format == FQM_LUT4; }
+
 size_t fqm_gemm_workspace_size(const fqm_weights* w, int64_t M) {
-    if (check_weights(w) != FQM_OK || w->format != FQM_LUT6 || M <= 0 || w->rows == 0) return 0;
+    if (check_weights(w) != FQM_OK || !lut_format(*w) || M <= 0 || w->rows == 0) return 0;
     if (w->cols % 64 || M * w->cols * 2 > INT32_MAX) return 0;
     if (gemm_as_gemv(*w, M)) return fqm::lut_gemv_mfma_workspace(*w, (int)M);
-    return fqm::lut6_gemm_workspace(*w, M);
+    return fqm::lut_gemm_workspace(*w, M);
 }
 
 fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_t M, void* workspace,
                     size_t ws_bytes, void* stream) {
     const fqm_status st = check_weights(w);
     if (st != FQM_OK) return st;
-    if (w->format != FQM_LUT6) return FQM_E_UNSUPPORTED;
+    if (!lut_format(*w)) return FQM_E_UNSUPPORTED;
     if (M < 0) return FQM_E_SHAPE;
     if (M > (int64_t)65535 * 128) return FQM_E_SHAPE;
     if (M == 0 || w->rows == 0) return FQM_OK;
@@ -223,9 +226,11 @@ fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_
     const size_t need = fqm_gemm_workspace_size(w, M);
     if (need && (!workspace || ws_bytes < need)) return FQM_E_WORKSPACE;
     if (need && !aligned16(workspace)) return FQM_E_ALIGN;
+    float* gws = static_cast<float*>(workspace);
     if (gemm_as_gemv(*w, M))  // Y[M][rows] bf16 is the GEMV's y[batch][rows]
-        return hip_status(launch_lut6_gemv(*w, X, Y, 0, (int)M, static_cast<float*>(workspace), as_stream(stream)));
-    return hip_status(launch_lut6_gemm(*w, X, Y, M, workspace, ws_bytes, as_stream(stream)));
+        return hip_status(w->format == FQM_LUT4 ? launch_lut4_gemv(*w, X, Y, 0, (int)M, gws, as_stream(stream))
+                                                : launch_lut6_gemv(*w, X, Y, 0, (int)M, gws, as_stream(stream)));
+    return hip_status(launch_lut_gemm(*w, X, Y, M, workspace, ws_bytes, as_stream(stream)));
 }
 
 }  // extern "C"

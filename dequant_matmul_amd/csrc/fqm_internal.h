@@ -79,6 +79,9 @@ hipError_t launch_dequant_lut6(const fqm_weights& w, uint16_t* W, hipStream_t s)
 hipError_t launch_dequant_lut4(const fqm_weights& w, uint16_t* W, hipStream_t s);
 hipError_t launch_lut4_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
                             float* ws, hipStream_t s);
+// true when launch_lut4_gemv takes a tuned kernel for this shape and batch
+// (the cell kernel at batch 1, the matrix-core kernel at 2..16)
+bool lut4_gemv_fast_path(const fqm_weights& w, int batch);
 hipError_t launch_dequant_fabq(const fqm_weights& w, uint16_t* W, hipStream_t s);
 
 hipError_t launch_lut6_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
@@ -94,9 +97,11 @@ bool lut6_gemv_fast_path(const fqm_weights& w, int batch);
 size_t lut_gemv_mfma_workspace(const fqm_weights& w, int batch);
 hipError_t launch_lut_gemv_mfma(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
                                 float* ws, hipStream_t s);
-size_t lut6_gemm_workspace(const fqm_weights& w, int64_t M);
-hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M, void* ws,
-                            size_t ws_bytes, hipStream_t s);
+// Prefill GEMM of either LUT format (6- or 4-bit codes); the tile plan and
+// its workspace depend on the shape, M and the device only.
+size_t lut_gemm_workspace(const fqm_weights& w, int64_t M);
+hipError_t launch_lut_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M, void* ws,
+                           size_t ws_bytes, hipStream_t s);
 hipError_t launch_fabq_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
                             int batch, hipStream_t s);
 // MDBF: workspace holds the bf16 hi/lo dense operands of both passes.

@@ -232,10 +232,18 @@ hipError_t launch_batch(const fqm_weights& w, const uint16_t* x, void* y, int y_
 
 }  // namespace
 
+static bool cells_supported(const fqm_weights& w) {
+    return w.cols > 0 && (w.cols & 1023) == 0 && (w.cols >> 10) <= kMaxCells;
+}
+
+bool lut4_gemv_fast_path(const fqm_weights& w, int batch) {
+    return batch == 1 ? cells_supported(w) : lut_gemv_mfma_supported(w, batch);
+}
+
 hipError_t launch_lut4_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
                             float* ws, hipStream_t s) {
     if (w.rows > 0x7fffffff) return hipErrorInvalidValue;
-    if (batch == 1 && w.cols > 0 && (w.cols & 1023) == 0 && (w.cols >> 10) <= kMaxCells)
+    if (batch == 1 && cells_supported(w))
         return launch_cells<1>(w, x, y, y_f32, s);
     if (lut_gemv_mfma_supported(w, batch)) return launch_lut_gemv_mfma(w, x, y, y_f32, batch, ws, s);
     return launch_batch<1>(w, x, y, y_f32, batch, s);

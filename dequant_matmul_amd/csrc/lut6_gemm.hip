@@ -1,8 +1,12 @@
-// Per-row LUT 6-bit GEMM (prefill): Y[m][n] = sum_k X[m][k] * lut[n][code[n][k]].
+// Per-row LUT GEMM (prefill): Y[m][n] = sum_k X[m][k] * lut[n][code[n][k]],
+// 6-bit codes (64-entry tables) or 4-bit codes (16-entry tables).
 //
 // Source: "Qwen3.8-27B - BenQ 6-bit", "What BenQ stores": decode is the
 // row-wise gather of codes into the row's table, fused into the matrix
-// product so the decoded matrix is never written out.  Each workgroup owns a
+// product so the decoded matrix is never written out ("Why equal-width
+// shells" places 8 tiers in 4 bits, read the same way).  The text below
+// gives the 6-bit sizes; 4-bit codes take 16 bytes per lane per step and
+// 2 KB table planes.  Each workgroup owns a
 // BM x BN tile of Y and contracts it on the bf16 matrix cores
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulate); the decoded weights are exact
 // (the table entries are bf16).
@@ -66,7 +70,6 @@ typedef __attribute__((address_space(3))) void lvoid;
 constexpr int BM_BIG = 256, BM_SMALL = 64;
 constexpr int BN = 256, BK = 64;
 constexpr int NWAVE = 8;                       // 8 waves along N, BM x 32 outputs each
-constexpr int TAB_BYTES = BN * 128;            // BN row tables, bank-sliced
 constexpr int CD = 3;                          // codes are requested CD steps ahead
 static_assert(BN == 32 * NWAVE && CD == 3, "tile constants (the loop is unrolled by CD + 1)");
 template <int BM>
@@ -77,16 +80,28 @@ struct TileShape {
     static_assert(XDMA >= 1 && BM % 64 == 0, "every wave loads whole kilobytes of the X tile");
 };
 
+// Per code width: table entries, a table plane (64 rows' tables, bank-sliced),
+// the code bytes a lane reads per K step (32 codes) and a row's bytes per step.
+template <int BITS>
+struct GemmFmt {
+    static constexpr int ENTRIES = 1 << BITS;
+    static constexpr int PLANE = 128 * ENTRIES;  // 8 KB (6-bit), 2 KB (4-bit)
+    static constexpr int TAB_BYTES = (BN / 64) * PLANE;
+    static constexpr int ND = BITS;              // dwords of code per lane per step
+    static constexpr int STEP_BYTES = 8 * BITS;  // a row's 64 codes
+    static constexpr int CODE_LOADS = ND == 6 ? 2 : 1;  // global loads per lane per step (16 + 8 or 16 bytes)
+};
+
 template <int BUF>
 using Buf = std::integral_constant<int, BUF>;
 
-// Table offset of code C (0..31) of a lane's 24-byte code run d[0..5]: the
-// code's 6 bits moved to bits 7..12 and OR-ed into the lane's row offset.
-template <int C>
-__device__ __forceinline__ uint32_t code_addr(const uint32_t (&d)[6], uint32_t mask, uint32_t base) {
-    constexpr int bit = 6 * C, w = bit >> 5, o = bit & 31;
+// Table offset of code C (0..31) of a lane's code run d[0..ND): the code's
+// bits moved to bits 7.. and OR-ed into the lane's row offset.
+template <int BITS, int C, int ND>
+__device__ __forceinline__ uint32_t code_addr(const uint32_t (&d)[ND], uint32_t mask, uint32_t base) {
+    constexpr int bit = BITS * C, w = bit >> 5, o = bit & 31;
     uint32_t v;
-    if constexpr (o + 6 <= 32) {
+    if constexpr (o + BITS <= 32) {
         if constexpr (o >= 7) v = d[w] >> (o - 7);
         else v = d[w] << (7 - o);
     } else {
@@ -96,16 +111,16 @@ __device__ __forceinline__ uint32_t code_addr(const uint32_t (&d)[6], uint32_t m
 }
 
 // The 8 gather addresses of slice Q (codes 8 Q .. 8 Q + 7).
-template <int Q>
-__device__ __forceinline__ void slice_addrs(const uint32_t (&d)[6], uint32_t mask, uint32_t base, uint32_t (&ad)[8]) {
-    ad[0] = code_addr<8 * Q + 0>(d, mask, base);
-    ad[1] = code_addr<8 * Q + 1>(d, mask, base);
-    ad[2] = code_addr<8 * Q + 2>(d, mask, base);
-    ad[3] = code_addr<8 * Q + 3>(d, mask, base);
-    ad[4] = code_addr<8 * Q + 4>(d, mask, base);
-    ad[5] = code_addr<8 * Q + 5>(d, mask, base);
-    ad[6] = code_addr<8 * Q + 6>(d, mask, base);
-    ad[7] = code_addr<8 * Q + 7>(d, mask, base);
+template <int BITS, int Q, int ND>
+__device__ __forceinline__ void slice_addrs(const uint32_t (&d)[ND], uint32_t mask, uint32_t base, uint32_t (&ad)[8]) {
+    ad[0] = code_addr<BITS, 8 * Q + 0>(d, mask, base);
+    ad[1] = code_addr<BITS, 8 * Q + 1>(d, mask, base);
+    ad[2] = code_addr<BITS, 8 * Q + 2>(d, mask, base);
+    ad[3] = code_addr<BITS, 8 * Q + 3>(d, mask, base);
+    ad[4] = code_addr<BITS, 8 * Q + 4>(d, mask, base);
+    ad[5] = code_addr<BITS, 8 * Q + 5>(d, mask, base);
+    ad[6] = code_addr<BITS, 8 * Q + 6>(d, mask, base);
+    ad[7] = code_addr<BITS, 8 * Q + 7>(d, mask, base);
 }
 
 template <int Q>
@@ -129,7 +144,7 @@ __device__ __forceinline__ void barrier_after_loads() {
 // tt = b / ksplit, over K steps [t0, t1) of its split b % ksplit.  PARTIAL:
 // the fp32 tile (all BM x BN values) goes to part[b]; otherwise the bf16
 // outputs inside M x N go to Y.
-template <bool PARTIAL, int BM>
+template <int BITS, bool PARTIAL, int BM>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
                                                                const uint8_t* __restrict__ packed,
                                                                int64_t ld,
@@ -138,6 +153,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
                                                                int M, int N, int K, int mtiles, int nt0,
                                                                int ksplit) {
     constexpr int MB = TileShape<BM>::MB, XT_BYTES = TileShape<BM>::XT_BYTES, XDMA = TileShape<BM>::XDMA;
+    using F = GemmFmt<BITS>;
+    constexpr int TAB_BYTES = F::TAB_BYTES, PLANE = F::PLANE, ND = F::ND, EPT = F::ENTRIES / 8;
     // Separate LDS objects: the X tiles are written by direct global -> LDS
     // loads, and distinct objects let the compiler see that the table
     // gathers do not wait for those loads.
@@ -158,16 +175,24 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
 
     // ---- row tables, bank-sliced (resident for the whole K loop) ------------------
     for (int i = tid; i < BN * 8; i += 64 * NWAVE) {
-        const int r = i >> 3, part = i & 7;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (n0 + r < N) v = *reinterpret_cast<const u32x4*>(lut + (int64_t)(n0 + r) * 64 + part * 8);
-        lds8* dst = TAB + 8192 * (r >> 6) + 4 * (r & 31) + 2 * ((r >> 5) & 1) + 128 * 8 * part;
+        const int r = i >> 3, part = i & 7;  // entries EPT part .. + EPT - 1 of tile row r
+        uint32_t v[4] = {0u, 0u, 0u, 0u};
+        if (n0 + r < N) {
+            const uint16_t* src = lut + (int64_t)(n0 + r) * F::ENTRIES + part * EPT;
+            if constexpr (EPT == 8) {
+                const u32x4 q = *reinterpret_cast<const u32x4*>(src);
+                v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+            } else {
+                v[0] = *reinterpret_cast<const uint32_t*>(src);
+            }
+        }
+        lds8* dst = TAB + PLANE * (r >> 6) + 4 * (r & 31) + 2 * ((r >> 5) & 1) + 128 * EPT * part;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *(lds16*)(dst + 128 * e) = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        for (int e = 0; e < EPT; ++e) *(lds16*)(dst + 128 * e) = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
     }
-    // this lane's row 32 wn + j: plane wn / 2, half wn % 2 (bits 1..6 and 13 only)
-    const uint32_t tbase = 8192u * (wn >> 1) + 4u * j + 2u * (wn & 1);
-    uint32_t cmask = 0x1F80u;
+    // this lane's row 32 wn + j: plane wn / 2, half wn % 2 (bits below the code's and above them only)
+    const uint32_t tbase = (uint32_t)PLANE * (wn >> 1) + 4u * j + 2u * (wn & 1);
+    uint32_t cmask = (uint32_t)(F::ENTRIES - 1) << 7;
     asm volatile("" : "+v"(cmask));  // in a VGPR: (v & mask) | base is one v_and_or_b32
 
     // ---- X: direct global -> LDS, 1 KB (8 rows) per wave instruction -----------
@@ -197,14 +222,16 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
     };
 
     // ---- codes: 24 bytes of row 32 wn + j per lane per step, CD steps ahead -------
-    const uint8_t* csrc = packed + (int64_t)min(n0 + 32 * wn + j, N - 1) * ld + 24 * g;
-    uint32_t cw[CD + 1][6];
+    const uint8_t* csrc = packed + (int64_t)min(n0 + 32 * wn + j, N - 1) * ld + 4 * ND * g;
+    uint32_t cw[CD + 1][ND];
     auto load_codes = [&](int slot, int t) {
-        const uint8_t* p = csrc + 48 * t;
+        const uint8_t* p = csrc + F::STEP_BYTES * t;
         const u32x4 lo = *reinterpret_cast<const u32x4_a8*>(p);
-        const u32x2 hi = *reinterpret_cast<const u32x2_a8*>(p + 16);
         cw[slot][0] = lo[0]; cw[slot][1] = lo[1]; cw[slot][2] = lo[2]; cw[slot][3] = lo[3];
-        cw[slot][4] = hi[0]; cw[slot][5] = hi[1];
+        if constexpr (ND == 6) {
+            const u32x2 hi = *reinterpret_cast<const u32x2_a8*>(p + 16);
+            cw[slot][4] = hi[0]; cw[slot][5] = hi[1];
+        }
     };
 
     // ---- X operand offsets ------------------------------------------------------
@@ -234,7 +261,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
     // Step t0 + t (X buffer B = t % 2, code slot S = t % (CD + 1)): request X(t+1),
     // then the codes of step t + CD, then the four slices of step t (operand
     // reads, gathers, MFMAs).  Before the closing barrier publishes X(t+1) the
-    // wave waits until at most the two code loads of this step are in flight
+    // wave waits until at most the code loads of this step (two 6-bit, one
+    // 4-bit) are in flight
     // (memory loads complete in issue order, so X(t+1) and every older code
     // load have landed); the last steps wait for everything.  Past the end the
     // indices are clamped (the extra work lands in buffers that are never read).
@@ -251,7 +279,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
 #pragma unroll
             for (int i = 0; i < MB; ++i) a[i] = __builtin_bit_cast(bf16x8, *(lds128c*)(XS[B] + aoff[q] + 4096 * i));
             uint32_t ad[8];
-            slice_addrs<q>(cw[S], cmask, tbase, ad);
+            slice_addrs<BITS, q>(cw[S], cmask, tbase, ad);
             uint32_t wv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) wv[e] = *(lds16c*)(TAB + ad[e]);
@@ -269,7 +297,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
         if constexpr (LAST)
             barrier_after_loads<0>();
         else
-            barrier_after_loads<2>();  // this step's two code loads may stay in flight
+            barrier_after_loads<F::CODE_LOADS>();  // only this step's code loads may stay in flight
     };
     // The four steps of an iteration run unconditionally (one basic block), so
     // each step's loads stay where the scheduling barriers put them; the
@@ -312,14 +340,23 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
         int K, int mtiles, int nt0, int ksplit
 template <bool PARTIAL>
 __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(FQM_GEMM_ARGS) {
-    gemm_tile<PARTIAL, BM_BIG>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
+    gemm_tile<6, PARTIAL, BM_BIG>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
 }
 // 64-row tiles: 48 KB of LDS and at most 96 VGPRs (five waves per SIMD), so
 // two workgroups share a CU
 template <bool PARTIAL>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(5))) void lut6_gemm_small_kernel(
     FQM_GEMM_ARGS) {
-    gemm_tile<PARTIAL, BM_SMALL>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
+    gemm_tile<6, PARTIAL, BM_SMALL>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
+}
+template <bool PARTIAL>
+__global__ __launch_bounds__(64 * NWAVE) void lut4_gemm_kernel(FQM_GEMM_ARGS) {
+    gemm_tile<4, PARTIAL, BM_BIG>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
+}
+template <bool PARTIAL>
+__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(5))) void lut4_gemm_small_kernel(
+    FQM_GEMM_ARGS) {
+    gemm_tile<4, PARTIAL, BM_SMALL>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
 }
 #undef FQM_GEMM_ARGS
 
@@ -393,25 +430,34 @@ GemmPlan gemm_plan(int64_t rows, int64_t cols, int64_t M, int cus) {
     return p;
 }
 
-template <int BM>
+template <int BITS, int BM>
 hipError_t launch_plan(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M, void* ws,
                        const GemmPlan& p, hipStream_t s) {
     hipError_t e;
     const int64_t main_tiles = (int64_t)p.nt_main * p.mtiles;
     auto kernel = [](bool partial) {
-        if constexpr (BM == BM_SMALL) return partial ? lut6_gemm_small_kernel<true> : lut6_gemm_small_kernel<false>;
-        else return partial ? lut6_gemm_kernel<true> : lut6_gemm_kernel<false>;
+        if constexpr (BITS == 4 && BM == BM_SMALL)
+            return partial ? lut4_gemm_small_kernel<true> : lut4_gemm_small_kernel<false>;
+        else if constexpr (BITS == 4)
+            return partial ? lut4_gemm_kernel<true> : lut4_gemm_kernel<false>;
+        else if constexpr (BM == BM_SMALL)
+            return partial ? lut6_gemm_small_kernel<true> : lut6_gemm_small_kernel<false>;
+        else
+            return partial ? lut6_gemm_kernel<true> : lut6_gemm_kernel<false>;
     };
+    const uint8_t* packed = BITS == 4 ? w.lut4.packed : w.lut6.packed;
+    const int64_t ld = BITS == 4 ? w.lut4.ld : w.lut6.ld;
+    const uint16_t* lut = BITS == 4 ? w.lut4.lut : w.lut6.lut;
     if (main_tiles > 0) {
         hipLaunchKernelGGL(kernel(false), dim3((unsigned)main_tiles), dim3(64 * NWAVE), 0, s, X,
-                           w.lut6.packed, w.lut6.ld, w.lut6.lut, Y, nullptr, (int)M, (int)w.rows, (int)w.cols,
+                           packed, ld, lut, Y, nullptr, (int)M, (int)w.rows, (int)w.cols,
                            p.mtiles, 0, 1);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (p.tail > 0) {
         float* part = static_cast<float*>(ws);
         hipLaunchKernelGGL(kernel(true), dim3((unsigned)(p.tail * p.ksplit)), dim3(64 * NWAVE), 0, s,
-                           X, w.lut6.packed, w.lut6.ld, w.lut6.lut, Y, part, (int)M, (int)w.rows, (int)w.cols,
+                           X, packed, ld, lut, Y, part, (int)M, (int)w.rows, (int)w.cols,
                            p.mtiles, p.nt_main, p.ksplit);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int64_t groups = p.tail * BM * (BN / 4);
@@ -431,15 +477,15 @@ hipError_t device_cus(int* cus) {
 
 }  // namespace
 
-size_t lut6_gemm_workspace(const fqm_weights& w, int64_t M) {
+size_t lut_gemm_workspace(const fqm_weights& w, int64_t M) {
     int cus = 0;
     if (M <= 0 || device_cus(&cus) != hipSuccess) return 0;
     return gemm_plan(w.rows, w.cols, M, cus).ws_bytes;
 }
 
-hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M, void* ws,
-                            size_t ws_bytes, hipStream_t s) {
-    if (w.cols % BK || w.rows > 0x7fffffff || M > 0x7fffffff || w.cols > 0x7fffffff ||
+hipError_t launch_lut_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M, void* ws,
+                           size_t ws_bytes, hipStream_t s) {
+    if ((w.format != FQM_LUT6 && w.format != FQM_LUT4) || w.cols % BK || w.rows > 0x7fffffff || M > 0x7fffffff || w.cols > 0x7fffffff ||
         M * w.cols * 2 > 0x7fffffff)
         return hipErrorInvalidValue;
     int cus = 0;
@@ -448,7 +494,11 @@ hipError_t launch_lut6_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y
     const GemmPlan p = gemm_plan(w.rows, w.cols, M, cus);
     if ((int64_t)p.ntiles * p.mtiles > 0x7fffffff) return hipErrorInvalidValue;
     if (p.ws_bytes > ws_bytes || (p.ws_bytes && !ws)) return hipErrorInvalidValue;
-    return p.bm == BM_SMALL ? launch_plan<BM_SMALL>(w, X, Y, M, ws, p, s) : launch_plan<BM_BIG>(w, X, Y, M, ws, p, s);
+    if (w.format == FQM_LUT4)
+        return p.bm == BM_SMALL ? launch_plan<4, BM_SMALL>(w, X, Y, M, ws, p, s)
+                                : launch_plan<4, BM_BIG>(w, X, Y, M, ws, p, s);
+    return p.bm == BM_SMALL ? launch_plan<6, BM_SMALL>(w, X, Y, M, ws, p, s)
+                            : launch_plan<6, BM_BIG>(w, X, Y, M, ws, p, s);
 }
 
 }  // namespace fqm

@@ -213,18 +213,18 @@ size_t fqm_workspace_size(const fqm_weights* w, int32_t batch);
 fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
                     int32_t batch, void* workspace, size_t ws_bytes, void* stream);
 
-/* Bytes of device workspace fqm_gemm needs for this LUT6 descriptor and M on
+/* Bytes of device workspace fqm_gemm needs for this LUT6 or LUT4 descriptor and M on
  * the current device: for M <= 16 on a shape the GEMV kernels cover (batch 1:
  * cols = 1024 c, 1 <= c <= 31; batch 2..16: cols a multiple of 512) it is
  * fqm_workspace_size(w, M), since fqm_gemm then runs those kernels; otherwise
  * 256 * 256 * 4 bytes per K part of each 256 x 256 output tile of a last,
  * partial round of tiles (one round = one tile per compute unit), when such
  * tiles are split along K, and 0 when nothing is split.  A function of rows,
- * cols, M and the device's compute-unit count.  Returns 0 for an invalid or
- * non-LUT6 descriptor. */
+ * cols, M and the device's compute-unit count (the same for both formats).
+ * Returns 0 for an invalid, FABQ or MDBF descriptor. */
 size_t fqm_gemm_workspace_size(const fqm_weights* w, int64_t M);
 
-/* Y = X W^T for a LUT6 descriptor (prefill): X [M][cols] bf16, Y [M][rows]
+/* Y = X W^T for a LUT6 or LUT4 descriptor (prefill): X [M][cols] bf16, Y [M][rows]
  * bf16, both row-major; cols a multiple of 64 and M * cols * 2 < 2^31
  * (FQM_E_SHAPE otherwise).  Each weight is gathered from its row's table
  * (exact: the levels are bf16) straight into the operands of the bf16 matrix
@@ -235,7 +235,7 @@ size_t fqm_gemm_workspace_size(const fqm_weights* w, int64_t M);
  * Up to 16 rows of X on a shape the GEMV kernels cover run those kernels (the
  * same product as fqm_gemv with batch = M and bf16 output; the 256-row tiles
  * would mostly multiply padding there).
- * LUT4 / FABQ / MDBF descriptors return FQM_E_UNSUPPORTED. */
+ * FABQ / MDBF descriptors return FQM_E_UNSUPPORTED. */
 fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_t M,
                     void* workspace, size_t ws_bytes, void* stream);
 

@@ -100,9 +100,15 @@ def test_lut4_argument_errors(lib):
     assert gemv(lib, lut4(lut=None)) == E["NULL"]
     assert gemv(lib, lut4(), batch=17) == E["SHAPE"]
     assert gemv(lib, lut4(rows=0, packed=None, lut=None)) == E["OK"]
-    assert gemm(lib, lut4()) == E["UNSUPPORTED"]              # no LUT4 GEMM
+    assert gemm(lib, lut4(), M=-1) == E["SHAPE"]
+    assert gemm(lib, lut4(cols=96)) == E["SHAPE"]
+    assert gemm(lib, lut4(), X=None) == E["NULL"]
+    assert gemm(lib, lut4(), Y=FAKE + 2) == E["ALIGN"]
+    assert gemm(lib, lut4(rows=0, packed=None, lut=None)) == E["OK"]
     assert lib.fqm_workspace_size(ctypes.byref(lut4()), 8) == 0
-    assert lib.fqm_gemm_workspace_size(ctypes.byref(lut4()), 8) == 0
+    for M in (1, 8, 17, 300):  # the GEMM's tile plan does not depend on the code width
+        assert (lib.fqm_gemm_workspace_size(ctypes.byref(lut4(5120, 17408, ld=8704)), M)
+                == lib.fqm_gemm_workspace_size(ctypes.byref(lut6(5120, 17408, ld=13056)), M))
 
 
 def test_lut4_batch_workspace_follows_the_lut6_rule(lib):

@@ -106,3 +106,40 @@ def test_gemv_mirror_negates():
     y = to_f64(fqm.gemv(w, x, out_dtype=torch.float32))
     ym = to_f64(fqm.gemv(wm, x, out_dtype=torch.float32))
     assert np.allclose(ym, -y, rtol=1e-5, atol=1e-6 * np.abs(y).max())
+
+
+@pytest.mark.parametrize("M", [17, 64, 100, 300])
+def test_gemm_ragged(M):
+    """Prefill GEMM on the matrix cores: 64-row tiles up to 64 rows, 256-row
+    tiles above; rows not a multiple of the 256-row N tile."""
+    rows, cols, seed = 600, 1536, 16
+    inp, packed = case(rows, cols, seed)
+    w = weights(rows, cols, seed)
+    X = synth.activations(M, cols, seed)
+    buf, Y = guarded((M, rows), torch.bfloat16)
+    fqm.gemm(w, bf16_dev(X), Y=Y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(Y), oracle.lut4.gemv(packed, inp.lut, X, cols), "bf16", f"M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_gemm_small_m_is_the_gemv(M):
+    rows, cols, seed = 17408, 5120, 7
+    w = weights(rows, cols, seed)
+    X = bf16_dev(synth.activations(M, cols, 17))
+    assert torch.equal(fqm.gemm(w, X), fqm.gemv(w, X))
+
+
+def test_gemm_prefill_full_layer_sampled():
+    """M = 2048 on the up layer (17408 x 5120), checked on 48 sampled rows of
+    X against the oracle (the whole product is too slow for the oracle)."""
+    rows, cols, seed = 17408, 5120, 7
+    inp, packed = case(rows, cols, seed)
+    w = weights(rows, cols, seed)
+    X = synth.activations(2048, cols, 18)
+    Y = fqm.gemm(w, bf16_dev(X))
+    pick = np.random.default_rng(0).choice(2048, size=48, replace=False)
+    pick[:2] = [0, 2047]
+    assert_close(to_f64(Y)[pick], oracle.lut4.gemv(packed, inp.lut, X[pick], cols), "bf16", "prefill")
+    assert torch.equal(Y, fqm.gemm(w, bf16_dev(X)))  # fixed-order sums: bitwise repeatable
