@@ -402,13 +402,13 @@ def gemv(w: _WeightsBase, x: torch.Tensor, y: torch.Tensor | None = None,
     return y
 
 
-def gemm_workspace_size(w: Lut6Weights, M: int) -> int:
+def gemm_workspace_size(w: _WeightsBase, M: int) -> int:
     return int(load().fqm_gemm_workspace_size(w.ref, M))
 
 
-def gemm(w: Lut6Weights, X: torch.Tensor, Y: torch.Tensor | None = None,
+def gemm(w: _WeightsBase, X: torch.Tensor, Y: torch.Tensor | None = None,
          workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Y[M][rows] = X[M][cols] W^T in bf16 with fp32 accumulation."""
+    """Y[M][rows] = X[M][cols] W^T in bf16 with fp32 accumulation (LUT6 or LUT4 weights)."""
     M = X.shape[0]
     if Y is None:
         Y = torch.empty((M, w.rows), dtype=torch.bfloat16, device=X.device)
