@@ -11,6 +11,7 @@ synthetic input already resident in HBM:
   lut4_prefill               LUT4 GEMM, X 2048x5120 times the LUT4 up weights
   fabq_b1, fabq_b8           FABQ-RC-style GEMV, 5120x5120, the layer's drawn blocksize
   mdbf_b1, mdbf_b16          MDBF GEMV, n = m = 4096, r = 2000, l = 2, P = 1
+  mdbf_up_b1, mdbf_down_b1   MDBF GEMV on the MLP shapes (17408x5120, 5120x17408), r = 3913 (1 bpw)
 
 ``value`` is the batch-1 LUT-GEMV effective bandwidth: algorithmic bytes of
 the up and down calls divided by their summed kernel time.  Weight tensors are
@@ -209,15 +210,17 @@ def main():
                              flops=2 * b * cfg["rows"] * cfg["cols"], bound="alu",
                              kernel=f"fabq_gemv batch {b}")
 
-    # ---- MDBF (n = m = 4096, r = 2000, l = 2, P = 1) ------------------------------
-    if wanted("mdbf_b1", "mdbf_b16"):
-        cfg = C["mdbf"]
+    # ---- MDBF (n = m = 4096, r = 2000, l = 2, P = 1; MLP shapes at 1 bpw) ---------
+    for prefix in ("mdbf", "mdbf_up", "mdbf_down"):
+        cfg = C[prefix]
+        if not wanted(*[f"{prefix}_b{b}" for b in cfg["batches"]]):
+            continue
         inp = synth.mdbf_input(cfg["n"], cfg["m"], cfg["r"], cfg["l"], cfg["P"], cfg["seed"])
         m0 = fqm.MdbfWeights.from_arrays(inp.n, inp.m, inp.r, inp.l, inp.S_A, inp.S_B,
                                          inp.A_amp, inp.B_amp, inp.Q_U, inp.Q_V, device=dev)
         mcopies = [m0] + [m0.clone() for _ in range(n_copies(m0) - 1)]
         for b in cfg["batches"]:
-            key = f"mdbf_b{b}"
+            key = f"{prefix}_b{b}"
             if not wanted(key):
                 continue
             x = bf16(synth.activations(b, cfg["m"], cfg["seed"]))

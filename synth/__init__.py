@@ -330,4 +330,8 @@ CONFIGS = {
     "prefill": dict(M=2048, weights="lut6_up", seed=4),
     "fabq": dict(rows=5120, cols=5120, seed=5, batches=(1, 8)),
     "mdbf": dict(n=4096, m=4096, r=2000, l=2, P=1, seed=6, batches=(1, 16)),
+    # MLP shapes; r = 3913 is the rank the page's bit accounting gives for
+    # 1 bit per weight at l = 2, P = 1 (2 bits is past the shape's maximum)
+    "mdbf_up": dict(n=17408, m=5120, r=3913, l=2, P=1, seed=9, batches=(1,)),
+    "mdbf_down": dict(n=5120, m=17408, r=3913, l=2, P=1, seed=10, batches=(1,)),
 }

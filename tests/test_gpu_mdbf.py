@@ -73,3 +73,22 @@ def test_deterministic_and_batch_independent():
     # a batch row computed alone matches its row of the batch
     y3 = to_f64(fqm.gemv(w, bf16_dev(x[5:6]), out_dtype=torch.float32))
     assert np.linalg.norm(y3[0] - y1[5]) <= 1e-6 * np.linalg.norm(y1[5])
+
+
+# Rectangular MLP shapes of a 27B-class layer (up 17408 x 5120, down
+# 5120 x 17408), the rank taken from the page's bit accounting at 2 bits per
+# weight (clamped to the shape's reachable maximum), with more envelopes (l)
+# and two paths (P).
+@pytest.mark.parametrize("n,m,l,P,batch", [(17408, 5120, 4, 2, 1), (5120, 17408, 4, 2, 16),
+                                           (17408, 5120, 16, 1, 8), (5120, 17408, 1, 2, 1)])
+def test_mlp_shapes_more_envelopes_and_paths(n, m, l, P, batch):
+    r = oracle.mdbf.rank(2.0, n, m, l, P)
+    assert 1 <= r <= min(n, m)
+    inp, paths = case(n, m, r, l, P, 80 + l + P)
+    x = synth.activations(batch, m, 81)
+    print(f"mdbf n={n} m={m} r={r} l={l} P={P} batch {batch}", flush=True)
+    buf, y = guarded((batch, n), torch.float32)
+    fqm.gemv(weights(inp), bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.mdbf.gemv_factored(paths, x, n, m, r), "f32", f"{n}x{m} l={l} P={P}")
