@@ -101,8 +101,16 @@ def main():
         print(json.dumps(msweep(fqm, synth, bf16, dev, args.rotate_gb)))
         return
 
+    K = args.steps
+
     def n_copies(w):
-        return max(2, int(np.ceil(args.rotate_gb * 1e9 / w.nbytes())))
+        # Call s reads copy s mod n.  Eager warm-up calls are s < W, the timed
+        # graph s in [W, W + K), the untimed replay right before it s in
+        # [W + K, W + 2K): with n >= W + 2K every call of the three reads a
+        # copy of its own, so the timed calls never start on copies the
+        # untimed replay just left in the last-level cache; n also covers the
+        # rotation floor (>= 1.2 GB, several times the 256 MB cache).
+        return max(int(np.ceil(args.rotate_gb * 1e9 / w.nbytes())), args.warmup + 2 * K + 2)
 
     t_gen = time.time()
     C = synth.CONFIGS
@@ -143,12 +151,12 @@ def main():
         ws = lut6["up"]
         X = bf16(synth.activations(M, C["lut6_up"]["cols"], C["prefill"]["seed"]))
         Y = torch.empty((M, C["lut6_up"]["rows"]), dtype=torch.bfloat16, device=dev)
-        Nn, K = C["lut6_up"]["rows"], C["lut6_up"]["cols"]
+        Nn, Kc = C["lut6_up"]["rows"], C["lut6_up"]["cols"]
         gws_bytes = fqm.gemm_workspace_size(ws[0], M)
         gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev) if gws_bytes else None
         rows["prefill"] = dict(
             fn=lambda s, ws=ws, X=X, Y=Y, gws=gws: fqm.gemm(ws[(s + 1) % len(ws)], X, Y=Y, workspace=gws),
-            bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * K,
+            bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * Kc,
             bound="mfma", kernel="lut6_gemm (with its K-split last round and reduction)")
 
     # ---- LUT4 weights (up, down shapes), batch 1 and 8, prefill on the up layer --
@@ -181,12 +189,12 @@ def main():
         ws = lut4["up"]
         X = bf16(synth.activations(M, C["lut4_up"]["cols"], C["prefill"]["seed"]))
         Y = torch.empty((M, C["lut4_up"]["rows"]), dtype=torch.bfloat16, device=dev)
-        Nn, K = C["lut4_up"]["rows"], C["lut4_up"]["cols"]
+        Nn, Kc = C["lut4_up"]["rows"], C["lut4_up"]["cols"]
         gws_bytes = fqm.gemm_workspace_size(ws[0], M)
         gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev) if gws_bytes else None
         rows["lut4_prefill"] = dict(
             fn=lambda s, ws=ws, X=X, Y=Y, gws=gws: fqm.gemm(ws[(s + 1) % len(ws)], X, Y=Y, workspace=gws),
-            bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * K,
+            bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * Kc,
             bound="mfma", kernel="lut4_gemm (with its K-split last round and reduction)")
 
     # ---- FABQ (5120^2, the layer's drawn blocksize) ------------------------------
@@ -249,16 +257,17 @@ def main():
     # rotating across device copies) are captured into one HIP graph, so the
     # launches go out back to back without per-call Python overhead; the
     # graph is replayed between two HIP events recorded on the launch stream,
-    # and a row's time is its average call duration in that stream.
-    K = args.steps
-    graphs = {}
+    # and a row's time is its average call duration in that stream.  A second
+    # graph of K calls over other copies is replayed untimed right before it.
+    graphs, warm_graphs = {}, {}
     if not args.no_graph:
         for k in order:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for s in range(K):
-                    rows[k]["fn"](args.warmup + s)
-            graphs[k] = g
+            for dst, s0 in ((graphs, args.warmup), (warm_graphs, args.warmup + K)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for s in range(K):
+                        rows[k]["fn"](s0 + s)
+                dst[k] = g
     ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for k in order}
     torch.cuda.synchronize()
@@ -267,10 +276,11 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for k in order:
-        # an untimed replay of the row's own graph first: each row is timed on
-        # a GPU that has just run that row, not whatever row preceded it
+        # an untimed replay of the row's own calls first (on other weight
+        # copies): each row is timed on a GPU that has just run that row, not
+        # whatever row preceded it, and its timed calls still read HBM
         if graphs:
-            graphs[k].replay()
+            warm_graphs[k].replay()
         ev[k][0].record(stream)
         if graphs:
             graphs[k].replay()
@@ -311,6 +321,11 @@ def main():
                     bytes_per_launch={k: res[k]["bytes"] for k in b1},
                     us_per_launch={k: round(res[k]["us_per_call"], 3) for k in b1})
 
+    ceiling = stream_read_ceiling(K, args.warmup, args.rotate_gb, dev)
+    if ceiling:
+        roofline["stream_read_ceiling_gbs"] = ceiling["gbs"]
+        roofline["frac_of_stream_read_ceiling"] = round(value / ceiling["gbs"], 4)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(lut6_inputs, rows, res, fqm, bf16, dev)
@@ -333,6 +348,7 @@ def main():
         "prefill_gemm_tflops": round(res["prefill"]["tflops"], 1) if "prefill" in res else None,
         "prefill_frac_of_bf16_peak": round(res["prefill"]["frac_mfma"], 4) if "prefill" in res else None,
         "roofline": roofline,
+        "hbm_stream_read_ceiling": ceiling,
         "cpu_baseline": cpu,
         "dense_reference": dense,
         "rows": {k: {kk: (round(v, 3) if isinstance(v, float) else v) for kk, v in d.items()}
@@ -340,6 +356,54 @@ def main():
         "setup_s": round(t_gen, 1), "timed_wall_s": round(wall, 3),
     }
     print(json.dumps(out))
+
+
+def stream_read_ceiling(K, warmup, rotate_gb, dev, nbytes=69_120_000):
+    """A plain streaming read of nbytes (the up layer's packed codes and
+    tables) per call, timed as the rows are: K calls in a graph over rotating
+    buffers (>= 1.2 GB, disjoint from an untimed replay right before); the
+    achievable HBM read bandwidth of this GPU, context for the GEMV rows."""
+    import ctypes
+    import torch
+    from dequant_matmul_amd import build as fbuild
+    if not os.path.exists(fbuild.BENCH_LIB):
+        return None
+    lib = ctypes.CDLL(fbuild.BENCH_LIB)
+    fn = lib.fqm_bench_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    n = max(int(np.ceil(rotate_gb * 1e9 / nbytes)), warmup + 2 * K + 2)
+    bufs = [torch.full((nbytes,), 1, dtype=torch.uint8, device=dev) for _ in range(n)]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(s):
+        rc = fn(bufs[s % n].data_ptr(), nbytes, sink.data_ptr(), 0xDEADBEEF, stream.cuda_stream)
+        if rc:
+            raise RuntimeError(f"stream read launch failed ({rc})")
+
+    for s in range(warmup):
+        call(s)
+    graphs = []
+    for s0 in (warmup, warmup + K):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(K):
+                call(s0 + s)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    graphs[1].replay()
+    e0.record(stream)
+    graphs[0].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / K
+    del bufs
+    torch.cuda.empty_cache()
+    return dict(kernel="stream_read_kernel (libfqm_bench.so)", bytes_per_call=nbytes,
+                us_per_call=round(us, 3), gbs=round(nbytes / us * 1e-3, 1),
+                frac_of_peak=round(nbytes / us * 1e-3 / HBM_PEAK_GBS, 4))
 
 
 def traffic_record():
@@ -370,19 +434,22 @@ def msweep(fqm, synth, bf16, dev, rotate_gb, K_CALLS=20):
     cfg = synth.CONFIGS["lut6_up"]
     inp = synth.lut6_input(cfg["rows"], cfg["cols"], cfg["seed"])
     w0 = fqm.Lut6Weights.from_codes(inp.codes, inp.lut, device=dev)
-    ws = [w0] + [w0.clone() for _ in range(max(2, int(np.ceil(rotate_gb * 1e9 / w0.nbytes()))) - 1)]
+    n = max(int(np.ceil(rotate_gb * 1e9 / w0.nbytes())), 2 * K_CALLS + 2)
+    ws = [w0] + [w0.clone() for _ in range(n - 1)]
     N, K = cfg["rows"], cfg["cols"]
 
     def timed(fn):
         fn(0)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(K_CALLS):
-                fn(i + 1)
-        g.replay()
+        g, warm = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        for graph, s0 in ((g, 1), (warm, 1 + K_CALLS)):  # disjoint weight copies
+            with torch.cuda.graph(graph):
+                for i in range(K_CALLS):
+                    fn(s0 + i)
+        warm.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        warm.replay()
         e0.record()
         g.replay()
         e1.record()
@@ -455,11 +522,27 @@ def dense_reference(res, rotate_gb, dev):
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(lut6_inputs, rows, res, fqm, bf16, dev):
-    """The oracle (numpy fp64: unpack, decode, product) on the host cores, on
-    the batch-1 up and down layers: the median of three timed passes with the
-    BLAS threads the host offers, and one pass on a single thread; also checks
-    the GPU result of those calls against it."""
+    """The oracle (numpy fp64: unpack, decode, product) on the host cores.
+
+    Headline: one batch-1 call each of the up and down LUT6 layers (the
+    metric's workload), the median of three passes with the BLAS threads the
+    host offers, plus one single-thread pass; the GPU result of those calls is
+    checked against it.  Beside it, the oracle on the other workloads, each on
+    a bounded sample: the tiny LUT6 GEMV (median of 20), 256 of the prefill's
+    2048 rows of X, the FABQ layer at batch 1 and the MDBF layer at batch 1
+    (median of 3 each).  Inputs are prepared outside the timed region."""
     import oracle
     import synth
     try:
@@ -505,6 +588,43 @@ def cpu_baseline(lut6_inputs, rows, res, fqm, bf16, dev):
         ok, m = oracle.compare.check(y, yo[key], "bf16")
         parity[key] = dict(ok=ok, rel_l2=m["rel_l2"], max_rel=m["max_rel"])
     flops = sum(rows[key]["flops"] for key, *_ in cases)
+
+    def med(fn, n):
+        ts = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[n // 2]
+
+    others = {}
+    cfg = C["tiny_lut6"]
+    ti = synth.lut6_input(cfg["rows"], cfg["cols"], cfg["seed"])
+    tp, tx = oracle.lut6.pack_codes(ti.codes), synth.activations(1, cfg["cols"], cfg["seed"])
+    t = med(lambda: oracle.lut6.gemv(tp, ti.lut, tx, cfg["cols"]), 20)
+    b = cfg["rows"] * cfg["cols"] * 3 // 4 + cfg["rows"] * 128 + cfg["cols"] * 2 + cfg["rows"] * 4
+    others["tiny_lut6_256x512_b1"] = dict(seconds=round(t, 5), gbs=round(b / t / 1e9, 4))
+    if "up" in lut6_inputs:
+        up, sub = lut6_inputs["up"], 256
+        cu = C["lut6_up"]
+        Xs = synth.activations(C["prefill"]["M"], cu["cols"], C["prefill"]["seed"])[:sub]
+        pu = oracle.lut6.pack_codes(up.codes)
+        t = med(lambda: oracle.lut6.gemm(pu, up.lut, Xs, cu["cols"]), 1)
+        f = 2 * sub * cu["rows"] * cu["cols"]
+        others["prefill_256_of_2048_rows"] = dict(seconds=round(t, 3), gflops=round(f / t / 1e9, 2),
+                                                  full_m_estimate_s=round(t * C["prefill"]["M"] / sub, 1))
+    cf = C["fabq"]
+    fi = synth.fabq_input(cf["rows"], cf["cols"], cf["seed"])
+    fp, fx = oracle.fabq.pack(fi), synth.activations(1, cf["cols"], cf["seed"])
+    t = med(lambda: oracle.fabq.gemv(fp, fx, cf["rows"], cf["cols"], fi.blocksize, fi.n_hi), 3)
+    others["fabq_b1"] = dict(seconds=round(t, 4), gbs=round(rows["fabq_b1"]["bytes"] / t / 1e9, 4)
+                             if "fabq_b1" in rows else None)
+    cm = C["mdbf"]
+    mi = synth.mdbf_input(cm["n"], cm["m"], cm["r"], cm["l"], cm["P"], cm["seed"])
+    mp, mx = oracle.mdbf.pack(mi), synth.activations(1, cm["m"], cm["seed"])
+    t = med(lambda: oracle.mdbf.gemv_factored(mp, mx, cm["n"], cm["m"], cm["r"]), 3)
+    others["mdbf_b1"] = dict(seconds=round(t, 4), gbs=round(rows["mdbf_b1"]["bytes"] / t / 1e9, 4)
+                             if "mdbf_b1" in rows else None)
     return dict(value=round(tot_bytes / tot_t / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
                 sample="one batch-1 call each of the up (17408x5120) and down (5120x17408) "
                        "layers: numpy fp64 unpack + decode + matmul, median of 3 passes; cores = "
@@ -512,7 +632,7 @@ def cpu_baseline(lut6_inputs, rows, res, fqm, bf16, dev):
                 seconds=round(tot_t, 3), gflops=round(flops / tot_t / 1e9, 3),
                 single_thread_seconds=round(single, 3) if single is not None else None,
                 single_thread_gbs=round(tot_bytes / single / 1e9, 3) if single else None,
-                blas=blas, cpu=platform.processor() or platform.machine(),
+                blas=blas, cpu=cpu_model(), other_workloads=others,
                 parity_vs_gpu=parity)
 
 

@@ -292,6 +292,10 @@ class FabqWeights(_WeightsBase):
         device tensors, with q4 / signs / idx packed on the GPU."""
         n_lo = rows - n_hi
         nb = cols // blocksize
+        ro = np.asarray(row_of).reshape(-1)
+        if ro.shape != (rows,) or not np.array_equal(np.sort(ro), np.arange(rows)):
+            raise ValueError("row_of must be a permutation of range(rows): each output row is "
+                             "written by exactly one stored row")
         q4_d = _dev((np.asarray(q4).astype(np.int16) & 15).astype(np.uint8).reshape(n_hi, cols),
                     torch.uint8, device)
         signs_d = _dev(np.asarray(signs, dtype=np.uint8).reshape(n_lo, cols), torch.uint8, device)
@@ -379,6 +383,36 @@ def dequant(w: _WeightsBase, stream=None) -> torch.Tensor:
     return out
 
 
+def _weights_device(w: _WeightsBase):
+    return next((t.device for t in w._keep if isinstance(t, torch.Tensor)), None)
+
+
+def _check_operand(t: torch.Tensor, name: str, shape: tuple, dtypes: tuple, device):
+    """The C ABI sees only a pointer, so a wrong dtype, shape, layout or
+    device would read or write past the tensor: refuse it here."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} is on {t.device}; the library takes GPU tensors")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device} but the weights are on {device}")
+
+
+def _check_workspace(ws, device):
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor) or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous torch.Tensor")
+    if ws.device.type != "cuda" or (device is not None and ws.device != device):
+        raise ValueError(f"workspace is on {ws.device}; expected the weights' device {device}")
+
+
 def workspace_size(w: _WeightsBase, batch: int) -> int:
     return int(load().fqm_workspace_size(w.ref, batch))
 
@@ -387,11 +421,21 @@ def gemv(w: _WeightsBase, x: torch.Tensor, y: torch.Tensor | None = None,
          out_dtype: torch.dtype = torch.bfloat16, workspace: torch.Tensor | None = None,
          stream=None) -> torch.Tensor:
     """y[batch][rows] = x[batch][cols] W^T (batch 1..16), decoded in-kernel."""
+    if not isinstance(x, torch.Tensor):
+        raise ValueError("x must be a torch.Tensor")
     if x.dim() == 1:
         x = x[None]
+    if x.dim() != 2:
+        raise ValueError(f"x must be [batch][cols]; got shape {tuple(x.shape)}")
     batch = x.shape[0]
+    dev = _weights_device(w)
+    _check_operand(x, "x", (batch, w.cols), (torch.bfloat16,), dev)
     if y is None:
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError(f"out_dtype must be bfloat16 or float32, not {out_dtype}")
         y = torch.empty((batch, w.rows), dtype=out_dtype, device=x.device)
+    _check_operand(y, "y", (batch, w.rows), (torch.bfloat16, torch.float32), dev)
+    _check_workspace(workspace, dev)
     ydt = FQM_F32 if y.dtype == torch.float32 else FQM_BF16
     need = workspace_size(w, batch)
     if need and workspace is None:
@@ -409,9 +453,15 @@ def gemm_workspace_size(w: _WeightsBase, M: int) -> int:
 def gemm(w: _WeightsBase, X: torch.Tensor, Y: torch.Tensor | None = None,
          workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Y[M][rows] = X[M][cols] W^T in bf16 with fp32 accumulation (LUT6 or LUT4 weights)."""
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise ValueError("X must be a 2-D torch.Tensor [M][cols]")
     M = X.shape[0]
+    dev = _weights_device(w)
+    _check_operand(X, "X", (M, w.cols), (torch.bfloat16,), dev)
     if Y is None:
         Y = torch.empty((M, w.rows), dtype=torch.bfloat16, device=X.device)
+    _check_operand(Y, "Y", (M, w.rows), (torch.bfloat16,), dev)
+    _check_workspace(workspace, dev)
     need = gemm_workspace_size(w, M)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)

@@ -1,7 +1,8 @@
 """Build the HIP library ``libfqm.so`` in-tree for gfx950 with hipcc.
 
 Every source under ``csrc/`` is compiled and linked into one shared object
-next to this file.  Packed-FP32 instruction selection is disabled for the
+next to this file; the benchmark's reference kernel under ``bench_kernels/``
+goes into ``libfqm_bench.so`` beside it.  Packed-FP32 instruction selection is disabled for the
 device code (``-packed-fp32-ops``).
 """
 from __future__ import annotations
@@ -29,13 +30,28 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
+BENCH_LIB = os.path.join(HERE, "libfqm_bench.so")
+
+
+def bench_sources():
+    return sorted(glob.glob(os.path.join(HERE, "bench_kernels", "*.hip")))
+
+
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+    """Build libfqm.so (the library) and libfqm_bench.so (the benchmark's
+    streaming-read reference kernel)."""
+    _hipcc_shared(LIB, sources(), verbose)
+    _hipcc_shared(BENCH_LIB, bench_sources(), verbose)
+    return LIB
+
+
+def _hipcc_shared(lib: str, srcs, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-function",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           "-o", tmp] + sources()
+           "-o", tmp] + list(srcs)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,8 +61,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

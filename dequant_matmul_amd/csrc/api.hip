@@ -167,6 +167,8 @@ fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_
     if (!aligned16(y) || (x && !aligned16(x))) return FQM_E_ALIGN;
     const int y_f32 = y_dtype == FQM_F32;
     hipStream_t s = as_stream(stream);
+    if (w->cols == 0)  // an empty sum: y = 0 whatever the format (x is not read)
+        return hip_status(launch_zero_fill(y, (int64_t)batch * w->rows, y_f32 ? 4 : 2, s));
     switch (w->format) {
         case FQM_LUT6: {
             const size_t need = fqm_workspace_size(w, batch);
@@ -208,6 +210,7 @@ static bool lut_format(const fqm_weights& w) { return w.format == FQM_LUT6 || w.
 size_t fqm_gemm_workspace_size(const fqm_weights* w, int64_t M) {
     if (check_weights(w) != FQM_OK || !lut_format(*w) || M <= 0 || w->rows == 0) return 0;
     if (w->cols % 64 || M * w->cols * 2 > INT32_MAX) return 0;
+    if (w->cols == 0) return 0;  // Y is zero-filled, no K parts
     if (gemm_as_gemv(*w, M)) return fqm::lut_gemv_mfma_workspace(*w, (int)M);
     return fqm::lut_gemm_workspace(*w, M);
 }
@@ -221,11 +224,13 @@ fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_
     if (M > (int64_t)65535 * 128) return FQM_E_SHAPE;
     if (M == 0 || w->rows == 0) return FQM_OK;
     if (w->cols % 64 || M * w->cols * 2 > INT32_MAX) return FQM_E_SHAPE;
-    if (!Y || !X) return FQM_E_NULL;
-    if (!aligned16(Y) || !aligned16(X)) return FQM_E_ALIGN;
+    if (!Y || (w->cols > 0 && !X)) return FQM_E_NULL;
+    if (!aligned16(Y) || (X && !aligned16(X))) return FQM_E_ALIGN;
     const size_t need = fqm_gemm_workspace_size(w, M);
     if (need && (!workspace || ws_bytes < need)) return FQM_E_WORKSPACE;
     if (need && !aligned16(workspace)) return FQM_E_ALIGN;
+    if (w->cols == 0)  // an empty sum: Y = 0 (the tile kernels assume at least one K step)
+        return hip_status(launch_zero_fill(Y, M * w->rows, 2, as_stream(stream)));
     float* gws = static_cast<float*>(workspace);
     if (gemm_as_gemv(*w, M))  // Y[M][rows] bf16 is the GEMV's y[batch][rows]
         return hip_status(w->format == FQM_LUT4 ? launch_lut4_gemv(*w, X, Y, 0, (int)M, gws, as_stream(stream))

@@ -73,6 +73,8 @@ __device__ __forceinline__ void codes16(uint32_t d0, uint32_t d1, uint32_t d2, u
 
 hipError_t launch_pack_bits(const uint8_t* vals, uint8_t* out, int64_t rows, int64_t cols,
                             int bits, int64_t ld, int32_t* d_err, hipStream_t s);
+// Zeroes n elements of elem_bytes (2 or 4) at p, with a kernel (graph-safe).
+hipError_t launch_zero_fill(void* p, int64_t n, int elem_bytes, hipStream_t s);
 hipError_t launch_unpack6(const uint8_t* packed, uint8_t* codes, int64_t rows, int64_t cols,
                           int64_t ld, hipStream_t s);
 hipError_t launch_dequant_lut6(const fqm_weights& w, uint16_t* W, hipStream_t s);

@@ -133,9 +133,28 @@ __global__ __launch_bounds__(256) void dequant_fabq_kernel(fqm_fabq f, int64_t r
     W[out_row * cols + k] = f64_to_bf16_rne(w);
 }
 
+// Zeroes n 16-bit or 32-bit elements (an empty product: cols == 0).  A fill
+// kernel rather than hipMemsetAsync, so the call can sit in a captured graph.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint32_t* __restrict__ p, int64_t words,
+                                                        uint16_t* __restrict__ tail) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < words) p[t] = 0u;
+    if (t == 0 && tail) *tail = 0;
+}
+
 inline unsigned grid_for(int64_t n, int block) { return (unsigned)((n + block - 1) / block); }
 
 }  // namespace
+
+hipError_t launch_zero_fill(void* p, int64_t n, int elem_bytes, hipStream_t s) {
+    const int64_t bytes = n * elem_bytes;
+    if (bytes == 0) return hipSuccess;
+    const int64_t words = bytes / 4;  // p is 16-byte aligned (checked by the callers)
+    uint16_t* tail = (bytes & 2) ? reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p) + 4 * words) : nullptr;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(grid_for(words > 0 ? words : 1, 256)), dim3(256), 0, s,
+                       static_cast<uint32_t*>(p), words, tail);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack_bits(const uint8_t* vals, uint8_t* out, int64_t rows, int64_t cols,
                             int bits, int64_t ld, int32_t* d_err, hipStream_t s) {

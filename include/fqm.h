@@ -61,8 +61,9 @@
  *     are reported through a device flag instead.
  *   - Alignment: every tensor base pointer must be 16-byte aligned and every
  *     row stride `ld` a multiple of 16 bytes (FQM_E_ALIGN otherwise).
- *   - Empty work: rows == 0, batch rows == 0 or M == 0 enqueue nothing and
- *     return FQM_OK; cols == 0 writes zeros to y.
+ *   - Empty work: rows == 0 or M == 0 enqueue nothing and return FQM_OK;
+ *     cols == 0 writes zeros to y (fqm_gemv) or Y (fqm_gemm), and x / X may
+ *     then be NULL.
  */
 #ifndef FQM_H
 #define FQM_H

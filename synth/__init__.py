@@ -90,7 +90,27 @@ class Lut6Input:
     seed: int
 
 
-def lut6_input(rows: int, cols: int, seed: int, *, exact_argmin: bool = False) -> Lut6Input:
+def _signed_levels(delta, tiers: int, jitter: float, seed: int, stream: int) -> np.ndarray:
+    """The 2T signed levels of each row, ascending: shell centres (t + 1/2) D_r
+    mirrored about zero; with ``jitter`` > 0 each of the 2T levels is moved
+    independently by U(-jitter, jitter) D_r (stream [seed, stream]), so the
+    table is still sorted with T negative then T positive entries (jitter <
+    1/2) but no longer mirror-symmetric, as a Lloyd-refined table is not."""
+    rows = delta.shape[0]
+    t = np.arange(tiers, dtype=np.float64) + 0.5
+    if not jitter:
+        pos = t[None, :] * delta[:, None]
+        return np.concatenate([-pos[:, ::-1], pos], axis=1)
+    if not 0 < jitter < 0.5:
+        raise ValueError("jitter must lie in (0, 1/2)")
+    jr = np.random.default_rng([seed, stream])
+    neg = (t[None, :] + jr.uniform(-jitter, jitter, size=(rows, tiers))) * delta[:, None]
+    pos = (t[None, :] + jr.uniform(-jitter, jitter, size=(rows, tiers))) * delta[:, None]
+    return np.concatenate([-neg[:, ::-1], pos], axis=1)
+
+
+def lut6_input(rows: int, cols: int, seed: int, *, exact_argmin: bool = False,
+               level_jitter: float = 0.0) -> Lut6Input:
     """Gaussian rows, 32 equal-width shells per sign, nearest-level codes.
 
     sigma_r is log-uniform on [0.005, 0.05]; w ~ N(0, sigma_r^2) in fp64.
@@ -98,16 +118,16 @@ def lut6_input(rows: int, cols: int, seed: int, *, exact_argmin: bool = False) -
     the shell centres (t + 1/2) D_r.  The table is the 64 signed levels sorted
     ascending (-l_31 ... -l_0, l_0 ... l_31), rounded fp64 -> fp32 -> bf16.
     A weight's code is the index of the nearest bf16 level (fp64 distance,
-    ties to the lower index).
+    ties to the lower index).  ``level_jitter`` (at most 0.3 keeps the
+    nearest level within one of the shell's own) moves every level on its own
+    (stream [seed, 5]), giving sorted tables that are not mirror-symmetric.
     """
     rng = np.random.default_rng(seed)
     sigma = np.exp(rng.uniform(math.log(0.005), math.log(0.05), size=rows))
     w = rng.standard_normal((rows, cols)) * sigma[:, None]
     amax = np.abs(w).max(axis=1)
     delta = amax / 32.0
-    t = np.arange(32, dtype=np.float64) + 0.5
-    pos = t[None, :] * delta[:, None]                       # [rows][32]
-    table = np.concatenate([-pos[:, ::-1], pos], axis=1)   # ascending by value
+    table = _signed_levels(delta, 32, level_jitter, seed, 5)   # ascending by value
     lut = bf16_bits_from_f64(table)
     lutv = _bf16_bits_to_f64(lut)
     if exact_argmin:
@@ -127,7 +147,10 @@ def _nearest_shell(w, delta, lutv, chunk_rows: int = 1024):
 
     bf16 rounding moves a level by at most 2^-9 of its value (< 0.07 D with
     32 tiers, < 0.015 D with 8), so the nearest rounded level is the shell's
-    own level or an adjacent one.  The tier count T is half the table width.
+    own level or an adjacent one; that still holds when every level is also
+    moved by up to 0.3 D (a weight of shell t is then within 0.87 D of level t
+    and at least 1.13 D from levels t +- 2).  The tier count T is half the
+    table width.
     """
     rows, cols = w.shape
     T = lutv.shape[1] // 2
@@ -158,7 +181,8 @@ class Lut4Input:
     seed: int
 
 
-def lut4_input(rows: int, cols: int, seed: int, *, exact_argmin: bool = False) -> Lut4Input:
+def lut4_input(rows: int, cols: int, seed: int, *, exact_argmin: bool = False,
+               level_jitter: float = 0.0) -> Lut4Input:
     """Gaussian rows, 8 equal-width shells per sign, nearest-level codes.
 
     As lut6_input with 8 tiers: sigma_r log-uniform on [0.005, 0.05],
@@ -166,14 +190,14 @@ def lut4_input(rows: int, cols: int, seed: int, *, exact_argmin: bool = False) -
     t = 0..7; the table is the 16 signed levels ascending, rounded fp64 ->
     fp32 -> bf16; a weight's code is the index of the nearest bf16 level
     (fp64 distance, ties to the lower index), found by the shell shortcut
-    unless ``exact_argmin``.
+    unless ``exact_argmin``.  ``level_jitter`` moves every level on its own
+    (stream [seed, 6]) as in ``lut6_input``.
     """
     rng = np.random.default_rng([seed, 4])
     sigma = np.exp(rng.uniform(math.log(0.005), math.log(0.05), size=rows))
     w = rng.standard_normal((rows, cols)) * sigma[:, None]
     delta = np.abs(w).max(axis=1) / 8.0
-    pos = (np.arange(8, dtype=np.float64) + 0.5)[None, :] * delta[:, None]
-    lut = bf16_bits_from_f64(np.concatenate([-pos[:, ::-1], pos], axis=1))
+    lut = bf16_bits_from_f64(_signed_levels(delta, 8, level_jitter, seed, 6))
     lutv = _bf16_bits_to_f64(lut)
     if exact_argmin:
         codes = np.empty((rows, cols), dtype=np.uint8)

@@ -218,3 +218,73 @@ def test_mdbf_argument_errors_and_workspace(lib):
     assert lib.fqm_workspace_size(ctypes.byref(mdbf(P=2)), 3) == 2 * 2 * 1 * 64 * (4096 + 2048)
     assert lib.fqm_dequant(ctypes.byref(mdbf()), FAKE, None) == E["UNSUPPORTED"]
     assert gemm(lib, mdbf(), M=1) == E["UNSUPPORTED"]
+
+
+def test_zero_cols_needs_no_x_and_no_workspace(lib):
+    """cols == 0 is an empty sum: y (or Y) is zero-filled by a kernel, x / X
+    may be NULL, and no K parts need a workspace.  Without a GPU the fill
+    launch itself fails (FQM_E_HIP); what matters here is that the host
+    checks let it through instead of reaching a tile kernel with no K steps."""
+    w = lut6(cols=0, ld=16)
+    assert lib.fqm_gemm_workspace_size(ctypes.byref(w), 300) == 0
+    assert gemm(lib, w, X=None, M=300) in (E["OK"], E["HIP"])
+    assert gemv(lib, w, x=None, batch=3) in (E["OK"], E["HIP"])
+    assert gemm(lib, w, X=None, Y=None, M=300) == E["NULL"]
+
+
+# ---- the Python binding refuses operands the C ABI cannot check -------------
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+
+def _host_lut6(rows=4, cols=64):
+    return fqm.Lut6Weights(torch.zeros((rows, 48), dtype=torch.uint8),
+                           torch.zeros((rows, 64), dtype=torch.bfloat16), rows, cols)
+
+
+@pytest.mark.parametrize("bad", ["dtype", "cols", "strided", "host", "ndim"])
+def test_binding_rejects_bad_x(bad):
+    w = _host_lut6()
+    x = {"dtype": torch.zeros((1, 64), dtype=torch.float32),
+         "cols": torch.zeros((1, 60), dtype=torch.bfloat16),
+         "strided": torch.zeros((64, 2), dtype=torch.bfloat16).t(),
+         "host": torch.zeros((1, 64), dtype=torch.bfloat16),
+         "ndim": torch.zeros((1, 1, 64), dtype=torch.bfloat16)}[bad]
+    with pytest.raises(ValueError):
+        fqm.gemv(w, x)
+    if x.dim() == 2:
+        with pytest.raises(ValueError):
+            fqm.gemm(w, x)
+
+
+@pytest.mark.parametrize("bad", ["shape", "dtype", "strided"])
+def test_binding_rejects_bad_y(bad):
+    w = _host_lut6()
+    y = {"shape": torch.zeros((2, 4), dtype=torch.bfloat16),
+         "dtype": torch.zeros((1, 4), dtype=torch.float16),
+         "strided": torch.zeros((4, 1), dtype=torch.float32).t()[:, :]}[bad]
+    if bad == "strided":
+        y = torch.zeros((4, 2), dtype=torch.float32)[:, :1].t()
+    with pytest.raises(ValueError):
+        fqm.gemv(w, torch.zeros((1, 64), dtype=torch.bfloat16), y=y)
+
+
+def test_binding_rejects_bad_gemm_output():
+    w = _host_lut6()
+    X = torch.zeros((3, 64), dtype=torch.bfloat16)
+    for Y in (torch.zeros((3, 5), dtype=torch.bfloat16), torch.zeros((3, 4), dtype=torch.float32)):
+        with pytest.raises(ValueError):
+            fqm.gemm(w, X, Y=Y)
+
+
+@pytest.mark.parametrize("row_of", [[0, 1, 1, 3], [0, 1, 2], [0, 1, 2, 4]])
+def test_fabq_row_map_must_be_a_permutation(row_of):
+    """A repeated or out-of-range output row would make the kernels write one
+    output twice or outside y: refused on the host before any upload."""
+    rows, cols, bs = 4, 64, 64
+    with pytest.raises(ValueError):
+        fqm.FabqWeights.from_arrays(rows, cols, bs, 1, np.asarray(row_of, np.int32),
+                                    np.zeros((1, cols), np.int8), np.zeros(1, np.uint16),
+                                    np.zeros((3, cols), np.uint8), np.zeros((3, 1), np.uint16),
+                                    np.zeros((3, 1), np.uint8), np.zeros(16, np.uint16),
+                                    device="cpu")

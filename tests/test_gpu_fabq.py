@@ -1,4 +1,5 @@
 """GPU parity for the FABQ-RC-style binary-core GEMV."""
+import dataclasses
 import functools
 
 import numpy as np
@@ -66,3 +67,41 @@ def test_all_int4_and_all_binary_layers(batch):
         x = synth.activations(batch, 1024, 52)
         y = fqm.gemv(weights(inp), bf16_dev(x), out_dtype=torch.float32)
         assert_close(to_f64(y), oracle.fabq.gemv(p, x, 64, 1024, 64, inp.n_hi), "f32", f"hi={frac}")
+
+
+def _full_nibble_range(rows, cols, seed, bs, hi_frac):
+    """A layer whose int4 rows hold every value -8..7.  The quantizer's
+    max|w|/7 scale never produces -8 (nibble 0x8), so the int4 values are
+    drawn directly; the binary rows come from the generator."""
+    base = synth.fabq_input(rows, cols, seed, blocksize=bs, hi_frac=hi_frac)
+    rng = np.random.default_rng(seed + 1)
+    q4 = rng.integers(-8, 8, size=base.q4.shape).astype(np.int8)
+    q4[:, :16] = np.arange(-8, 8, dtype=np.int8)
+    q4[:, -8:] = -8
+    inp = dataclasses.replace(base, q4=q4)
+    p = oracle.fabq.pack(inp)
+    assert (p["q4"] & 0x0F == 0x08).any() and (p["q4"] >> 4 == 0x08).any()
+    return inp, p
+
+
+@pytest.mark.parametrize("hi_frac", [0.25, 1.0])
+def test_int4_minus_eight_dequant_bit_exact(hi_frac):
+    inp, p = _full_nibble_range(96, 1024, 53, 128, hi_frac)
+    W = fqm.dequant(weights(inp)).view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.numerics.bf16_bits_from_f64_rne(oracle.fabq.decode(p, 96, 1024, 128, inp.n_hi))
+    assert np.array_equal(W, ref)
+
+
+@pytest.mark.parametrize("hi_frac", [0.25, 1.0])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+def test_int4_minus_eight_gemv(hi_frac, batch):
+    """Batches 1-3 on the VALU kernel, 4 and up on the matrix cores; int4 rows
+    with -8 in every position of a nibble pair."""
+    inp, p = _full_nibble_range(96, 1024, 53, 128, hi_frac)
+    x = synth.activations(batch, 1024, 55)
+    buf, y = guarded((batch, 96), torch.float32)
+    fqm.gemv(weights(inp), bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.fabq.gemv(p, x, 96, 1024, 128, inp.n_hi), "f32",
+                 f"hi={hi_frac} b{batch}")

@@ -120,8 +120,12 @@ def test_gemv_zero_cols_and_padded_rows():
     w0 = fqm.Lut6Weights(torch.zeros((5, 16), dtype=torch.uint8, device=DEV),
                          torch.zeros((5, 64), dtype=torch.bfloat16, device=DEV), 5, 0)
     y = torch.full((2, 5), 7.0, device=DEV)
-    fqm.gemv(w0, torch.zeros((2, 16), dtype=torch.bfloat16, device=DEV), y=y)
+    fqm.gemv(w0, torch.zeros((2, 0), dtype=torch.bfloat16, device=DEV), y=y)
     assert (y == 0).all()
+    # and through the GEMM entry point with more rows than the GEMV takes
+    Y = torch.full((300, 5), 7.0, dtype=torch.bfloat16, device=DEV)
+    fqm.gemm(w0, torch.zeros((300, 0), dtype=torch.bfloat16, device=DEV), Y=Y)
+    assert (Y == 0).all()
     # a row stride larger than the packed row
     inp, packed = lut6_case(1000, 1088, 7)
     w = fqm.Lut6Weights.from_codes(inp.codes, inp.lut, device=DEV, ld=1024)

@@ -47,9 +47,11 @@ def test_variants(l, P):
     assert_close(to_f64(y), oracle.mdbf.gemv_dense(paths, x, n, m, r), "f32", f"l={l} P={P}")
 
 
-# Batch slices per workgroup are 32 // l rows: l = 16 splits a batch of 16 into
-# eight slices, l = 3 into slices of 10 and 6 (a partly empty second column
-# block); m = 544 and r = 300 are not multiples of the 256-column K block.
+# A batch slice is floor(64 / (3 l)) rows, at least 1 (three bf16 parts of
+# each of l envelopes per row fill the 64 operand columns): l = 16 splits a
+# batch of 16 into sixteen slices of one row, l = 3 into slices of 7, 7 and 2
+# (a partly empty last slice); m = 544 and r = 300 are not multiples of the
+# 256-column K block.
 @pytest.mark.parametrize("l,P,batch", [(16, 1, 16), (3, 2, 16), (2, 1, 7), (1, 2, 1)])
 def test_batch_slices_and_padding(l, P, batch):
     n, m, r = 333, 544, 300

@@ -1,6 +1,7 @@
 """Pins for the per-row LUT 4-bit oracle (the 8-tier row of "Qwen3.8-27B -
 BenQ 6-bit", "Why equal-width shells", read as the 6-bit format is)."""
 import numpy as np
+import pytest
 import torch
 
 import synth
@@ -86,8 +87,31 @@ def test_gemv_one_hot_constant_and_mirror():
     assert np.array_equal(ym, -y)
 
 
-def test_bits_per_weight():
-    assert lut4.bpw(5120) == 4.0 + 256.0 / 5120
+def test_bits_per_weight_counts_the_stored_bytes():
+    """bpw times the weight count is exactly the bits of what is stored: the
+    packed code array the oracle's own packer writes (two codes per byte, no
+    padding at these widths) plus the bf16 tables."""
+    for rows, cols in ((3, 64), (17, 1024), (5, 5120), (2, 17408)):
+        inp = synth.lut4_input(rows, cols, seed=cols)
+        packed = lut4.pack_codes(inp.codes)
+        stored_bits = 8 * (packed.nbytes + inp.lut.nbytes)
+        assert lut4.bpw(cols) * rows * cols == stored_bits
+    assert lut4.bpw(256) == 5.0  # 4 code bits + 256 table bits over 256 columns
+
+
+@pytest.mark.parametrize("jitter", [0.1, 0.3])
+def test_jittered_tables_sorted_not_mirror_and_codes_nearest(jitter):
+    """Tables with every level moved on its own stay sorted with 8 negative
+    then 8 positive entries but are not mirror-symmetric; the shell shortcut
+    still picks the nearest level."""
+    a = synth.lut4_input(128, 512, seed=9, level_jitter=jitter)
+    b = synth.lut4_input(128, 512, seed=9, level_jitter=jitter, exact_argmin=True)
+    lv = bf16_to_f64(a.lut)
+    assert np.all(np.diff(lv, axis=1) > 0)
+    assert np.all(lv[:, :8] < 0) and np.all(lv[:, 8:] > 0)
+    assert np.all(np.any(lv[:, ::-1] != -lv, axis=1))  # no row is a mirror image
+    assert np.mean(lv[:, ::-1] != -lv) > 0.5
+    assert np.array_equal(a.codes, b.codes)
 
 
 def test_generator_shell_shortcut_equals_full_argmin():

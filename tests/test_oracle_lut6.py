@@ -147,3 +147,31 @@ def test_bpw_formula_and_page_table():
     assert lo < float(g["total_bits"]) < hi
     assert float(g["code_bits"]) + float(g["lut_bits"]) == pytest.approx(float(g["total_bits"]), abs=0.005)
     assert lo - 6 < float(g["lut_bits"]) < hi - 6
+
+
+def test_bpw_counts_the_stored_bytes():
+    """bpw times the weight count equals the bits of the arrays actually
+    stored: the oracle packer's code bytes (4 codes per 3 bytes, unpadded)
+    plus the 64-entry bf16 tables."""
+    for rows, cols in ((3, 64), (8, 512), (2, 5120), (2, 17408)):
+        inp = synth.lut6_input(rows, cols, seed=cols)
+        packed = lut6.pack_codes(inp.codes)
+        assert lut6.bpw(cols) * rows * cols == 8 * (packed.nbytes + inp.lut.nbytes)
+
+
+@pytest.mark.parametrize("jitter", [0.1, 0.3])
+def test_jittered_tables_sorted_not_mirror_and_codes_nearest(jitter):
+    """Every level moved on its own (a stand-in for a Lloyd-refined table):
+    still sorted, 32 negative then 32 positive, but not mirror-symmetric, and
+    the shell shortcut still returns the nearest level."""
+    a = synth.lut6_input(128, 512, seed=11, level_jitter=jitter)
+    b = synth.lut6_input(128, 512, seed=11, level_jitter=jitter, exact_argmin=True)
+    lv = bf16_to_f64(a.lut)
+    assert np.all(np.diff(lv, axis=1) > 0)
+    assert np.all(lv[:, :32] < 0) and np.all(lv[:, 32:] > 0)
+    assert np.all(np.any(lv[:, ::-1] != -lv, axis=1))  # no row is a mirror image
+    assert np.mean(lv[:, ::-1] != -lv) > 0.5
+    assert np.array_equal(a.codes, b.codes)
+    # the decode does not assume symmetry: the gather returns each level as stored
+    W = lut6.decode(a.codes, a.lut)
+    assert np.array_equal(W, lv[np.arange(128)[:, None], a.codes])
