@@ -48,6 +48,10 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk 
 METRIC = "LUT-GEMV effective HBM GB/s (% of peak) at batch 1; prefill GEMM TFLOP/s"
 
 
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +135,7 @@ def main():
         lut6_inputs[name] = inp
         w0 = fqm.Lut6Weights.from_codes(inp.codes, inp.lut, device=dev)
         lut6[name] = [w0] + [w0.clone() for _ in range(n_copies(w0) - 1)]
+        progress(f"LUT6 {name} weights: {len(lut6[name])} copies")
         for b in cfg["batches"]:
             key = f"lut6_{name}_b{b}"
             if not wanted(key):
@@ -170,6 +175,7 @@ def main():
         q0 = fqm.Lut4Weights.from_codes(inp.codes, inp.lut, device=dev)
         qcopies = [q0] + [q0.clone() for _ in range(n_copies(q0) - 1)]
         lut4[name] = qcopies
+        progress(f"LUT4 {name} weights: {len(qcopies)} copies")
         for b, key in zip(cfg["batches"], keys):
             if not wanted(key):
                 continue
@@ -246,6 +252,7 @@ def main():
 
     order = list(rows)
     stream = torch.cuda.current_stream()
+    progress(f"inputs ready in {t_gen:.1f} s; warm-up, graph capture and timed replays of {len(order)} rows")
 
     # Warm-up: W passes over every row.
     for s in range(args.warmup):
@@ -321,6 +328,7 @@ def main():
                     bytes_per_launch={k: res[k]["bytes"] for k in b1},
                     us_per_launch={k: round(res[k]["us_per_call"], 3) for k in b1})
 
+    progress("timed replays done; streaming-read ceiling")
     ceiling = stream_read_ceiling(K, args.warmup, args.rotate_gb, dev)
     if ceiling:
         roofline["stream_read_ceiling_gbs"] = ceiling["gbs"]
@@ -328,6 +336,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
+        progress("oracle CPU baseline")
         cpu = cpu_baseline(lut6_inputs, rows, res, fqm, bf16, dev)
     dense = None
     if not args.no_dense:
