@@ -6,6 +6,7 @@ synthetic input already resident in HBM:
   lut6_up_b1, lut6_down_b1   LUT6 GEMV, batch 1 (W 17408x5120 and 5120x17408)
   lut6_up_b8, lut6_down_b8   LUT6 GEMV, batch 8
   prefill                    LUT6 GEMM, X 2048x5120 times the up weights
+  prefill_down               LUT6 GEMM, X 2048x17408 times the down weights (5120x17408)
   lut4_up_b1, lut4_down_b1   LUT4 GEMV, batch 1, the same two shapes
   lut4_up_b8, lut4_down_b8   LUT4 GEMV, batch 8
   lut4_prefill               LUT4 GEMM, X 2048x5120 times the LUT4 up weights
@@ -129,7 +130,7 @@ def main():
     lut6_inputs = {}
     for name in ("up", "down"):
         cfg = C[f"lut6_{name}"]
-        if not wanted(f"lut6_{name}_b1", f"lut6_{name}_b8", "prefill" if name == "up" else "-"):
+        if not wanted(f"lut6_{name}_b1", f"lut6_{name}_b8", "prefill" if name == "up" else "prefill_down"):
             continue
         inp = synth.lut6_input(cfg["rows"], cfg["cols"], cfg["seed"])
         lut6_inputs[name] = inp
@@ -163,6 +164,19 @@ def main():
             fn=lambda s, ws=ws, X=X, Y=Y, gws=gws: fqm.gemm(ws[(s + 1) % len(ws)], X, Y=Y, workspace=gws),
             bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * Kc,
             bound="mfma", kernel="lut6_gemm (with its K-split last round and reduction)")
+
+    if wanted("prefill_down"):
+        M = C["prefill"]["M"]
+        ws = lut6["down"]
+        Kc, Nn = C["lut6_down"]["cols"], C["lut6_down"]["rows"]
+        X = bf16(synth.activations(M, Kc, C["prefill"]["seed"]))
+        Y = torch.empty((M, Nn), dtype=torch.bfloat16, device=dev)
+        gws_bytes = fqm.gemm_workspace_size(ws[0], M)
+        gws = torch.empty(gws_bytes, dtype=torch.uint8, device=dev) if gws_bytes else None
+        rows["prefill_down"] = dict(
+            fn=lambda s, ws=ws, X=X, Y=Y, gws=gws: fqm.gemm(ws[(s + 1) % len(ws)], X, Y=Y, workspace=gws),
+            bytes=ws[0].nbytes() + X.numel() * 2 + Y.numel() * 2, flops=2 * M * Nn * Kc,
+            bound="mfma", kernel="lut6_gemm on the down layer (every tile split along K, then reduced)")
 
     # ---- LUT4 weights (up, down shapes), batch 1 and 8, prefill on the up layer --
     lut4 = {}
@@ -356,6 +370,7 @@ def main():
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "prefill_gemm_tflops": round(res["prefill"]["tflops"], 1) if "prefill" in res else None,
         "prefill_frac_of_bf16_peak": round(res["prefill"]["frac_mfma"], 4) if "prefill" in res else None,
+        "prefill_down_gemm_tflops": round(res["prefill_down"]["tflops"], 1) if "prefill_down" in res else None,
         "roofline": roofline,
         "hbm_stream_read_ceiling": ceiling,
         "cpu_baseline": cpu,
@@ -386,8 +401,9 @@ def stream_read_ceiling(K, warmup, rotate_gb, dev, nbytes=69_120_000):
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def call(s):
-        rc = fn(bufs[s % n].data_ptr(), nbytes, sink.data_ptr(), 0xDEADBEEF, stream.cuda_stream)
+    def call(s):  # on the current stream (the capture stream while a graph is captured)
+        rc = fn(bufs[s % n].data_ptr(), nbytes, sink.data_ptr(), 0xDEADBEEF,
+                torch.cuda.current_stream().cuda_stream)
         if rc:
             raise RuntimeError(f"stream read launch failed ({rc})")
 

@@ -392,12 +392,18 @@ __global__ __launch_bounds__(256) void lut6_gemm_reduce(const float* __restrict_
 // Tile plan.  Whole rounds of tiles (one per resident workgroup: one per
 // compute unit for 256-row tiles, two for 64-row tiles)
 // run as one launch.  The N tiles left for a last, partial round are split
-// along K (ksplit parts of at least MIN_SPLIT_STEPS steps; at most
+// along K into ksplit parts (of at least MIN_SPLIT_STEPS steps; at most
 // MAX_SPLIT_SMALL parts for 64-row tiles, whose fp32 partials would
-// otherwise outweigh the weights) so that they occupy the chip, and their
-// fp32 partial tiles are reduced afterwards.
+// otherwise outweigh the weights) and their fp32 partial tiles are reduced
+// afterwards.  ksplit minimises the last round's length in K steps,
+// ceil(tail * k / slots) * ceil(steps / k): for 32 tail tiles of 80 steps on
+// 256 slots that is 8 parts (one round of 10 steps); for 160 tiles of 272
+// steps (the 5120 x 17408 layer at 2048 rows) 3 parts, two rounds of 91
+// steps instead of one round of 272 on 160 of the 256 compute units.  Ties
+// take the fewer parts, and the partials are capped at MAX_SPLIT_BYTES.
 constexpr int MIN_SPLIT_STEPS = 8;
 constexpr int MAX_SPLIT_SMALL = 4;
+constexpr int64_t MAX_SPLIT_BYTES = (int64_t)256 << 20;
 constexpr int64_t SMALL_M_MAX = 64;  // M up to this takes 64-row tiles (measured: faster up to 64 rows, slower at 128 and 256)
 
 struct GemmPlan {
@@ -420,8 +426,15 @@ GemmPlan gemm_plan(int64_t rows, int64_t cols, int64_t M, int cus) {
     if (tiles % slots == 0) return p;
     const int nt_main = (int)((tiles / slots) * slots / p.mtiles);
     const int64_t tail = (int64_t)(p.ntiles - nt_main) * p.mtiles;
-    int64_t ksplit = std::min<int64_t>(slots / tail, cols / BK / MIN_SPLIT_STEPS);
-    if (small) ksplit = std::min<int64_t>(ksplit, MAX_SPLIT_SMALL);
+    const int64_t steps = cols / BK;
+    int64_t kmax = steps / MIN_SPLIT_STEPS;
+    if (small) kmax = std::min<int64_t>(kmax, MAX_SPLIT_SMALL);
+    int64_t ksplit = 1, best = ((tail + slots - 1) / slots) * steps;
+    for (int64_t k = 2; k <= kmax; ++k) {
+        if (tail * k * p.bm * BN * (int64_t)sizeof(float) > MAX_SPLIT_BYTES) break;
+        const int64_t len = ((tail * k + slots - 1) / slots) * ((steps + k - 1) / k);
+        if (len < best) best = len, ksplit = k;
+    }
     if (ksplit < 2) return p;
     p.nt_main = nt_main;
     p.ksplit = (int)ksplit;

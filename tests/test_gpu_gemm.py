@@ -67,8 +67,10 @@ def _plan_ws(rows, cols, M):
     """Workspace rule of the tile plan: tiles are 256 rows of X tall (64 when
     M <= 64) and 256 columns wide; whole rounds of tiles (one per compute unit,
     two per compute unit for 64-row tiles) run directly; the N tiles of a
-    last partial round split K into min(slots // tail tiles, steps // 8) parts
-    (at most 4 for 64-row tiles; split only when >= 2) of fp32 tiles."""
+    last partial round split K into the k parts (2 <= k <= steps // 8, at most
+    4 for 64-row tiles, partials at most 256 MB) that minimise
+    ceil(tail k / slots) * ceil(steps / k), fewer parts on ties, and only when
+    that beats ceil(tail / slots) * steps; fp32 partial tiles."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     small = M <= 64
     bm = 64 if small else 256
@@ -79,10 +81,16 @@ def _plan_ws(rows, cols, M):
         return 0
     nt_main = (tiles // slots) * slots // mt
     tail = (nt - nt_main) * mt
-    ks = min(slots // tail, cols // 64 // 8)
-    if small:
-        ks = min(ks, 4)
-    return tail * ks * bm * 256 * 4 if ks >= 2 else 0
+    steps = cols // 64
+    kmax = min(steps // 8, 4) if small else steps // 8
+    best_k, best = 1, -(-tail // slots) * steps
+    for k in range(2, kmax + 1):
+        if tail * k * bm * 256 * 4 > 256 << 20:
+            break
+        length = -(-tail * k // slots) * -(-steps // k)
+        if length < best:
+            best_k, best = k, length
+    return tail * best_k * bm * 256 * 4 if best_k >= 2 else 0
 
 
 @pytest.mark.parametrize("M", [1, 2, 8, 16])
@@ -115,7 +123,8 @@ def test_gemm_small_m_missing_workspace_is_an_error():
 
 
 @pytest.mark.parametrize("rows,cols,M", [(520, 1088, 300), (17408, 5120, 2048), (300, 128, 50),
-                                         (5120, 17408, 77), (17408, 5120, 64), (5120, 17408, 33)])
+                                         (5120, 17408, 77), (17408, 5120, 64), (5120, 17408, 33),
+                                         (5120, 17408, 2048), (2560, 17408, 1024)])
 def test_gemm_workspace_rule(rows, cols, M):
     w = lut6_weights(256, cols, 1)
     w.desc.rows = rows  # the rule reads the shape only (no launch)
@@ -146,3 +155,27 @@ def test_gemm_unsplit_short_k(rows, cols, M):
     torch.cuda.synchronize()
     assert canaries_intact(buf)
     assert_close(to_f64(Y), oracle.lut6.gemm(packed, inp.lut, X, cols), "bf16", f"rows={rows}")
+
+
+@pytest.mark.parametrize("M", [2048, 1500])
+def test_gemm_down_shape_sampled(M):
+    """The down layer (5120 x 17408, K = 17408) at a prefill's 2048 rows (and a
+    ragged 1500): 8 x 20 tiles of 256 x 256, fewer than the compute units, so
+    every tile is split along K (three parts at 2048 rows) and reduced; 40
+    sampled rows of X against the oracle."""
+    rows, cols, seed = 5120, 17408, 3
+    inp, packed = lut6_case(rows, cols, seed)
+    w = lut6_weights(rows, cols, seed)
+    need = fqm.gemm_workspace_size(w, M)
+    assert need == _plan_ws(rows, cols, M) > 0
+    X = synth.activations(M, cols, 44)
+    print(f"gemm down shape {M}x{rows}x{cols} workspace {need}", flush=True)
+    buf, Y = guarded((M, rows), torch.bfloat16)
+    fqm.gemm(w, bf16_dev(X), Y=Y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    pick = np.random.default_rng(M).choice(M, size=40, replace=False)
+    pick[:2] = [0, M - 1]
+    W = oracle.lut6.decode(inp.codes, inp.lut)
+    yo = oracle.numerics.bf16_to_f64(X[pick]) @ W.T
+    assert_close(to_f64(Y)[pick], yo, "bf16", f"down M={M}")
