@@ -7,7 +7,8 @@ device memory and the current HIP stream; the functions take and return
 is not built, importing works but every call raises ``FqmNotBuilt``.
 
 Functions mirror the C ABI names: ``pack_bits``, ``pack``, ``unpack``,
-``dequant``, ``workspace_size``, ``gemv``, ``gemm_workspace_size``, ``gemm``, ``version``,
+``dequant``, ``workspace_size``, ``gemv``, ``gemv_static``, ``gemm_workspace_size``, ``gemm``,
+``version``,
 ``status_str``.  Weight descriptors are built with ``Lut6Weights``,
 ``FabqWeights`` and ``MdbfWeights``; their ``from_*`` constructors upload
 unpacked host arrays and pack them on the GPU with ``fqm_pack_bits``.
@@ -28,13 +29,15 @@ FQM_BF16, FQM_F32 = 0, 1
 
 __all__ = [
     "FqmError", "FqmNotBuilt", "load", "version", "status_str", "pack_bits", "pack",
-    "unpack", "dequant", "workspace_size", "gemv", "gemm_workspace_size", "gemm", "Lut6Weights", "Lut4Weights", "FabqWeights",
+    "unpack", "dequant", "workspace_size", "gemv", "gemv_static", "gemm_workspace_size", "gemm", "Lut6Weights", "Lut4Weights", "FabqWeights",
     "MdbfWeights", "SYMBOLS",
 ]
 
 # Every symbol include/fqm.h declares.
 SYMBOLS = ("fqm_version", "fqm_status_str", "fqm_pack_bits", "fqm_pack", "fqm_unpack",
-           "fqm_dequant", "fqm_workspace_size", "fqm_gemv", "fqm_gemm_workspace_size", "fqm_gemm")
+           "fqm_dequant", "fqm_workspace_size", "fqm_gemv", "fqm_gemv_static",
+           "fqm_gemm_workspace_size", "fqm_gemm")
+STATIC_SCRATCH_BYTES = 16 << 20  # FQM_STATIC_SCRATCH_BYTES
 
 
 class FqmError(RuntimeError):
@@ -110,6 +113,8 @@ def load():
     lib.fqm_gemv.restype = c_int32
     lib.fqm_gemv.argtypes = [P(_Weights), c_void_p, c_void_p, c_int32, c_int32, c_void_p,
                              ctypes.c_size_t, c_void_p]
+    lib.fqm_gemv_static.restype = c_int32
+    lib.fqm_gemv_static.argtypes = [P(_Weights), c_void_p, c_void_p, c_int32, c_int32, c_void_p]
     lib.fqm_gemm.restype = c_int32
     lib.fqm_gemm.argtypes = [P(_Weights), c_void_p, c_void_p, c_int64, c_void_p, ctypes.c_size_t, c_void_p]
     lib.fqm_gemm_workspace_size.restype = ctypes.c_size_t
@@ -443,6 +448,31 @@ def gemv(w: _WeightsBase, x: torch.Tensor, y: torch.Tensor | None = None,
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().fqm_gemv(w.ref, _ptr(x), _ptr(y), ydt, batch, _ptr(workspace), ws_bytes,
                            _stream(stream)), "fqm_gemv")
+    return y
+
+
+def gemv_static(w: _WeightsBase, x: torch.Tensor, y: torch.Tensor | None = None,
+                out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """``gemv`` through ``fqm_gemv_static``: no workspace; the library's
+    per-GPU static scratch stands in for it (calls overlapping on one GPU
+    race).  With ``y`` given, nothing is allocated."""
+    if not isinstance(x, torch.Tensor):
+        raise ValueError("x must be a torch.Tensor")
+    if x.dim() == 1:
+        x = x[None]
+    if x.dim() != 2:
+        raise ValueError(f"x must be [batch][cols]; got shape {tuple(x.shape)}")
+    batch = x.shape[0]
+    dev = _weights_device(w)
+    _check_operand(x, "x", (batch, w.cols), (torch.bfloat16,), dev)
+    if y is None:
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError(f"out_dtype must be bfloat16 or float32, not {out_dtype}")
+        y = torch.empty((batch, w.rows), dtype=out_dtype, device=x.device)
+    _check_operand(y, "y", (batch, w.rows), (torch.bfloat16, torch.float32), dev)
+    ydt = FQM_F32 if y.dtype == torch.float32 else FQM_BF16
+    _check(load().fqm_gemv_static(w.ref, _ptr(x), _ptr(y), ydt, batch, _stream(stream)),
+           "fqm_gemv_static")
     return y
 
 

@@ -2,13 +2,47 @@
 // Nothing here allocates, synchronises or keeps state between calls.
 #include <string.h>
 
+#include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "fqm_internal.h"
 
 using namespace fqm;
 
 namespace {
+
+// ---- the static scratch of fqm_gemv_static ----------------------------------
+// One array per GPU the library runs on, held until the process ends.  Host
+// code never uses the array's name as an address (on the host it is only a
+// stand-in): each device's address is looked up once, with that device
+// current, and kept in scratch_addr.
+__device__ __align__(256) uint8_t scratch[FQM_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_mu;
+
+// The current device's copy of `scratch`.
+hipError_t scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool ld_ok(int64_t ld, int64_t need) { return ld >= need && (ld & 15) == 0; }
@@ -105,6 +139,7 @@ const char* fqm_status_str(int32_t status) {
         case FQM_E_WORKSPACE: return "workspace missing or too small";
         case FQM_E_UNSUPPORTED: return "combination not supported";
         case FQM_E_HIP: return "HIP launch failed";
+        case FQM_E_SCRATCH: return "needs more scratch than fqm_gemv_static's static maximum";
         default: return "unknown status";
     }
 }
@@ -194,6 +229,18 @@ fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_
         }
     }
     return FQM_E_FORMAT;
+}
+
+fqm_status fqm_gemv_static(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
+                           int32_t batch, void* stream) {
+    const fqm_status st = check_weights(w);
+    if (st != FQM_OK) return st;
+    if (batch < 1 || batch > 16) return FQM_E_SHAPE;
+    const size_t need = fqm_workspace_size(w, batch);
+    if (need > FQM_STATIC_SCRATCH_BYTES) return FQM_E_SCRATCH;
+    void* ws = nullptr;
+    if (need && scratch_for_current_device(&ws) != hipSuccess) return FQM_E_HIP;
+    return fqm_gemv(w, x, y, y_dtype, batch, ws, need, stream);
 }
 
 // Up to 16 rows of X go to the GEMV kernels when they have a tuned kernel

@@ -47,9 +47,10 @@
  *   - Ownership: the caller allocates and frees every buffer.  All tensor
  *     pointers are DEVICE pointers unless stated otherwise; descriptor
  *     structs (fqm_weights) are HOST memory and are read during the call
- *     only.  The library allocates nothing, frees nothing, keeps no pointer
- *     after returning and holds no mutable global state; calls on different
- *     streams may run concurrently.
+ *     only.  The library allocates nothing, frees nothing and keeps no
+ *     pointer after returning; calls on different streams may run
+ *     concurrently.  The one piece of global state is the per-GPU static
+ *     scratch array of fqm_gemv_static (see there).
  *   - Ordering: every call only enqueues work on `stream` (a hipStream_t
  *     passed as void*, NULL = the null stream) and returns; inputs must stay
  *     valid and unmodified, and outputs unread, until the stream passes the
@@ -75,7 +76,10 @@
 extern "C" {
 #endif
 
-#define FQM_VERSION 2
+#define FQM_VERSION 3
+
+/* Bytes of the device scratch array fqm_gemv_static uses on each GPU. */
+#define FQM_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
 
 typedef enum fqm_status {
     FQM_OK = 0,
@@ -85,7 +89,8 @@ typedef enum fqm_status {
     FQM_E_FORMAT = 4,      /* unknown format tag or format parameter out of range */
     FQM_E_WORKSPACE = 5,   /* workspace missing or smaller than fqm_workspace_size */
     FQM_E_UNSUPPORTED = 6, /* valid request this build does not implement */
-    FQM_E_HIP = 7          /* a HIP launch failed */
+    FQM_E_HIP = 7,         /* a HIP launch failed */
+    FQM_E_SCRATCH = 8      /* fqm_gemv_static: needs more than FQM_STATIC_SCRATCH_BYTES */
 } fqm_status;
 
 enum fqm_format { FQM_LUT6 = 1, FQM_FABQ = 2, FQM_MDBF = 3, FQM_LUT4 = 4 };
@@ -213,6 +218,25 @@ size_t fqm_workspace_size(const fqm_weights* w, int32_t batch);
  * above; every decoded weight stays in fp32 (never rounded to bf16). */
 fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
                     int32_t batch, void* workspace, size_t ws_bytes, void* stream);
+
+/* fqm_gemv without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The same kernels and results as fqm_gemv (bit for
+ * bit); where fqm_gemv would use the caller's workspace, this call uses a
+ * static device array of FQM_STATIC_SCRATCH_BYTES (16 MiB) that the library
+ * holds on each GPU it runs on until the process ends.  The array of the
+ * current device (hipGetDevice) is used, so `stream` must belong to that
+ * device; its address is looked up on the first call on each device that
+ * needs scratch.  Nothing is allocated, freed or cleared (the kernels need no
+ * zeroed scratch: every word they read they first write in the same call).
+ * Calls that overlap on one GPU (concurrent streams, host threads, or graph
+ * replays in flight together) share the array and RACE: serialise them.
+ * Returns FQM_E_SCRATCH, enqueuing nothing, when fqm_workspace_size(w,
+ * batch) exceeds FQM_STATIC_SCRATCH_BYTES (for example MDBF with many
+ * envelopes at large batch on the 27B-class MLP shapes); FQM_E_HIP if the
+ * address lookup fails; otherwise as fqm_gemv. */
+fqm_status fqm_gemv_static(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
+                           int32_t batch, void* stream);
 
 /* Bytes of device workspace fqm_gemm needs for this LUT6 or LUT4 descriptor and M on
  * the current device: for M <= 16 on a shape the GEMV kernels cover (batch 1:

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert decl == set(fqm.SYMBOLS)
     for name in decl:
         assert hasattr(lib, name), name
-    assert lib.fqm_version() == 2
+    assert lib.fqm_version() == 3
 
 
 def test_status_strings(lib):
@@ -288,3 +288,22 @@ def test_fabq_row_map_must_be_a_permutation(row_of):
                                     np.zeros((3, cols), np.uint8), np.zeros((3, 1), np.uint16),
                                     np.zeros((3, 1), np.uint8), np.zeros(16, np.uint16),
                                     device="cpu")
+
+
+def test_gemv_static_rejects_more_than_its_scratch(lib):
+    """fqm_gemv_static refuses, before any device call, a request whose
+    workspace exceeds the static array (16 MiB): MDBF with 16 envelopes and
+    two paths at batch 16 on the 5120 x 17408 shape needs 88 MB."""
+    w = fqm._Weights()
+    w.format, w.rows, w.cols = fqm.FQM_MDBF, 5120, 17408
+    w.mdbf.r, w.mdbf.l, w.mdbf.P = 4096, 16, 2
+    for p in range(2):
+        q = w.mdbf.path[p]
+        q.S_A, q.ld_A, q.S_B, q.ld_B = FAKE, 512, FAKE, 2176
+        q.A_amp = q.B_amp = q.Q_U = q.Q_V = FAKE
+    need = lib.fqm_workspace_size(ctypes.byref(w), 16)
+    assert need == 128 * 2 * 16 * (17408 + 4096) > fqm.STATIC_SCRATCH_BYTES
+    rc = lib.fqm_gemv_static(ctypes.byref(w), FAKE, FAKE, 0, 16, None)
+    assert rc == 8 and lib.fqm_status_str(rc).startswith(b"needs more scratch")
+    assert lib.fqm_gemv_static(ctypes.byref(w), FAKE, FAKE, 0, 17, None) == E["SHAPE"]
+    assert lib.fqm_gemv_static(None, FAKE, FAKE, 0, 1, None) == E["NULL"]
