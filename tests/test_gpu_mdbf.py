@@ -94,3 +94,45 @@ def test_mlp_shapes_more_envelopes_and_paths(n, m, l, P, batch):
     torch.cuda.synchronize()
     assert canaries_intact(buf)
     assert_close(to_f64(y), oracle.mdbf.gemv_factored(paths, x, n, m, r), "f32", f"{n}x{m} l={l} P={P}")
+
+
+def test_workspace_contents_and_repeated_calls():
+    """The workspace's contents on entry do not matter: a workspace full of
+    0xFF bytes, and the same workspace reused call after call, give the same
+    bits (every operand word is written before it is read)."""
+    inp, paths = case(4096, 4096, 2000, 2, 1, 6)
+    w = weights(inp)
+    x = bf16_dev(synth.activations(16, 4096, 12))
+    need = fqm.workspace_size(w, 16)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+    y0 = fqm.gemv(w, x, out_dtype=torch.float32, workspace=ws)
+    for _ in range(3):
+        y1 = fqm.gemv(w, x, out_dtype=torch.float32, workspace=ws)
+        assert torch.equal(y0, y1)
+    yo = oracle.mdbf.gemv_factored(paths, synth.activations(16, 4096, 12), 4096, 4096, 2000)
+    assert_close(to_f64(y0), yo, "f32", "garbage workspace")
+
+
+def test_graph_replays_match_eager():
+    """Captured in a HIP graph and replayed several times, with eager work in
+    between, every replay gives the eager result."""
+    inp, paths = case(4096, 4096, 2000, 2, 1, 6)
+    w = weights(inp)
+    xs = [bf16_dev(synth.activations(1, 4096, 20 + i)) for i in range(3)]
+    x = xs[0].clone()
+    need = fqm.workspace_size(w, 1)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    y = torch.empty((1, 4096), dtype=torch.float32, device=DEV)
+    fqm.gemv(w, x, y=y, workspace=ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fqm.gemv(w, x, y=y, workspace=ws)
+    for xi in xs:
+        x.copy_(xi)
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        eager = fqm.gemv(w, xi, out_dtype=torch.float32)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager)
