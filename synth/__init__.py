@@ -223,8 +223,13 @@ class FabqInput:
     signs: np.ndarray       # uint8 [n_lo][cols], 1 -> +1, 0 -> -1
     s_blk: np.ndarray       # uint16 fp16 bits [n_lo][cols/bs]
     idx: np.ndarray         # uint8 [n_lo][cols/bs], 0..15
-    codebook: np.ndarray    # uint16 fp16 bits [16]
+    codebook: np.ndarray    # uint16 fp16 bits: [16] (cb_mode 0) or [4][64] (cb_mode 1)
     seed: int
+    hi_bits: int = 4        # 4 or 8: width of the high-precision rows' values (q4 holds them)
+    cb_mode: int = 0        # 0 scalar 16, 1 tiered scalar 4 x 64, 2 tiered vector 4 x 64 x 128
+    cb_base: int = 0        # first of the 16 active centroids of each tier (modes 1, 2)
+    tier: np.ndarray | None = None       # uint8 [n_lo]: tier 0..3 of each binary row (modes 1, 2)
+    vcodebook: np.ndarray | None = None  # float32 [4][64][128] (mode 2)
 
 
 def fabq_blocksize_draw(seed: int) -> int:
@@ -234,7 +239,8 @@ def fabq_blocksize_draw(seed: int) -> int:
 
 
 def fabq_input(rows: int, cols: int, seed: int, blocksize: int | None = None,
-               hi_frac: float = 0.05, n_codes: int = 16) -> FabqInput:
+               hi_frac: float = 0.05, n_codes: int = 16, hi_bits: int = 4, cb_mode: int = 0,
+               cb_base: int | None = None) -> FabqInput:
     """Gaussian rows (per-row sigma as for the LUT rows); seeded importance.
 
     * importance ~ U(0,1) per output row; the top ``hi_frac`` rows are int4:
@@ -246,33 +252,56 @@ def fabq_input(rows: int, cols: int, seed: int, blocksize: int | None = None,
       (i + 1/2)/16 quantiles, run until assignments stop changing (<= 100
       iterations; an empty cluster keeps its centroid), rounded to fp16;
       idx_b = nearest fp16 centroid (ties to the lower index).
+    * ``hi_bits`` = 8: s_r = fp16(max|w_r| / 127), q = clip(rint(w / s_r), -128, 127).
+    * ``cb_mode`` 1 / 2 (tiered codebooks): see ``fabq_quantize``; ``cb_base``
+      is a seeded draw from {0, 16, 32, 48} (stream [seed, 3]) unless given.
     """
     bs = fabq_blocksize_draw(seed) if blocksize is None else int(blocksize)
     rng = np.random.default_rng(seed)
     sigma = np.exp(rng.uniform(math.log(0.005), math.log(0.05), size=rows))
     w = rng.standard_normal((rows, cols)) * sigma[:, None]
     importance = rng.uniform(size=rows)
-    return fabq_quantize(w, importance, bs, hi_frac=hi_frac, n_codes=n_codes, seed=seed)
+    if cb_base is None:
+        cb_base = 16 * int(np.random.default_rng([seed, 3]).integers(0, 4))
+    return fabq_quantize(w, importance, bs, hi_frac=hi_frac, n_codes=n_codes, seed=seed,
+                         hi_bits=hi_bits, cb_mode=cb_mode, cb_base=cb_base)
 
 
 def fabq_quantize(w: np.ndarray, importance: np.ndarray, bs: int, hi_frac: float = 0.05,
-                  n_codes: int = 16, seed: int = -1) -> FabqInput:
-    """Quantizer-side construction of the stored tensors from fp64 weights."""
+                  n_codes: int = 16, seed: int = -1, hi_bits: int = 4, cb_mode: int = 0,
+                  cb_base: int = 0) -> FabqInput:
+    """Quantizer-side construction of the stored tensors from fp64 weights.
+
+    Tiered codebooks (cb_mode 1, 2): a binary row's tier is the quartile of
+    its importance among the binary rows (0 = least important).  Each tier's
+    codebook has 64 entries; the layer's 16 sit at [cb_base, cb_base + 16)
+    and the other 48 (other layers' centroids) are seeded stand-ins
+    (stream [seed, 7]).  cb_mode 1: the layer's 16 fp16 centroids of a tier
+    are the 1-D Lloyd k-means of that tier's block residual means; idx_b =
+    nearest of them.  cb_mode 2: they are 128-float vectors, the k-means
+    (6 Lloyd rounds from 16 seeded windows, stream [seed, 8]) of the tier's
+    rows' residuals w - s_b * sign over whole 128-column windows; idx_b = the
+    centroid whose elements k mod 128 best match the block's residuals
+    (least squares; ties to the lower index).
+    """
     rows, cols = w.shape
     if cols % bs:
         raise ValueError("blocksize must divide cols")
+    if hi_bits not in (4, 8) or cb_mode not in (0, 1, 2) or cb_base not in (0, 16, 32, 48):
+        raise ValueError("hi_bits in {4, 8}, cb_mode in {0, 1, 2}, cb_base in {0, 16, 32, 48}")
     n_hi = int(round(hi_frac * rows))
     order = np.argsort(-np.asarray(importance), kind="stable")
     hi_rows = np.sort(order[:n_hi])
     lo_rows = np.sort(order[n_hi:])
     row_of = np.concatenate([hi_rows, lo_rows]).astype(np.int32)
 
+    qmax = (1 << (hi_bits - 1)) - 1
     wh = w[hi_rows]
-    s_hi = fp16_bits_from_f64(np.abs(wh).max(axis=1) / 7.0)
+    s_hi = fp16_bits_from_f64(np.abs(wh).max(axis=1) / qmax)
     s_hi_v = s_hi.view(np.float16).astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.where(s_hi_v[:, None] > 0, np.rint(wh / s_hi_v[:, None]), 0.0)
-    q4 = np.clip(q, -8, 7).astype(np.int8)
+    q4 = np.clip(q, -qmax - 1, qmax).astype(np.int8)
 
     wl = w[lo_rows]
     nb = cols // bs
@@ -282,14 +311,68 @@ def fabq_quantize(w: np.ndarray, importance: np.ndarray, bs: int, hi_frac: float
     pos = wb >= 0
     pm1 = np.where(pos, 1.0, -1.0)
     mu = (wb - s_blk_v[:, :, None] * pm1).mean(axis=2)
-    codebook = _lloyd_1d(mu.ravel(), n_codes) if mu.size else np.zeros(n_codes)
-    cb_bits = fp16_bits_from_f64(codebook)
-    cb_v = cb_bits.view(np.float16).astype(np.float64)
-    idx = np.argmin(np.abs(mu[:, :, None] - cb_v[None, None, :]), axis=2).astype(np.uint8)
     signs = pos.reshape(len(lo_rows), cols).astype(np.uint8)
-    return FabqInput(rows=rows, cols=cols, blocksize=bs, row_of=row_of, n_hi=n_hi,
-                     q4=q4, s_hi=s_hi, signs=signs, s_blk=s_blk, idx=idx,
-                     codebook=cb_bits, seed=seed)
+    common = dict(rows=rows, cols=cols, blocksize=bs, row_of=row_of, n_hi=n_hi, q4=q4, s_hi=s_hi,
+                  signs=signs, s_blk=s_blk, seed=seed, hi_bits=hi_bits)
+    if cb_mode == 0:
+        codebook = _lloyd_1d(mu.ravel(), n_codes) if mu.size else np.zeros(n_codes)
+        cb_bits = fp16_bits_from_f64(codebook)
+        cb_v = cb_bits.view(np.float16).astype(np.float64)
+        idx = np.argmin(np.abs(mu[:, :, None] - cb_v[None, None, :]), axis=2).astype(np.uint8)
+        return FabqInput(idx=idx, codebook=cb_bits, **common)
+
+    n_lo = len(lo_rows)
+    rank = np.empty(n_lo, np.int64)
+    rank[np.argsort(np.asarray(importance)[lo_rows], kind="stable")] = np.arange(n_lo)
+    tier = (rank * 4 // max(n_lo, 1)).astype(np.uint8)
+    spread = float(np.std(mu)) if mu.size else 1e-3
+    filler = np.random.default_rng([seed, 7]).standard_normal((4, 64)) * spread
+    idx = np.zeros((n_lo, nb), np.uint8)
+    if cb_mode == 1:
+        C = filler.copy()
+        for t in range(4):
+            sel = tier == t
+            if sel.any():
+                C[t, cb_base:cb_base + 16] = _lloyd_1d(mu[sel].ravel(), 16)
+        cb_bits = fp16_bits_from_f64(C).reshape(4, 64)
+        Cv = cb_bits.view(np.float16).astype(np.float64)
+        for t in range(4):
+            sel = tier == t
+            act = Cv[t, cb_base:cb_base + 16]
+            idx[sel] = np.argmin(np.abs(mu[sel][:, :, None] - act[None, None, :]), axis=2)
+        return FabqInput(idx=idx, codebook=cb_bits, cb_mode=1, cb_base=cb_base, tier=tier, **common)
+
+    resid = wl - np.repeat(s_blk_v, bs, axis=1) * np.where(pos.reshape(n_lo, cols), 1.0, -1.0)
+    V = np.repeat(filler[:, :, None], 128, axis=2) * 0.5
+    nwin = cols // 128
+    krng = np.random.default_rng([seed, 8])
+    kcol = np.arange(cols) % 128
+    for t in range(4):
+        sel = np.flatnonzero(tier == t)
+        if len(sel) == 0 or nwin == 0:
+            continue
+        X = resid[sel, :nwin * 128].reshape(-1, 128)
+        cent = X[krng.choice(len(X), size=16, replace=len(X) < 16)].copy()
+        for _ in range(6):
+            d = (X * X).sum(1)[:, None] - 2 * X @ cent.T + (cent * cent).sum(1)[None, :]
+            a = np.argmin(d, axis=1)
+            for c in range(16):
+                if (a == c).any():
+                    cent[c] = X[a == c].mean(axis=0)
+        V[t, cb_base:cb_base + 16] = cent
+    V = V.astype(np.float32)
+    for t in range(4):
+        sel = np.flatnonzero(tier == t)
+        if len(sel) == 0:
+            continue
+        act = V[t, cb_base:cb_base + 16].astype(np.float64)[:, kcol]            # [16][cols]
+        Rb = resid[sel].reshape(len(sel), nb, bs)
+        Ab = act.reshape(16, nb, bs)
+        d = ((Rb[:, None, :, :] - Ab[None, :, :, :]) ** 2).sum(axis=3)          # [n][16][nb]
+        idx[sel] = np.argmin(d, axis=1)
+    cb_bits = fp16_bits_from_f64(np.zeros(16))
+    return FabqInput(idx=idx, codebook=cb_bits, cb_mode=2, cb_base=cb_base, tier=tier, vcodebook=V,
+                     **common)
 
 
 def _lloyd_1d(v: np.ndarray, k: int, max_iter: int = 100) -> np.ndarray:
