@@ -11,6 +11,9 @@ synthetic input already resident in HBM:
   lut4_up_b8, lut4_down_b8   LUT4 GEMV, batch 8
   lut4_prefill               LUT4 GEMM, X 2048x5120 times the LUT4 up weights
   fabq_b1, fabq_b8           FABQ-RC-style GEMV, 5120x5120, the layer's drawn blocksize
+  fabq_int8_b1, fabq_bs16_b1 the same layer with int8 high rows / 16-column blocks
+  fabq_tiered_b1/_b8         ... with tiered codebooks (4 x 64 fp16 centroids, 16 active)
+  fabq_vector_b1/_b8         ... with 128-float vector centroids (4 x 64 x 128 fp32)
   mdbf_b1, mdbf_b16          MDBF GEMV, n = m = 4096, r = 2000, l = 2, P = 1
   mdbf_up_b1, mdbf_down_b1   MDBF GEMV on the MLP shapes (17408x5120, 5120x17408), r = 3913 (1 bpw)
 
@@ -237,6 +240,30 @@ def main():
                              bytes=fcopies[0].nbytes() + x.numel() * 2 + y.numel() * 2,
                              flops=2 * b * cfg["rows"] * cfg["cols"], bound="alu",
                              kernel=f"fabq_gemv batch {b}")
+
+    # ---- FABQ variants on the same layer: int8 high rows, 16-column blocks,
+    # tiered codebooks (4 x 64 fp16) and 128-float vector centroids -------------
+    for key, kw, batches in (("fabq_int8", dict(hi_bits=8), (1,)),
+                             ("fabq_bs16", dict(blocksize=16), (1,)),
+                             ("fabq_tiered", dict(cb_mode=1), (1, 8)),
+                             ("fabq_vector", dict(cb_mode=2), (1, 8))):
+        if not wanted(*[f"{key}_b{b}" for b in batches]):
+            continue
+        cfg = C["fabq"]
+        inp = synth.fabq_input(cfg["rows"], cfg["cols"], cfg["seed"], **kw)
+        f0 = fqm.FabqWeights.from_arrays(inp.rows, inp.cols, inp.blocksize, inp.n_hi, inp.row_of, inp.q4,
+                                         inp.s_hi, inp.signs, inp.s_blk, inp.idx, inp.codebook, device=dev,
+                                         hi_bits=inp.hi_bits, cb_mode=inp.cb_mode, cb_base=inp.cb_base,
+                                         tier=inp.tier, vcodebook=inp.vcodebook)
+        fcopies = [f0] + [f0.clone() for _ in range(n_copies(f0) - 1)]
+        for b in batches:
+            x = bf16(synth.activations(b, cfg["cols"], cfg["seed"]))
+            y = torch.empty((b, cfg["rows"]), dtype=torch.bfloat16, device=dev)
+            rows[f"{key}_b{b}"] = dict(
+                fn=lambda s, ws=fcopies, x=x, y=y: fqm.gemv(ws[s % len(ws)], x, y=y),
+                bytes=f0.nbytes() + x.numel() * 2 + y.numel() * 2,
+                flops=2 * b * cfg["rows"] * cfg["cols"], bound="alu",
+                kernel=f"fabq_gemv {key[5:]} (block {inp.blocksize}, int{inp.hi_bits} rows) batch {b}")
 
     # ---- MDBF (n = m = 4096, r = 2000, l = 2, P = 1; MLP shapes at 1 bpw) ---------
     for prefix in ("mdbf", "mdbf_up", "mdbf_down"):

@@ -25,6 +25,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfqm.so")
 
 FQM_LUT6, FQM_FABQ, FQM_MDBF, FQM_LUT4 = 1, 2, 3, 4
+FQM_CB_SCALAR16, FQM_CB_TIERED, FQM_CB_VECTOR = 0, 1, 2
 FQM_BF16, FQM_F32 = 0, 1
 
 __all__ = [
@@ -64,7 +65,9 @@ class _Fabq(ctypes.Structure):
     _fields_ = [("blocksize", c_int32), ("n_hi", c_int32), ("row_of", c_void_p),
                 ("q4", c_void_p), ("ld_q4", c_int64), ("s_hi", c_void_p),
                 ("signs", c_void_p), ("ld_signs", c_int64), ("s_blk", c_void_p),
-                ("idx", c_void_p), ("ld_idx", c_int64), ("codebook", c_void_p)]
+                ("idx", c_void_p), ("ld_idx", c_int64), ("codebook", c_void_p),
+                ("hi_bits", c_int32), ("cb_mode", c_int32), ("cb_base", c_int32),
+                ("tier", c_void_p), ("vcodebook", c_void_p)]
 
 
 class _MdbfPath(ctypes.Structure):
@@ -275,11 +278,13 @@ class FabqWeights(_WeightsBase):
     """FABQ-RC-style weights; see ``fqm_fabq`` in include/fqm.h for the layout."""
     fmt = FQM_FABQ
 
-    def __init__(self, rows, cols, blocksize, n_hi, row_of, q4, s_hi, signs, s_blk, idx, codebook):
+    def __init__(self, rows, cols, blocksize, n_hi, row_of, q4, s_hi, signs, s_blk, idx, codebook,
+                 hi_bits=4, cb_mode=FQM_CB_SCALAR16, cb_base=0, tier=None, vcodebook=None):
         super().__init__(rows, cols)
         self.blocksize, self.n_hi = int(blocksize), int(n_hi)
+        self.hi_bits, self.cb_mode, self.cb_base = int(hi_bits), int(cb_mode), int(cb_base)
         self.tensors = dict(row_of=row_of, q4=q4, s_hi=s_hi, signs=signs, s_blk=s_blk, idx=idx,
-                            codebook=codebook)
+                            codebook=codebook, tier=tier, vcodebook=vcodebook)
         f = self.desc.fabq
         f.blocksize, f.n_hi = self.blocksize, self.n_hi
         f.row_of = self._hold(row_of)
@@ -289,47 +294,71 @@ class FabqWeights(_WeightsBase):
         f.s_blk = self._hold(s_blk)
         f.idx, f.ld_idx = self._hold(idx), idx.shape[1]
         f.codebook = self._hold(codebook)
+        f.hi_bits, f.cb_mode, f.cb_base = self.hi_bits, self.cb_mode, self.cb_base
+        f.tier = self._hold(tier) if tier is not None else None
+        f.vcodebook = self._hold(vcodebook) if vcodebook is not None else None
 
     @classmethod
     def from_arrays(cls, rows, cols, blocksize, n_hi, row_of, q4, s_hi, signs, s_blk, idx,
-                    codebook, device="cuda"):
+                    codebook, device="cuda", hi_bits=4, cb_mode=FQM_CB_SCALAR16, cb_base=0,
+                    tier=None, vcodebook=None):
         """Unpacked host arrays (as the synthetic generator returns them) ->
-        device tensors, with q4 / signs / idx packed on the GPU."""
+        device tensors, with the high rows (hi_bits-wide fields), signs and
+        indices packed on the GPU.  codebook: [16] fp16 bits (scalar mode) or
+        [4][64] (tiered); tier: [rows - n_hi] 0..3 (tiered and vector modes);
+        vcodebook: [4][64][128] float32 (vector mode)."""
         n_lo = rows - n_hi
         nb = cols // blocksize
         ro = np.asarray(row_of).reshape(-1)
         if ro.shape != (rows,) or not np.array_equal(np.sort(ro), np.arange(rows)):
             raise ValueError("row_of must be a permutation of range(rows): each output row is "
                              "written by exactly one stored row")
-        q4_d = _dev((np.asarray(q4).astype(np.int16) & 15).astype(np.uint8).reshape(n_hi, cols),
-                    torch.uint8, device)
+        if hi_bits not in (4, 8) or cb_mode not in (0, 1, 2):
+            raise ValueError("hi_bits must be 4 or 8 and cb_mode 0, 1 or 2")
+        if cb_mode and (tier is None or np.asarray(tier).shape != (n_lo,)):
+            raise ValueError("the tiered codebook modes need one tier per binary row")
+        if cb_mode == FQM_CB_VECTOR and (vcodebook is None or np.asarray(vcodebook).size != 4 * 64 * 128):
+            raise ValueError("the vector codebook mode needs a [4][64][128] float32 vcodebook")
+        mask = (1 << hi_bits) - 1
+        q_d = _dev((np.asarray(q4).astype(np.int16) & mask).astype(np.uint8).reshape(n_hi, cols),
+                   torch.uint8, device)
         signs_d = _dev(np.asarray(signs, dtype=np.uint8).reshape(n_lo, cols), torch.uint8, device)
         idx_d = _dev(np.asarray(idx, dtype=np.uint8).reshape(n_lo, nb), torch.uint8, device)
-        q4_p = pack_bits(q4_d, 4, ld=max(16, _round16(cols // 2)))
+        q_p = pack_bits(q_d, hi_bits, ld=max(16, _round16(cols * hi_bits // 8)))
         signs_p = pack_bits(signs_d, 1, ld=max(16, _round16(cols // 8)))
         idx_p = pack_bits(idx_d, 4, ld=max(16, _round16((nb + 1) // 2)))
 
         def t16(a):
             return _dev(np.asarray(a, dtype=np.uint16).view(np.int16), torch.int16, device)
 
+        cb = np.asarray(codebook, dtype=np.uint16).reshape(-1)
+        tier_d = _dev(np.asarray(tier, dtype=np.uint8), torch.uint8, device) if cb_mode else None
+        v_d = (_dev(np.asarray(vcodebook, dtype=np.float32).reshape(4, 64, 128), torch.float32, device)
+               if cb_mode == FQM_CB_VECTOR else None)
         return cls(rows, cols, blocksize, n_hi,
                    _dev(np.asarray(row_of, dtype=np.int32), torch.int32, device),
-                   q4_p, t16(s_hi).view(torch.float16), signs_p,
+                   q_p, t16(s_hi).view(torch.float16), signs_p,
                    t16(np.asarray(s_blk).reshape(n_lo, nb)).view(torch.float16), idx_p,
-                   t16(codebook).view(torch.float16))
+                   t16(cb).view(torch.float16), hi_bits=hi_bits, cb_mode=cb_mode, cb_base=cb_base,
+                   tier=tier_d, vcodebook=v_d)
 
     def clone(self):
-        t = {k: v.clone() for k, v in self.tensors.items()}
+        t = {k: (v.clone() if v is not None else None) for k, v in self.tensors.items()}
         return FabqWeights(self.rows, self.cols, self.blocksize, self.n_hi, t["row_of"], t["q4"],
-                           t["s_hi"], t["signs"], t["s_blk"], t["idx"], t["codebook"])
+                           t["s_hi"], t["signs"], t["s_blk"], t["idx"], t["codebook"],
+                           hi_bits=self.hi_bits, cb_mode=self.cb_mode, cb_base=self.cb_base,
+                           tier=t["tier"], vcodebook=t["vcodebook"])
 
     def nbytes(self) -> int:
-        """Algorithmic bytes: int4 rows + scales, sign bits + block scales +
-        4-bit indices, codebook and row map (all unpadded)."""
+        """Algorithmic bytes: high rows + scales, sign bits + block scales +
+        4-bit indices, the codebook (16 or 4 x 64 fp16, or 4 x 64 x 128
+        fp32), tier bytes and the row map (all unpadded)."""
         n_lo = self.rows - self.n_hi
         nb = self.cols // self.blocksize
-        return (self.n_hi * self.cols // 2 + 2 * self.n_hi + n_lo * self.cols // 8
-                + n_lo * nb * 2 + (n_lo * nb + 1) // 2 + 32 + 4 * self.rows)
+        cb = {FQM_CB_SCALAR16: 32, FQM_CB_TIERED: 4 * 64 * 2, FQM_CB_VECTOR: 4 * 64 * 128 * 4}[self.cb_mode]
+        tier = n_lo if self.cb_mode else 0
+        return (self.n_hi * self.cols * self.hi_bits // 8 + 2 * self.n_hi + n_lo * self.cols // 8
+                + n_lo * nb * 2 + (n_lo * nb + 1) // 2 + cb + tier + 4 * self.rows)
 
 
 class MdbfWeights(_WeightsBase):

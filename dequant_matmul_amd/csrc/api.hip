@@ -77,24 +77,32 @@ fqm_status check_weights(const fqm_weights* w) {
         case FQM_FABQ: {
             const fqm_fabq& f = w->fabq;
             const int bs = f.blocksize;
-            if (bs != 64 && bs != 128 && bs != 256 && bs != 512) return FQM_E_FORMAT;
+            if (bs != 16 && bs != 32 && bs != 64 && bs != 128 && bs != 256 && bs != 512) return FQM_E_FORMAT;
+            if (f.hi_bits != 0 && f.hi_bits != 4 && f.hi_bits != 8) return FQM_E_FORMAT;
+            if (f.cb_mode < FQM_CB_SCALAR16 || f.cb_mode > FQM_CB_VECTOR) return FQM_E_FORMAT;
+            if (f.cb_mode != FQM_CB_SCALAR16 && (f.cb_base < 0 || f.cb_base > 48 || (f.cb_base & 15)))
+                return FQM_E_FORMAT;
             if (w->cols % bs) return FQM_E_SHAPE;
             if (f.n_hi < 0 || f.n_hi > w->rows) return FQM_E_SHAPE;
             if (w->rows == 0) return FQM_OK;
             const int64_t n_lo = w->rows - f.n_hi;
             const int64_t nb = w->cols / bs;
+            const int hb = f.hi_bits ? f.hi_bits : 4;
             if (!f.row_of) return FQM_E_NULL;
             if (!aligned16(f.row_of)) return FQM_E_ALIGN;
             if (f.n_hi > 0) {
                 if (!f.q4 || !f.s_hi) return FQM_E_NULL;
                 if (!aligned16(f.q4) || !aligned16(f.s_hi)) return FQM_E_ALIGN;
-                if (f.ld_q4 < w->cols / 2) return FQM_E_SHAPE;
+                if (f.ld_q4 < w->cols * hb / 8) return FQM_E_SHAPE;
                 if (f.ld_q4 & 15) return FQM_E_ALIGN;
             }
             if (n_lo > 0) {
-                if (!f.signs || !f.s_blk || !f.idx || !f.codebook) return FQM_E_NULL;
+                if (!f.signs || !f.s_blk || !f.idx) return FQM_E_NULL;
+                if (f.cb_mode == FQM_CB_VECTOR ? !f.vcodebook : !f.codebook) return FQM_E_NULL;
+                if (f.cb_mode != FQM_CB_SCALAR16 && !f.tier) return FQM_E_NULL;
                 if (!aligned16(f.signs) || !aligned16(f.s_blk) || !aligned16(f.idx) ||
-                    !aligned16(f.codebook))
+                    (f.codebook && !aligned16(f.codebook)) || (f.tier && !aligned16(f.tier)) ||
+                    (f.vcodebook && !aligned16(f.vcodebook)))
                     return FQM_E_ALIGN;
                 if (f.ld_signs < w->cols / 8 || f.ld_idx < (nb + 1) / 2) return FQM_E_SHAPE;
                 if ((f.ld_signs & 15) || (f.ld_idx & 15)) return FQM_E_ALIGN;
@@ -146,7 +154,7 @@ const char* fqm_status_str(int32_t status) {
 
 fqm_status fqm_pack_bits(const uint8_t* vals, uint8_t* out, int64_t rows, int64_t cols,
                          int32_t bits, int64_t ld, int32_t* d_err, void* stream) {
-    if (bits != 1 && bits != 4 && bits != 6) return FQM_E_FORMAT;
+    if (bits != 1 && bits != 4 && bits != 6 && bits != 8) return FQM_E_FORMAT;
     if (rows < 0 || cols < 0) return FQM_E_SHAPE;
     if (rows == 0) return FQM_OK;
     if (!out || (cols > 0 && !vals)) return FQM_E_NULL;

@@ -60,25 +60,35 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                           false);
 }
 
-// Vector-ALU kernel (batch 1..3), one stored row per wave.  Every lane runs
-// the same number of steps (indices past the row are clamped and their
-// results dropped by a select), so each group of U steps issues all its loads
-// before the first use; the row's output slot, int4 scale and the codebook
-// (one centroid per lane, looked up across lanes) are requested up front.
-template <int B>
+// Vector-ALU kernel, one stored row per wave (batch 1..3, and every batch
+// for blocks of 16 columns or vector centroids).  Every lane runs the same
+// number of steps (indices past the row are clamped and their results dropped
+// by a select), so each group of U steps issues all its loads before the
+// first use; the row's output slot, high-row scale and its 16 active
+// centroids (one pair per lane, looked up across lanes; the tier's window in
+// the tiered mode) are requested up front.  A sign dword covers 32 columns:
+// one block, part of one, or (16-column blocks) two, so its products are
+// summed per 16-column half.  VEC: the correction is a 128-float vector
+// centroid, sum_k V[k mod 128] x[k] over the half, in fp32.
+template <int B, bool VEC>
 __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16_t* __restrict__ x,
                                                         void* __restrict__ y, int y_f32,
                                                         int64_t rows, int64_t cols) {
-    constexpr int UI = B == 1 ? 5 : 1;  // int4 steps per group (64 dwords of 8 fields each)
-    constexpr int UB = B == 1 ? 3 : 1;  // binary steps per group (64 dwords of 32 signs each)
+    constexpr int UI = B == 1 ? 5 : 1;             // high-row steps per group (64 dwords of fields each)
+    constexpr int UB = (B == 1 && !VEC) ? 3 : 1;   // binary steps per group (64 dwords of 32 signs each)
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t i_u = (int64_t)blockIdx.x * kWaves + wave;  // stored row
     if (i_u >= rows) return;
     const int64_t i = i_u;
-    const bool has_bin = f.n_hi < rows;
+    const int64_t n_lo = rows - f.n_hi;
+    const bool has_bin = n_lo > 0;
+    const int64_t j = max(i - (int64_t)f.n_hi, (int64_t)0);        // binary row (when i >= n_hi)
+    const int tier = (has_bin && f.cb_mode != FQM_CB_SCALAR16) ? f.tier[min(j, n_lo - 1)] : 0;
+    const int cbase = 64 * tier + (f.cb_mode != FQM_CB_SCALAR16 ? f.cb_base : 0);
     // unconditional loads (x stands in for an array the matrix does not have)
-    const uint32_t cbits = *(reinterpret_cast<const uint32_t*>(has_bin ? f.codebook : x) + (lane & 7));
+    const uint32_t cbits = *(reinterpret_cast<const uint32_t*>((has_bin && !VEC) ? f.codebook + cbase : x) +
+                             (lane & 7));
     const int32_t out_row = f.row_of[i];
     const uint16_t hbits = *(f.n_hi > 0 ? f.s_hi + min(i, (int64_t)f.n_hi - 1) : x);
 
@@ -86,7 +96,47 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.f;
 
-    if (i < f.n_hi) {
+    if (i < f.n_hi && f.hi_bits == 8) {
+        // int8 row: two dwords = 8 fields = 8 columns per lane step.
+        const uint2* q = reinterpret_cast<const uint2*>(f.q4 + i * f.ld_q4);
+        const int64_t nw = cols / 8;
+        for (int64_t p0 = 0; p0 < nw; p0 += 64 * UI) {
+            uint2 d[UI];
+            uint4 xv[UI][B];
+#pragma unroll
+            for (int u = 0; u < UI; ++u) {
+                const int64_t p = min(p0 + 64 * u + lane, nw - 1);
+                d[u] = q[p];
+#pragma unroll
+                for (int b = 0; b < B; ++b) xv[u][b] = *reinterpret_cast<const uint4*>(x + (int64_t)b * cols + 8 * p);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < UI; ++u) {
+                const bool ok = p0 + 64 * u + lane < nw;
+                float wq[8];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    wq[jj] = (float)((int32_t)(d[u].x << (24 - 8 * jj)) >> 24);
+                    wq[4 + jj] = (float)((int32_t)(d[u].y << (24 - 8 * jj)) >> 24);
+                }
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const uint32_t xs[4] = {xv[u][b].x, xv[u][b].y, xv[u][b].z, xv[u][b].w};
+                    float a = acc[b];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        a = fmaf(wq[2 * jj], bf16lo(xs[jj]), a);
+                        a = fmaf(wq[2 * jj + 1], bf16hi(xs[jj]), a);
+                    }
+                    acc[b] = ok ? a : acc[b];
+                }
+            }
+        }
+        const float s = fp16_to_f32(hbits);
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] *= s;
+    } else if (i < f.n_hi) {
         // int4 row: one dword = 8 nibbles = 8 columns per lane step.
         const uint32_t* q = reinterpret_cast<const uint32_t*>(f.q4 + i * f.ld_q4);
         const int64_t nw = cols / 8;
@@ -124,29 +174,30 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[b] *= s;
     } else {
-        // binary row: one dword = 32 sign bits; a block (>= 64 columns) holds whole dwords.
-        // centroids 2 (lane % 8) and 2 (lane % 8) + 1 (fp16 pairs), read across lanes where used
+        // binary row: one dword = 32 sign bits, columns 32 p .. 32 p + 31.
         uint32_t ones = 0x3F803F80u;  // bf16 (1, 1), held in a register
         asm volatile("" : "+v"(ones));
-        const int64_t j = i - f.n_hi;
         const uint32_t* sg = reinterpret_cast<const uint32_t*>(f.signs + j * f.ld_signs);
         const int64_t nb = cols / f.blocksize;
         const uint16_t* sb = f.s_blk + j * nb;
         const uint8_t* ib = f.idx + j * f.ld_idx;
-        const int wshift = __builtin_ctz((unsigned)f.blocksize) - 5;  // log2(sign dwords per block)
+        const bool bs16 = f.blocksize == 16;
+        const int wshift = bs16 ? 0 : __builtin_ctz((unsigned)f.blocksize) - 5;  // log2(sign dwords per block)
         const int nw = (int)(cols / 32);
+        const float* vrow = VEC ? f.vcodebook + (int64_t)cbase * 128 : nullptr;
         for (int p0 = 0; p0 < nw; p0 += 64 * UB) {
             uint32_t d[UB];
-            uint16_t sbits[UB];
+            uint16_t sbits[UB][2];
             uint8_t ibits[UB];
             int bodd[UB];
             uint4 xv[UB][B][4];
 #pragma unroll
             for (int u = 0; u < UB; ++u) {
                 const int p = min(p0 + 64 * u + lane, nw - 1);
-                const int blk = p >> wshift;
+                const int blk = bs16 ? 2 * p : p >> wshift;  // block of the dword's first half
                 d[u] = sg[p];
-                sbits[u] = sb[blk];
+                sbits[u][0] = sb[blk];
+                sbits[u][1] = sb[bs16 ? blk + 1 : blk];
                 ibits[u] = ib[blk >> 1];
                 bodd[u] = blk & 1;
 #pragma unroll
@@ -159,26 +210,56 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
 #pragma unroll
             for (int u = 0; u < UB; ++u) {
                 const bool ok = p0 + 64 * u + lane < nw;
-                const float s = fp16_to_f32(sbits[u]);
-                const int id = (ibits[u] >> (4 * bodd[u])) & 15;
-                const uint32_t cpair = (uint32_t)__shfl((int)cbits, id >> 1);
-                const float c = fp16_to_f32((uint16_t)(cpair >> (16 * (id & 1))));
+                const float s0 = fp16_to_f32(sbits[u][0]), s1 = fp16_to_f32(sbits[u][1]);
+                // centroid of each half: bs16 -> the byte's two nibbles, else one nibble twice
+                const int id0 = bs16 ? (ibits[u] & 15) : (ibits[u] >> (4 * bodd[u])) & 15;
+                const int id1 = bs16 ? (ibits[u] >> 4) : id0;
+                float c0 = 0.f, c1 = 0.f;
+                float4 v[2][4];
+                if (VEC) {
+                    const int p = min(p0 + 64 * u + lane, nw - 1);
+                    const float* v0 = vrow + id0 * 128 + ((32 * p) & 127);
+                    const float* v1 = vrow + id1 * 128 + ((32 * p) & 127) + 16;
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        v[0][q4] = reinterpret_cast<const float4*>(v0)[q4];
+                        v[1][q4] = reinterpret_cast<const float4*>(v1)[q4];
+                    }
+                } else {
+                    const uint32_t cp0 = (uint32_t)__shfl((int)cbits, id0 >> 1);
+                    const uint32_t cp1 = (uint32_t)__shfl((int)cbits, id1 >> 1);
+                    c0 = fp16_to_f32((uint16_t)(cp0 >> (16 * (id0 & 1))));
+                    c1 = fp16_to_f32((uint16_t)(cp1 >> (16 * (id1 & 1))));
+                }
                 // the 32 signs as bf16 +-1.0 pairs: products with x are exact
                 uint32_t sv[16];
                 signs32_to_bf16(d[u], ones, sv);
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
-                    float ps = 0.f, xsum = 0.f;
+                    float ps[2] = {0.f, 0.f}, xsum[2] = {0.f, 0.f}, vx[2] = {0.f, 0.f};
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
+                        const int half = h >> 1;
                         const uint32_t xs[4] = {xv[u][b][h].x, xv[u][b][h].y, xv[u][b][h].z, xv[u][b][h].w};
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
-                            ps = dot2_bf16(sv[4 * h + t], xs[t], ps);
-                            xsum = dot2_bf16(ones, xs[t], xsum);
+                            ps[half] = dot2_bf16(sv[4 * h + t], xs[t], ps[half]);
+                            if (VEC) {
+                                const float4 vv = v[half][2 * (h & 1) + (t >> 1)];
+                                const float vl = (t & 1) ? vv.z : vv.x, vh = (t & 1) ? vv.w : vv.y;
+                                vx[half] = fmaf(vl, bf16lo(xs[t]), fmaf(vh, bf16hi(xs[t]), vx[half]));
+                            } else {
+                                xsum[half] = dot2_bf16(ones, xs[t], xsum[half]);
+                            }
                         }
                     }
-                    const float a = fmaf(s, ps, fmaf(c, xsum, acc[b]));
+                    float a = acc[b];
+                    if (VEC) {
+                        a = fmaf(s0, ps[0], fmaf(s1, ps[1], a + (vx[0] + vx[1])));
+                    } else {
+                        a = fmaf(s0, ps[0], fmaf(c0, xsum[0], a));
+                        a = fmaf(s1, ps[1], fmaf(c1, xsum[1], a));
+                    }
                     acc[b] = ok ? a : acc[b];
                 }
             }
@@ -197,18 +278,20 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core kernel (every batch 1..16).  A workgroup owns 16 stored rows
+// Matrix-core kernel (batch >= 4, blocks of 32 columns or more, scalar
+// centroids).  A workgroup owns 16 stored rows
 // (one v_mfma_f32_16x16x32_bf16 row block); its 8 waves split the row's
 // 32-wide k slices.  Every weight enters the product exactly as a bf16: a
-// sign bit as +-1.0, an int4 value as itself, and x is bf16 already, so each
-// product is exact and sums in fp32.  Per block a wave scales its partial
+// sign bit as +-1.0, an int4 or int8 value as itself (HI8: int8 high rows),
+// and x is bf16 already, so each product is exact and sums in fp32.  Per block a wave scales its partial
 // sum: binary rows add s_b * (sum of +-x) over the wave's slices of the
 // block (linear, so the waves' parts add up to the block's); int4 rows add
 // the plain sum and take the row scale at the end.  The codebook term
 // c[idx_b] * (sum of x over the wave's slices of block b) takes its sum of x
 // from a second MFMA per slice with an all-ones row operand (the matrix
-// cores are otherwise idle; no vector instructions per slice).  The per-block scales and centroids of the 16 rows are staged in LDS
-// first, so a flush reads LDS only.  The waves' results are added in
+// cores are otherwise idle; no vector instructions per slice).  The per-block
+// scales and centroid values of the 16 rows (the row's tier window in the
+// tiered mode) are staged in LDS first, so a flush reads LDS only.  The waves' results are added in
 // wave order.  A row block that is all binary (or all int4) decodes only its
 // own kind; a mixed one decodes both and selects per lane.
 // Latency shapes the loop: the first slices' loads go out before the tables
@@ -219,6 +302,21 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
 constexpr int kMW = 8;        // waves per workgroup
 constexpr int kGS = 8;        // slices whose loads a wave issues together
 constexpr int kMaxNB = 256;   // blocks per row the LDS tables hold (larger: VALU kernel)
+
+// Eight bf16 from eight 8-bit two's complement fields (field e at bits 8e of
+// the 64-bit lo | hi << 32), exact.
+__device__ __forceinline__ bf16x8_t bytes_to_bf16(uint32_t lo, uint32_t hi) {
+    u32x4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t d = e < 2 ? lo : hi;
+        const int sh = 16 * (e & 1);
+        const float a = (float)((int32_t)(d << (24 - sh)) >> 24);
+        const float b = (float)((int32_t)(d << (16 - sh)) >> 24);
+        v[e] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+    }
+    return __builtin_bit_cast(bf16x8_t, v);
+}
 
 // Eight bf16 from eight 4-bit two's complement fields (field e at bits 4e), exact.
 __device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t d) {
@@ -232,12 +330,12 @@ __device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t d) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-__global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(4))) void fabq_gemv_mfma_kernel(fqm_fabq f, const uint16_t* __restrict__ x,
+template <bool HI8>
+__global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(HI8 ? 2 : 4))) void fabq_gemv_mfma_kernel(fqm_fabq f, const uint16_t* __restrict__ x,
                                                                   void* __restrict__ y, int y_f32, int rows,
                                                                   int cols, int batch) {
-    __shared__ float s_sc[16 * kMaxNB];     // [row][blk]: s_b (binary) or 1 (int4)
-    __shared__ uint8_t s_ix[16 * kMaxNB];   // [row][blk]: idx_b (binary) or 16 (int4: centroid 0)
-    __shared__ float s_cb[17];              // centroids, and 0 at 16
+    __shared__ float s_sc[16 * kMaxNB];     // [row][blk]: s_b (binary) or 1 (high rows)
+    __shared__ float s_cv[16 * kMaxNB];     // [row][blk]: the block's centroid (binary) or 0 (high rows)
     __shared__ f32x4_t s_red[kMW * 64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -247,13 +345,15 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(4))) v
     // A operand: stored row r0 + lane % 16, k = 32 t + 8 g + e (g = lane / 16)
     const int g = lane >> 4;
     const int ra = min(r0 + (lane & 15), rows - 1);
-    const bool a_int4 = ra < f.n_hi;
-    // one dword per slice either way (no branch around the loads): int4 rows
-    // the dword of 8 fields at byte 16 t + 4 g, binary rows the dword at byte
-    // 4 t holding sign byte g
-    const uint8_t* arow = a_int4 ? f.q4 + (int64_t)ra * f.ld_q4 + 4 * g
+    const bool a_int4 = ra < f.n_hi;  // a high-precision row (int4, or int8 with HI8)
+    // the same loads either way (no branch around them): int4 rows the dword
+    // of 8 fields at byte 16 t + 4 g, int8 rows the two dwords of 8 fields at
+    // byte 32 t + 8 g, binary rows the dword at byte 4 t holding sign byte g
+    // (read twice where int8 rows read two)
+    const uint8_t* arow = a_int4 ? f.q4 + (int64_t)ra * f.ld_q4 + (HI8 ? 8 : 4) * g
                                  : f.signs + (int64_t)(ra - f.n_hi) * f.ld_signs;
-    const int astep = a_int4 ? 16 : 4;
+    const int astep = a_int4 ? (HI8 ? 32 : 16) : 4;
+    const int ahi = (HI8 && a_int4) ? 4 : 0;
     const int ashift = a_int4 ? 0 : 8 * g;
     // B operand: batch row lane % 16 (rows past the batch repeat the last one; never stored)
     const uint16_t* xrow = x + (int64_t)min(lane & 15, batch - 1) * cols + 8 * g;
@@ -265,12 +365,14 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(4))) v
     // (indices past the wave's last slice repeat it, or slice 0 for a wave
     // without slices; never used)
     uint32_t wq[2][kGS];
+    uint32_t wq2[2][HI8 ? kGS : 1];
     u32x4_t xv[2][kGS];
     auto load_group = [&](int q, int base) {
 #pragma unroll
         for (int u = 0; u < kGS; ++u) {
             const int t = max(min(base + u, t1 - 1), 0);
             wq[q][u] = *reinterpret_cast<const uint32_t*>(arow + astep * t);
+            if constexpr (HI8) wq2[q][u] = *reinterpret_cast<const uint32_t*>(arow + astep * t + ahi);
             xv[q][u] = *reinterpret_cast<const u32x4_t*>(xrow + 32 * t);
         }
     };
@@ -288,9 +390,10 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(4))) v
     const int64_t ejb = max(esr - f.n_hi, 0);
     const uint16_t* ps = has_bin ? f.s_blk + ejb * nblk + eb : x;
     const uint8_t* pi = has_bin ? f.idx + ejb * f.ld_idx + (eb >> 1) : reinterpret_cast<const uint8_t*>(x);
-    const uint16_t* pcb = has_bin ? f.codebook + (tid & 15) : x;
-    const uint16_t sraw = *ps, craw = *pcb;
-    const uint8_t iraw = *pi;
+    const bool tiered = f.cb_mode == FQM_CB_TIERED;
+    const uint8_t* pt = (has_bin && tiered) ? f.tier + ejb : reinterpret_cast<const uint8_t*>(x);
+    const uint16_t sraw = *ps;
+    const uint8_t iraw = *pi, traw = *pt;
     __builtin_amdgcn_sched_barrier(0);
     load_group(0, t0);  // unconditional, so the waits below count exactly
     // the output row and int4 row scale this thread stores at the end
@@ -298,25 +401,29 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(4))) v
     const int32_t out_row = f.row_of[srow];
     const uint16_t hraw = *(f.n_hi > 0 ? f.s_hi + min(srow, f.n_hi - 1) : x);  // used for int4 rows only
 
+    // centroid of binary row jb's block: the codebook entry, or the row's
+    // tier window entry
+    auto centroid = [&](int64_t jb, uint32_t id, uint32_t t) {
+        return fp16_to_f32(f.codebook[(tiered ? 64 * t + f.cb_base : 0) + id]);
+    };
     if (tid < ne) {
         const bool bin = esr >= f.n_hi;
         s_sc[er * kMaxNB + eb] = bin ? fp16_to_f32(sraw) : 1.f;
-        s_ix[er * kMaxNB + eb] = bin ? (uint8_t)((iraw >> ((eb & 1) * 4)) & 15u) : (uint8_t)16;
+        s_cv[er * kMaxNB + eb] = bin ? centroid(ejb, (iraw >> ((eb & 1) * 4)) & 15u, traw) : 0.f;
     }
     for (int e = tid + 64 * kMW; e < ne; e += 64 * kMW) {  // blocks shorter than 5120 / 32 columns
         const int r = e / nblk, blk = e - r * nblk;
         const int sr = min(r0 + r, rows - 1);
-        float sc = 1.f;
-        uint32_t ix = 16u;
+        float sc = 1.f, cv = 0.f;
         if (sr >= f.n_hi) {
             const int64_t jb = sr - f.n_hi;
             sc = fp16_to_f32(f.s_blk[jb * nblk + blk]);
-            ix = (f.idx[jb * f.ld_idx + (blk >> 1)] >> ((blk & 1) * 4)) & 15u;
+            cv = centroid(jb, (f.idx[jb * f.ld_idx + (blk >> 1)] >> ((blk & 1) * 4)) & 15u,
+                          tiered ? f.tier[jb] : 0u);
         }
         s_sc[r * kMaxNB + blk] = sc;
-        s_ix[r * kMaxNB + blk] = (uint8_t)ix;
+        s_cv[r * kMaxNB + blk] = cv;
     }
-    if (tid < 17) s_cb[tid] = (tid < 16 && has_bin) ? fp16_to_f32(craw) : 0.f;
     __syncthreads();  // tables
 
     f32x4_t total = {0.f, 0.f, 0.f, 0.f}, acc = {0.f, 0.f, 0.f, 0.f};
@@ -327,7 +434,7 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * g + i;
-            const float cv = s_cb[s_ix[r * kMaxNB + blk]];
+            const float cv = s_cv[r * kMaxNB + blk];
             total[i] = fmaf(s_sc[r * kMaxNB + blk], acc[i], fmaf(cv, xb, total[i]));
             acc[i] = 0.f;
             accx[i] = 0.f;
@@ -349,12 +456,16 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(4))) v
                 cur = blk;
             }
             bf16x8_t av;
+            auto high = [&]() {
+                if constexpr (HI8) return bytes_to_bf16(wq[q][u], wq2[q][u]);
+                else return nibbles_to_bf16(wq[q][u]);
+            };
             if (kind == 0) {
                 av = signs_to_bf16((wq[q][u] >> ashift) & 255u);
             } else if (kind == 1) {
-                av = nibbles_to_bf16(wq[q][u]);
+                av = high();
             } else {
-                const u32x4_t ai = __builtin_bit_cast(u32x4_t, nibbles_to_bf16(wq[q][u]));
+                const u32x4_t ai = __builtin_bit_cast(u32x4_t, high());
                 const u32x4_t as = __builtin_bit_cast(u32x4_t, signs_to_bf16((wq[q][u] >> ashift) & 255u));
                 av = __builtin_bit_cast(bf16x8_t, a_int4 ? ai : as);
             }
@@ -392,41 +503,55 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(4))) v
 template <int B>
 hipError_t launch_b(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
     const unsigned grid = (unsigned)((w.rows + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL(fabq_gemv_kernel<B>, dim3(grid), dim3(64 * kWaves), 0, s, w.fabq, x, y,
-                       y_f32, w.rows, w.cols);
+    if (w.fabq.cb_mode == FQM_CB_VECTOR)
+        hipLaunchKernelGGL((fabq_gemv_kernel<B, true>), dim3(grid), dim3(64 * kWaves), 0, s, w.fabq, x, y, y_f32,
+                           w.rows, w.cols);
+    else
+        hipLaunchKernelGGL((fabq_gemv_kernel<B, false>), dim3(grid), dim3(64 * kWaves), 0, s, w.fabq, x, y, y_f32,
+                           w.rows, w.cols);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// The matrix-core kernel takes batch >= 4 when the per-block tables of 16
-// rows fit its LDS (cols / blocksize <= 256) and the sizes fit 32 bits; the
-// VALU kernel takes the rest (at batch 1 it is the faster one: 8.8 against
-// 19 us on the 5120 x 5120 layer, where 8 batch rows take 31 against 23 us).
+// The matrix-core kernel takes batch >= 4 when blocks are at least 32 columns
+// (a 32-wide k slice never holds two blocks), the centroids are scalars, the
+// per-block tables of 16 rows fit its LDS (cols / blocksize <= 256) and the
+// sizes fit 32 bits; the VALU kernel takes the rest (at batch 1 it is the
+// faster one: 8.8 against 19 us on the 5120 x 5120 layer, where 8 batch rows
+// take 31 against 23 us).
 hipError_t launch_fabq_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
                             int batch, hipStream_t s) {
-    if (batch >= 4 && w.cols / w.fabq.blocksize <= kMaxNB && w.rows <= 0x7fffffff && w.cols <= 0x7fffffff) {
-        hipLaunchKernelGGL(fabq_gemv_mfma_kernel, dim3((unsigned)((w.rows + 15) / 16)), dim3(64 * kMW), 0, s,
-                           w.fabq, x, y, y_f32, (int)w.rows, (int)w.cols, batch);
+    fqm_weights v = w;
+    if (!v.fabq.hi_bits) v.fabq.hi_bits = 4;
+    const fqm_fabq& f = v.fabq;
+    if (batch >= 4 && f.blocksize >= 32 && f.cb_mode != FQM_CB_VECTOR && v.cols / f.blocksize <= kMaxNB &&
+        v.rows <= 0x7fffffff && v.cols <= 0x7fffffff) {
+        if (f.hi_bits == 8)
+            hipLaunchKernelGGL(fabq_gemv_mfma_kernel<true>, dim3((unsigned)((v.rows + 15) / 16)), dim3(64 * kMW), 0, s,
+                               f, x, y, y_f32, (int)v.rows, (int)v.cols, batch);
+        else
+            hipLaunchKernelGGL(fabq_gemv_mfma_kernel<false>, dim3((unsigned)((v.rows + 15) / 16)), dim3(64 * kMW), 0,
+                               s, f, x, y, y_f32, (int)v.rows, (int)v.cols, batch);
         return hipGetLastError();
     }
     switch (batch) {
-        case 1: return launch_b<1>(w, x, y, y_f32, s);
-        case 2: return launch_b<2>(w, x, y, y_f32, s);
-        case 3: return launch_b<3>(w, x, y, y_f32, s);
-        case 4: return launch_b<4>(w, x, y, y_f32, s);
-        case 5: return launch_b<5>(w, x, y, y_f32, s);
-        case 6: return launch_b<6>(w, x, y, y_f32, s);
-        case 7: return launch_b<7>(w, x, y, y_f32, s);
-        case 8: return launch_b<8>(w, x, y, y_f32, s);
-        case 9: return launch_b<9>(w, x, y, y_f32, s);
-        case 10: return launch_b<10>(w, x, y, y_f32, s);
-        case 11: return launch_b<11>(w, x, y, y_f32, s);
-        case 12: return launch_b<12>(w, x, y, y_f32, s);
-        case 13: return launch_b<13>(w, x, y, y_f32, s);
-        case 14: return launch_b<14>(w, x, y, y_f32, s);
-        case 15: return launch_b<15>(w, x, y, y_f32, s);
-        case 16: return launch_b<16>(w, x, y, y_f32, s);
+        case 1: return launch_b<1>(v, x, y, y_f32, s);
+        case 2: return launch_b<2>(v, x, y, y_f32, s);
+        case 3: return launch_b<3>(v, x, y, y_f32, s);
+        case 4: return launch_b<4>(v, x, y, y_f32, s);
+        case 5: return launch_b<5>(v, x, y, y_f32, s);
+        case 6: return launch_b<6>(v, x, y, y_f32, s);
+        case 7: return launch_b<7>(v, x, y, y_f32, s);
+        case 8: return launch_b<8>(v, x, y, y_f32, s);
+        case 9: return launch_b<9>(v, x, y, y_f32, s);
+        case 10: return launch_b<10>(v, x, y, y_f32, s);
+        case 11: return launch_b<11>(v, x, y, y_f32, s);
+        case 12: return launch_b<12>(v, x, y, y_f32, s);
+        case 13: return launch_b<13>(v, x, y, y_f32, s);
+        case 14: return launch_b<14>(v, x, y, y_f32, s);
+        case 15: return launch_b<15>(v, x, y, y_f32, s);
+        case 16: return launch_b<16>(v, x, y, y_f32, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -118,8 +118,9 @@ __global__ __launch_bounds__(256) void dequant_fabq_kernel(fqm_fabq f, int64_t r
     const int64_t out_row = f.row_of[i];
     double w;
     if (i < f.n_hi) {
-        int q = (int)field(f.q4 + i * f.ld_q4, k, 4);
-        q = q >= 8 ? q - 16 : q;
+        const int hb = f.hi_bits ? f.hi_bits : 4;
+        int q = (int)field(f.q4 + i * f.ld_q4, k, hb);
+        q = q >= (1 << (hb - 1)) ? q - (1 << hb) : q;
         w = (double)q * (double)fp16_to_f32(f.s_hi[i]);
     } else {
         const int64_t j = i - f.n_hi;
@@ -127,7 +128,14 @@ __global__ __launch_bounds__(256) void dequant_fabq_kernel(fqm_fabq f, int64_t r
         const int64_t blk = k / f.blocksize;
         const double s = (double)fp16_to_f32(f.s_blk[j * nb + blk]);
         const uint32_t id = field(f.idx + j * f.ld_idx, blk, 4);
-        const double c = (double)fp16_to_f32(f.codebook[id]);
+        double c;
+        if (f.cb_mode == FQM_CB_SCALAR16) {
+            c = (double)fp16_to_f32(f.codebook[id]);
+        } else {
+            const int64_t cid = 64 * (int64_t)f.tier[j] + f.cb_base + id;
+            c = f.cb_mode == FQM_CB_TIERED ? (double)fp16_to_f32(f.codebook[cid])
+                                           : (double)f.vcodebook[cid * 128 + (k & 127)];
+        }
         w = (field(f.signs + j * f.ld_signs, k, 1) ? s : -s) + c;   // exact in fp64
     }
     W[out_row * cols + k] = f64_to_bf16_rne(w);

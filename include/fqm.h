@@ -21,11 +21,17 @@
  *             per byte.
  *   FQM_FABQ  "FABQ-RC" README "Key Ideas" and the FABQ-RC model card
  *             "How It Works" / "Quantization Details": the top 5 % of output
- *             rows as int4 with an fp16 row scale, the rest binary +-1 with an
- *             fp16 scale per block of `blocksize` columns plus a per-block
- *             4-bit index into a 16-entry fp16 residual codebook whose
- *             centroid is added back at inference:
- *                 w = s_b * (+-1) + c[idx_b].
+ *             rows as int4 (model card) or int8 (README) with an fp16 row
+ *             scale, the rest binary +-1 with an fp16 scale per block of
+ *             `blocksize` columns plus a per-block 4-bit index into a residual
+ *             codebook whose centroid is added back at inference:
+ *                 w = s_b * (+-1) + corr,
+ *             corr = c[idx_b] (one 16-entry fp16 codebook), or, with the
+ *             card's 4 tiered codebooks of 64 centroids (a binary row's tier
+ *             its importance quartile; 16 active centroids per layer from
+ *             cb_base), C[tier][cb_base + idx_b] (fp16 centroids) or
+ *             V[tier][cb_base + idx_b][k mod 128] (the card's
+ *             4 x 64 x 128 x 4-byte storage read as 128-float vectors).
  *   FQM_MDBF  OneCompression "MDBF", "Algorithm": W = sum_p F_p G_p with
  *             F = S_A (.) (A_amp Q_U^T), G = S_B (.) (Q_V B_amp^T), sign
  *             matrices packed 8 per byte and fp16 envelopes; evaluated as
@@ -39,6 +45,7 @@
  * last field are zero (fqm_pack writes them) and are ignored by the kernels.
  *   b = 6: LUT6 codes.  b = 1: signs, bit 1 = +1, bit 0 = -1.
  *   b = 4: int4 weights (two's complement) and codebook indices.
+ *   b = 8: int8 weights (two's complement).
  *
  * Numbers.  bf16 and fp16 values are passed as their uint16_t bit patterns.
  * Products accumulate in fp32; bf16 outputs are rounded to nearest even.
@@ -76,7 +83,7 @@
 extern "C" {
 #endif
 
-#define FQM_VERSION 3
+#define FQM_VERSION 4
 
 /* Bytes of the device scratch array fqm_gemv_static uses on each GPU. */
 #define FQM_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
@@ -113,23 +120,34 @@ typedef struct fqm_lut4 {
 } fqm_lut4;
 
 /* FABQ-RC-style core (rows = N, cols = K).  Stored row i (0 <= i < rows)
- * produces output row row_of[i]; stored rows 0..n_hi-1 are int4 rows, stored
- * rows n_hi..rows-1 are binary rows (binary row j = stored row n_hi + j).
- * row_of must be a permutation of 0..rows-1 (not checked: a repeated entry
- * makes two rows write the same output). */
+ * produces output row row_of[i]; stored rows 0..n_hi-1 are high-precision
+ * rows, stored rows n_hi..rows-1 are binary rows (binary row j = stored row
+ * n_hi + j).  row_of must be a permutation of 0..rows-1 (not checked: a
+ * repeated entry makes two rows write the same output).  A zeroed hi_bits /
+ * cb_mode means 4 / FQM_CB_SCALAR16. */
+enum fqm_cb_mode {
+    FQM_CB_SCALAR16 = 0,  /* codebook: [16] fp16; corr = codebook[idx] */
+    FQM_CB_TIERED = 1,    /* codebook: [4][64] fp16; corr = codebook[tier][cb_base + idx] */
+    FQM_CB_VECTOR = 2     /* vcodebook: [4][64][128] fp32; corr = vcodebook[tier][cb_base + idx][k % 128] */
+};
 typedef struct fqm_fabq {
-    int32_t blocksize;          /* 64, 128, 256 or 512; divides cols */
-    int32_t n_hi;               /* int4 rows, 0..rows */
+    int32_t blocksize;          /* 16, 32, 64, 128, 256 or 512; divides cols */
+    int32_t n_hi;               /* high-precision rows, 0..rows */
     const int32_t* row_of;      /* [rows] */
-    const uint8_t* q4;          /* [n_hi][ld_q4], 4-bit two's complement fields */
-    int64_t ld_q4;              /* >= cols/2 */
+    const uint8_t* q4;          /* [n_hi][ld_q4], hi_bits-wide two's complement fields */
+    int64_t ld_q4;              /* >= cols*hi_bits/8 */
     const uint16_t* s_hi;       /* [n_hi] fp16 row scales */
     const uint8_t* signs;       /* [rows-n_hi][ld_signs], 1-bit fields */
     int64_t ld_signs;           /* >= cols/8 */
     const uint16_t* s_blk;      /* [rows-n_hi][cols/blocksize] fp16, dense */
     const uint8_t* idx;         /* [rows-n_hi][ld_idx], 4-bit fields, one per block */
     int64_t ld_idx;             /* >= ceil(cols/blocksize/2) */
-    const uint16_t* codebook;   /* [16] fp16 centroids */
+    const uint16_t* codebook;   /* FQM_CB_SCALAR16: [16] fp16; FQM_CB_TIERED: [4][64] fp16 */
+    int32_t hi_bits;            /* 4 or 8 (0 = 4) */
+    int32_t cb_mode;            /* enum fqm_cb_mode */
+    int32_t cb_base;            /* tiered modes: 0, 16, 32 or 48 */
+    const uint8_t* tier;        /* tiered modes: [rows-n_hi], 0..3 per binary row */
+    const float* vcodebook;     /* FQM_CB_VECTOR: [4][64][128] fp32 */
 } fqm_fabq;
 
 /* One MDBF path (rows = n outputs, cols = m inputs, rank r, envelope rank l). */
@@ -168,7 +186,7 @@ int32_t fqm_version(void);
 /* Static, human-readable name of a status code (never NULL). */
 const char* fqm_status_str(int32_t status);
 
-/* Pack `bits`-wide unsigned fields (bits = 1, 4 or 6): vals [rows][cols]
+/* Pack `bits`-wide unsigned fields (bits = 1, 4, 6 or 8): vals [rows][cols]
  * uint8, one field per byte, row-major and dense; out [rows][ld] bytes under
  * the packed-field rule above, padding bytes zeroed.  A value >= 2^bits is
  * packed as (value & (2^bits - 1)) and sets bit 0 of *d_err (a device int32
@@ -192,7 +210,7 @@ fqm_status fqm_unpack(const uint8_t* packed, uint8_t* codes, int64_t rows, int64
 
 /* Test helper: write the decoded weights W [rows][cols] as bf16, row-major,
  * row index = output row.  LUT6 and LUT4: W[r][k] = lut[r][code] (an exact copy).
- * FABQ: the exact value of q*s or s_b*(+-1) + c[idx] rounded once to bf16
+ * FABQ: the exact value of q*s or s_b*(+-1) + corr rounded once to bf16
  * (nearest even).  MDBF: FQM_E_UNSUPPORTED (W is a product of factors). */
 fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
 

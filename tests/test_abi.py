@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert decl == set(fqm.SYMBOLS)
     for name in decl:
         assert hasattr(lib, name), name
-    assert lib.fqm_version() == 3
+    assert lib.fqm_version() == 4
 
 
 def test_status_strings(lib):
@@ -307,3 +307,35 @@ def test_gemv_static_rejects_more_than_its_scratch(lib):
     assert rc == 8 and lib.fqm_status_str(rc).startswith(b"needs more scratch")
     assert lib.fqm_gemv_static(ctypes.byref(w), FAKE, FAKE, 0, 17, None) == E["SHAPE"]
     assert lib.fqm_gemv_static(None, FAKE, FAKE, 0, 1, None) == E["NULL"]
+
+
+def test_fabq_variant_argument_errors(lib):
+    """The descriptor's variant fields are checked on the host: blocksizes 16
+    and 32 pass, other widths, high-row widths, codebook modes and windows are
+    refused; the tiered modes need the tier array, the vector mode its
+    vector codebook; int8 rows need cols bytes per row."""
+    for bs in (16, 32):
+        assert gemv(lib, fabq(bs=bs)) not in (E["FORMAT"], E["SHAPE"], E["NULL"], E["ALIGN"])
+    assert gemv(lib, fabq(bs=8)) == E["FORMAT"]
+    for field, bad in (("hi_bits", 6), ("cb_mode", 3), ("cb_mode", -1)):
+        w = fabq()
+        setattr(w.fabq, field, bad)
+        assert gemv(lib, w) == E["FORMAT"], field
+    for mode in (1, 2):
+        w = fabq()
+        w.fabq.cb_mode, w.fabq.cb_base = mode, 8  # not a multiple of 16
+        assert gemv(lib, w) == E["FORMAT"]
+        w.fabq.cb_base = 48
+        w.fabq.tier = None
+        assert gemv(lib, w) == E["NULL"]
+    w = fabq()
+    w.fabq.cb_mode, w.fabq.tier, w.fabq.vcodebook = 2, FAKE, None
+    assert gemv(lib, w) == E["NULL"]
+    w.fabq.vcodebook, w.fabq.codebook = FAKE, None  # the vector mode needs no fp16 codebook
+    assert gemv(lib, w) not in (E["FORMAT"], E["SHAPE"], E["NULL"], E["ALIGN"])
+    w = fabq()
+    w.fabq.hi_bits = 8  # int8 rows: ld_q4 >= cols = 512 bytes
+    assert gemv(lib, w) == E["SHAPE"]
+    w.fabq.ld_q4 = 512
+    assert gemv(lib, w) not in (E["FORMAT"], E["SHAPE"], E["NULL"], E["ALIGN"])
+    assert lib.fqm_pack_bits(FAKE, FAKE, 0, 64, 8, 64, None, None) == E["OK"]  # 8-bit fields

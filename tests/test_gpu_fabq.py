@@ -23,7 +23,9 @@ def case(rows, cols, seed, bs):
 def weights(inp):
     return fqm.FabqWeights.from_arrays(inp.rows, inp.cols, inp.blocksize, inp.n_hi, inp.row_of,
                                        inp.q4, inp.s_hi, inp.signs, inp.s_blk, inp.idx,
-                                       inp.codebook, device=DEV)
+                                       inp.codebook, device=DEV, hi_bits=inp.hi_bits,
+                                       cb_mode=inp.cb_mode, cb_base=inp.cb_base, tier=inp.tier,
+                                       vcodebook=inp.vcodebook)
 
 
 @pytest.mark.parametrize("bs", [64, 128, 256, 512])
@@ -105,3 +107,71 @@ def test_int4_minus_eight_gemv(hi_frac, batch):
     assert canaries_intact(buf)
     assert_close(to_f64(y), oracle.fabq.gemv(p, x, 96, 1024, 128, inp.n_hi), "f32",
                  f"hi={hi_frac} b{batch}")
+
+
+# ---- the variants: int8 high rows (README), blocks of 16 and 32 columns
+# (README's sweep), tiered codebooks of 4 x 64 centroids with 16 active per
+# layer and 128-float vector centroids (model card "Residual Codebook
+# Architecture").  Batches 1-3 run the VALU kernel; batch >= 4 the
+# matrix-core kernel except for 16-column blocks and vector centroids.
+VARIANTS = [  # (hi_bits, cb_mode, blocksize)
+    (8, 0, 64), (4, 0, 16), (4, 0, 32), (4, 1, 128), (8, 1, 32), (4, 1, 16),
+    (4, 2, 128), (8, 2, 16), (4, 2, 512), (8, 2, 32)]
+
+
+@functools.lru_cache(maxsize=None)
+def variant(rows, cols, seed, hi_bits, cb_mode, bs, hi_frac=0.05):
+    inp = synth.fabq_input(rows, cols, seed, blocksize=bs, hi_bits=hi_bits, cb_mode=cb_mode,
+                           hi_frac=hi_frac)
+    return inp, oracle.fabq.pack(inp)
+
+
+@pytest.mark.parametrize("hi_bits,cb_mode,bs", VARIANTS)
+def test_variant_dequant_bit_exact(hi_bits, cb_mode, bs):
+    inp, p = variant(301, 1536, 61, hi_bits, cb_mode, bs, 0.1)
+    W = fqm.dequant(weights(inp)).view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.numerics.bf16_bits_from_f64_rne(oracle.fabq.decode(p, 301, 1536, bs, inp.n_hi))
+    assert np.array_equal(W, ref)
+
+
+@pytest.mark.parametrize("hi_bits,cb_mode,bs", VARIANTS)
+@pytest.mark.parametrize("batch", [1, 3, 4, 16])
+def test_variant_gemv_ragged(hi_bits, cb_mode, bs, batch):
+    """301 rows (a partial 16-row block, a mixed block of high and binary
+    rows), 1536 columns."""
+    inp, p = variant(301, 1536, 61, hi_bits, cb_mode, bs, 0.1)
+    x = synth.activations(batch, 1536, 62)
+    buf, y = guarded((batch, 301), torch.float32)
+    print(f"fabq variant hi{hi_bits} cb{cb_mode} bs{bs} batch {batch}", flush=True)
+    fqm.gemv(weights(inp), bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.fabq.gemv(p, x, 301, 1536, bs, inp.n_hi), "f32",
+                 f"hi{hi_bits} cb{cb_mode} bs{bs} b{batch}")
+
+
+@pytest.mark.parametrize("hi_bits,cb_mode,bs", [(8, 1, 32), (4, 2, 512), (8, 0, 16), (4, 1, 64)])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_variant_full_layer(hi_bits, cb_mode, bs, batch):
+    """The 5120 x 5120 layer of the benchmark (256 high rows) in each variant."""
+    inp, p = variant(5120, 5120, 5, hi_bits, cb_mode, bs)
+    x = synth.activations(batch, 5120, 5)
+    print(f"fabq layer hi{hi_bits} cb{cb_mode} bs{bs} batch {batch}", flush=True)
+    y = fqm.gemv(weights(inp), bf16_dev(x))
+    assert_close(to_f64(y), oracle.fabq.gemv(p, x, 5120, 5120, bs, inp.n_hi), "bf16",
+                 f"hi{hi_bits} cb{cb_mode} bs{bs} b{batch}")
+
+
+def test_variant_invariants():
+    """One-hot x returns a decoded column (fp32 out, exact up to the order of
+    two additions); the same call twice gives the same bits."""
+    inp, p = variant(301, 1536, 61, 8, 2, 16, 0.1)
+    w = weights(inp)
+    W = oracle.fabq.decode(p, 301, 1536, 16, inp.n_hi)
+    for k in (0, 150, 1535):
+        x = np.zeros((1, 1536), np.uint16)
+        x[0, k] = 0x3F80
+        y = to_f64(fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32))[0]
+        assert np.allclose(y, W[:, k], rtol=2 ** -22, atol=0), k
+    x = bf16_dev(synth.activations(5, 1536, 63))
+    assert torch.equal(fqm.gemv(w, x, out_dtype=torch.float32), fqm.gemv(w, x, out_dtype=torch.float32))
