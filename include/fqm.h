@@ -204,12 +204,19 @@ fqm_status fqm_pack(const uint8_t* codes, uint8_t* packed, int64_t rows, int64_t
                     int64_t ld, int32_t* d_err, void* stream);
 
 /* Test helper: unpack 6-bit codes back to one byte per code, codes [rows][cols]
- * dense.  Requires cols % 4 == 0. */
+ * dense.  Requires cols % 4 == 0.  The inverse of fqm_pack: each group of three
+ * bytes (little-endian 24 bits) yields four codes of 6 bits, lowest first.
+ * Source: "Qwen3.8-27B - BenQ 6-bit", "What BenQ stores" (one 6-bit code per
+ * weight) and its usage note on packing the stored uint8 codes to 6 bits. */
 fqm_status fqm_unpack(const uint8_t* packed, uint8_t* codes, int64_t rows, int64_t cols,
                       int64_t ld, void* stream);
 
 /* Test helper: write the decoded weights W [rows][cols] as bf16, row-major,
- * row index = output row.  LUT6 and LUT4: W[r][k] = lut[r][code] (an exact copy).
+ * row index = output row.  Sources: LUT6 / LUT4 "Qwen3.8-27B - BenQ 6-bit",
+ * "What BenQ stores" (decode is a gather of the code's entry in the row's
+ * table); FABQ the FABQ-RC model card "Quantization Details" and the FABQ-RC
+ * README "Key Ideas" (scale times sign or int4 / int8 level, plus the residual
+ * codebook correction).  LUT6 and LUT4: W[r][k] = lut[r][code] (an exact copy).
  * FABQ: the exact value of q*s or s_b*(+-1) + corr rounded once to bf16
  * (nearest even).  MDBF: FQM_E_UNSUPPORTED (W is a product of factors). */
 fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
@@ -268,7 +275,9 @@ fqm_status fqm_gemv_static(const fqm_weights* w, const uint16_t* x, void* y, int
 size_t fqm_gemm_workspace_size(const fqm_weights* w, int64_t M);
 
 /* Y = X W^T for a LUT6 or LUT4 descriptor (prefill): X [M][cols] bf16, Y [M][rows]
- * bf16, both row-major; cols a multiple of 64 and M * cols * 2 < 2^31
+ * bf16, both row-major.  Source: "Qwen3.8-27B - BenQ 6-bit", "What BenQ stores":
+ * the gather of the decode fused into the GEMM so that the decoded matrix is
+ * never written out.  Shapes: cols a multiple of 64 and M * cols * 2 < 2^31
  * (FQM_E_SHAPE otherwise).  Each weight is gathered from its row's table
  * (exact: the levels are bf16) straight into the operands of the bf16 matrix
  * cores, fp32 accumulation.  workspace: device memory of at least
