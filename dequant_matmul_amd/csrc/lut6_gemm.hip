@@ -35,11 +35,13 @@
 // codes) hit 32 distinct banks: gathers never conflict.  A code c becomes the
 // gather address (c << 7) | base_lane, i.e. one shift and one v_and_or_b32.
 //
-// X: double-buffered 256 x 64 bf16 tiles (128-byte rows, 16-byte chunks
+// X: three 256 x 64 bf16 tile buffers (128-byte rows, 16-byte chunks
 // XOR-swizzled by (row / 2) % 8 so the operand reads of 16 rows hit 16
 // distinct bank groups), filled by direct global -> LDS loads one step ahead.
-// One workgroup barrier per step publishes the next X tile.  LDS: 64 KB of X
-// and 32 KB of tables, one workgroup per compute unit.
+// One workgroup barrier per step publishes the next X tile; with three
+// buffers it needs no wait for the wave's LDS reads, so the operand reads
+// and gathers stay one and two slices ahead of the MFMAs across it.  LDS:
+// 96 KB of X and 32 KB of tables, one workgroup per compute unit.
 //
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, and
 // workgroup b computes M tile b % mtiles, so with M = 8 * BM each XCD keeps
@@ -70,8 +72,8 @@ typedef __attribute__((address_space(3))) void lvoid;
 constexpr int BM_BIG = 256, BM_SMALL = 64;
 constexpr int BN = 256, BK = 64;
 constexpr int NWAVE = 8;                       // 8 waves along N, BM x 32 outputs each
-constexpr int CD = 3;                          // codes are requested CD steps ahead
-static_assert(BN == 32 * NWAVE && CD == 3, "tile constants (the loop is unrolled by CD + 1)");
+constexpr int NXB = 3;                         // X tile buffers (and code slots): the loop is unrolled by 3
+static_assert(BN == 32 * NWAVE, "tile constants");
 template <int BM>
 struct TileShape {
     static constexpr int MB = BM / 32;                    // 32-row blocks of X per wave
@@ -126,15 +128,16 @@ __device__ __forceinline__ void slice_addrs(const uint32_t (&d)[ND], uint32_t ma
 template <int Q>
 using Slice = std::integral_constant<int, Q>;
 
-// Workgroup barrier after this wave's LDS operations and all but its last N
-// vector-memory loads have completed (loads complete in issue order).  The
-// wait is the waitcnt builtin, so the compiler's own wait bookkeeping sees it;
-// the barrier is the bare instruction between two compiler memory barriers
-// (a workgroup fence would also wait for the loads left in flight).
+// Workgroup barrier after all but this wave's last N vector-memory loads have
+// completed (loads complete in issue order).  LDS reads may stay in flight:
+// the buffers they read are not rewritten before the next barrier.  The wait
+// is the waitcnt builtin, so the compiler's own wait bookkeeping sees it; the
+// barrier is the bare instruction between two compiler memory barriers (a
+// workgroup fence would also wait for the loads left in flight).
 template <int N>
 __device__ __forceinline__ void barrier_after_loads() {
     static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0070 | N);  // vmcnt(N) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt(N) expcnt(7) lgkmcnt(15)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -161,7 +164,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
     __shared__ __attribute__((aligned(8192))) uint8_t s_tab[TAB_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t s_x0[XT_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t s_x1[XT_BYTES];
-    lds8* const XS[2] = {(lds8*)s_x0, (lds8*)s_x1};
+    __shared__ __attribute__((aligned(16))) uint8_t s_x2[XT_BYTES];
+    lds8* const XS[NXB] = {(lds8*)s_x0, (lds8*)s_x1, (lds8*)s_x2};
     lds8* const TAB = (lds8*)s_tab;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -221,9 +225,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
                                                      xtile + (uint32_t)t * (BK * 2), 0, 0);
     };
 
-    // ---- codes: 24 bytes of row 32 wn + j per lane per step, CD steps ahead -------
+    // ---- codes: 24 bytes of row 32 wn + j per lane per step ------------------------
     const uint8_t* csrc = packed + (int64_t)min(n0 + 32 * wn + j, N - 1) * ld + 4 * ND * g;
-    uint32_t cw[CD + 1][ND];
+    uint32_t cw[NXB][ND];
     auto load_codes = [&](int slot, int t) {
         const uint8_t* p = csrc + F::STEP_BYTES * t;
         const u32x4 lo = *reinterpret_cast<const u32x4_a8*>(p);
@@ -250,70 +254,124 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X,
     const int t0 = (int)((int64_t)ks * ksteps / ksplit), t1 = (int)((int64_t)(ks + 1) * ksteps / ksplit);
     const int steps = t1 - t0;  // >= 1
     __builtin_assume(steps > 0);
-    // ---- prologue: tables, X(t0), codes of steps t0 .. t0 + CD - 1 -----------------
-    dma_x(0, t0);
+
+    // ---- operands: A one slice ahead, table gathers two slices ahead ----------------
+    // a[i] and bop hold the operands of the slice whose MFMAs issue next, wv
+    // the gathered table entries of the slice after it.  A slice first packs
+    // wv into the next B operand; while its MFMAs run, the wave reads the next
+    // slice's A operands (a[i] right after the MFMA that consumes it) and
+    // gathers the entries of the slice after that.  The order is pinned with
+    // scheduling groups, one MFMA at a time.
+    bf16x8 a[MB];
+    bf16x8 bop;
+    uint32_t wv[8];
+    auto pack_b = [&]() {
+        u32x4 bw;
 #pragma unroll
-    for (int u = 0; u < CD; ++u) load_codes(u, t0 + min(u, steps - 1));
+        for (int e = 0; e < 4; ++e) bw[e] = __builtin_amdgcn_perm(wv[2 * e + 1], wv[2 * e], 0x05040100u);
+        return __builtin_bit_cast(bf16x8, bw);
+    };
+    auto read_a = [&](int buf, auto qc) {
+        constexpr int q = decltype(qc)::value;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) a[i] = __builtin_bit_cast(bf16x8, *(lds128c*)(XS[buf] + aoff[q] + 4096 * i));
+    };
+    auto gather = [&](auto qc, int slot) {
+        constexpr int q = decltype(qc)::value;
+        uint32_t ad[8];
+        slice_addrs<BITS, q>(cw[slot], cmask, tbase, ad);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[e] = *(lds16c*)(TAB + ad[e]);
+    };
+    // Gathers ride with the first half of the slice's MFMAs (GPM per MFMA), so
+    // that the perms at the start of the next slice wait only for LDS reads
+    // issued half a slice earlier.
+    constexpr int HALF = MB / 2, GPM = 8 / HALF;
+    static_assert(GPM * HALF == 8, "8 gathers per slice");
+    // The MFMAs of the current slice; A of slice AQ from X buffer AB, gathers of
+    // slice GQ from code slot GS.
+    auto slice = [&](auto aqc, int ab, auto gqc, int gs) {
+        constexpr int aq = decltype(aqc)::value, gq = decltype(gqc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 bnext = pack_b();
+        uint32_t ad[8];
+        slice_addrs<BITS, gq>(cw[gs], cmask, tbase, ad);
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bop, acc[i], 0, 0, 0);
+            a[i] = __builtin_bit_cast(bf16x8, *(lds128c*)(XS[ab] + aoff[aq] + 4096 * i));
+            if (i < HALF) {
+#pragma unroll
+                for (int e = GPM * i; e < GPM * (i + 1); ++e) wv[e] = *(lds16c*)(TAB + ad[e]);
+            }
+        }
+        bop = bnext;
+        // perms and the first addresses; per MFMA: the MFMA, its A read (and in
+        // the first half its gathers), then the next gathers' addresses
+        __builtin_amdgcn_sched_group_barrier(0x0002, 4 + 2 * GPM, 0);
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x0100, 1 + GPM, 0);
+            __builtin_amdgcn_sched_group_barrier(0x0002, 2 * GPM, 0);
+        }
+#pragma unroll
+        for (int i = HALF; i < MB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: X(t0) and the codes of steps t0, t0 + 1 in place; then, as
+    // after every barrier, the next X tile and codes requested; operands of
+    // slice 0 read and entries of slices 0 and 1 gathered
+    dma_x(0, t0);
+    load_codes(0, t0);
+    load_codes(1, t0 + min(1, steps - 1));
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
+    __syncthreads();                     // tables and X(t0) visible
+    dma_x(1, t0 + min(1, steps - 1));
+    __builtin_amdgcn_sched_barrier(0);  // the X loads go out before the code loads
+    load_codes(2, t0 + min(2, steps - 1));
+    gather(Slice<0>{}, 0);
+    read_a(0, Slice<0>{});
+    bop = pack_b();
+    gather(Slice<1>{}, 0);
 
     // ---- main loop -----------------------------------------------------------------
-    // Step t0 + t (X buffer B = t % 2, code slot S = t % (CD + 1)): request X(t+1),
-    // then the codes of step t + CD, then the four slices of step t (operand
-    // reads, gathers, MFMAs).  Before the closing barrier publishes X(t+1) the
-    // wave waits until at most the code loads of this step (two 6-bit, one
-    // 4-bit) are in flight
-    // (memory loads complete in issue order, so X(t+1) and every older code
-    // load have landed); the last steps wait for everything.  Past the end the
-    // indices are clamped (the extra work lands in buffers that are never read).
-    auto step = [&](auto bufc, auto slotc, auto lastc, int t) {
-        constexpr int B = decltype(bufc)::value, S = decltype(slotc)::value;
-        constexpr bool LAST = decltype(lastc)::value;
-        dma_x(B ^ 1, t0 + min(t + 1, steps - 1));
-        __builtin_amdgcn_sched_barrier(0);
-        load_codes((S + CD) % (CD + 1), t0 + min(t + CD, steps - 1));
-        __builtin_amdgcn_sched_barrier(0);  // the loads go out first, in this order
-        auto slice = [&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            bf16x8 a[MB];
-#pragma unroll
-            for (int i = 0; i < MB; ++i) a[i] = __builtin_bit_cast(bf16x8, *(lds128c*)(XS[B] + aoff[q] + 4096 * i));
-            uint32_t ad[8];
-            slice_addrs<BITS, q>(cw[S], cmask, tbase, ad);
-            uint32_t wv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) wv[e] = *(lds16c*)(TAB + ad[e]);
-            u32x4 bw;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bw[e] = __builtin_amdgcn_perm(wv[2 * e + 1], wv[2 * e], 0x05040100u);
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-#pragma unroll
-            for (int i = 0; i < MB; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bop, acc[i], 0, 0, 0);
-        };
-        slice(Slice<0>{});
-        slice(Slice<1>{});
-        slice(Slice<2>{});
-        slice(Slice<3>{});
-        if constexpr (LAST)
-            barrier_after_loads<0>();
-        else
-            barrier_after_loads<F::CODE_LOADS>();  // only this step's code loads may stay in flight
+    // Step t0 + t uses X buffer and code slot P = t % 3.  Its slices 0..2 issue
+    // their MFMAs while reading A of slices 1..3 and gathering for slices 2, 3
+    // and slice 0 of step t+1; then the wave waits until X(t+1) (requested one
+    // step earlier) has landed, the workgroup barrier publishes it, and slice 3
+    // reads A of slice 0 of step t+1 from it and gathers for that step's slice
+    // 1.  After the barrier every wave has consumed X(t-1) (its MFMAs read those
+    // operands), so that buffer takes X(t+2); the codes of step t+3 go into
+    // slot P (its last gathers were issued in slice 1).  Memory loads complete
+    // in issue order: after the barrier a step issues X(t+2) and then
+    // codes(t+3), so at the next barrier only this step's code loads may still
+    // be in flight.  Past the end the indices are clamped; the extra reads land
+    // in buffers and registers that are never used.
+    auto step = [&](auto pc, int t) {
+        constexpr int P = decltype(pc)::value, P1 = (P + 1) % NXB, P2 = (P + 2) % NXB;
+        slice(Slice<1>{}, P, Slice<2>{}, P);
+        slice(Slice<2>{}, P, Slice<3>{}, P);
+        slice(Slice<3>{}, P, Slice<0>{}, P1);
+        barrier_after_loads<F::CODE_LOADS>();
+        dma_x(P2, t0 + min(t + 2, steps - 1));
+        __builtin_amdgcn_sched_barrier(0);  // the X loads go out before the code loads
+        load_codes(P, t0 + min(t + 3, steps - 1));
+        slice(Slice<0>{}, P1, Slice<1>{}, P1);
     };
-    // The four steps of an iteration run unconditionally (one basic block), so
-    // each step's loads stay where the scheduling barriers put them; the
-    // remaining 0..3 steps wait for all their loads.
-    using Fast = std::false_type;
-    using Last = std::true_type;
     int t = 0;
-    for (; t + 3 < steps; t += 4) {
-        step(Buf<0>{}, Buf<0>{}, Fast{}, t);
-        step(Buf<1>{}, Buf<1>{}, Fast{}, t + 1);
-        step(Buf<0>{}, Buf<2>{}, Fast{}, t + 2);
-        step(Buf<1>{}, Buf<3>{}, Fast{}, t + 3);
+    for (; t + 2 < steps; t += 3) {
+        step(Buf<0>{}, t);
+        step(Buf<1>{}, t + 1);
+        step(Buf<2>{}, t + 2);
     }
-    if (t < steps) step(Buf<0>{}, Buf<0>{}, Last{}, t);
-    if (t + 1 < steps) step(Buf<1>{}, Buf<1>{}, Last{}, t + 1);
-    if (t + 2 < steps) step(Buf<0>{}, Buf<2>{}, Last{}, t + 2);
+    if (t < steps) step(Buf<0>{}, t);
+    if (t + 1 < steps) step(Buf<1>{}, t + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no X load may still be writing this workgroup's LDS
 
     // D layout of a 32x32 block: lane l, item r -> row (r % 4) + 8 * (r / 4) + 4 * (l / 32), column l % 32.
     if constexpr (PARTIAL) {
@@ -342,10 +400,10 @@ template <bool PARTIAL>
 __global__ __launch_bounds__(64 * NWAVE) void lut6_gemm_kernel(FQM_GEMM_ARGS) {
     gemm_tile<6, PARTIAL, BM_BIG>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
 }
-// 64-row tiles: 48 KB of LDS and at most 96 VGPRs (five waves per SIMD), so
+// 64-row tiles: 56 KB of LDS and at most 128 VGPRs (four waves per SIMD), so
 // two workgroups share a CU
 template <bool PARTIAL>
-__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(5))) void lut6_gemm_small_kernel(
+__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(4))) void lut6_gemm_small_kernel(
     FQM_GEMM_ARGS) {
     gemm_tile<6, PARTIAL, BM_SMALL>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
 }
@@ -354,7 +412,7 @@ __global__ __launch_bounds__(64 * NWAVE) void lut4_gemm_kernel(FQM_GEMM_ARGS) {
     gemm_tile<4, PARTIAL, BM_BIG>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
 }
 template <bool PARTIAL>
-__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(5))) void lut4_gemm_small_kernel(
+__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(4))) void lut4_gemm_small_kernel(
     FQM_GEMM_ARGS) {
     gemm_tile<4, PARTIAL, BM_SMALL>(X, packed, ld, lut, Y, part, M, N, K, mtiles, nt0, ksplit);
 }
