@@ -103,11 +103,16 @@ __device__ __forceinline__ uint32_t code_x256(const uint32_t* d) {
 }
 
 // Byte offset of 16-byte chunk q (k = 8q .. 8q+7) of row r in a [16][512]
-// bf16 tile.  Row r's chunks are XORed with r (and chunk bit 4 into bit 0), so
-// a quarter wave reading one chunk of 16 rows, or writing chunks 2i (or
-// 2i+1) of one row for 16 consecutive i, touches 16 distinct bank groups.
+// bf16 tile.  Rows are 1024 bytes, so every row starts in bank 0; row r's
+// chunks are XORed with a permutation of r's bits (bit 0 -> 0, 1 -> 3, 2 -> 1,
+// 3 -> 2).  The operand read of a wave (lane (r, g) reads chunk 2 g + s of
+// row r % rows, s fixed) then spreads its 16-byte pieces evenly over the 16
+// bank groups of 64 banks: two per group for 8 batch rows (32 distinct
+// pieces), four for 16 (64 pieces), the minimum for 512 and 1024 bytes.
+// A wave storing the 64 chunks of one row is conflict-free for any XOR.
 __device__ __forceinline__ uint32_t tpos(uint32_t r, uint32_t q) {
-    return r * 1024u + 16u * (q ^ r ^ ((q >> 4) & 1u));
+    const uint32_t sw = (r & 1u) | ((r & 2u) << 2) | ((r & 4u) >> 1) | ((r & 8u) >> 1);
+    return r * 1024u + 16u * (q ^ sw);
 }
 
 // XROWS: batch rows an x block holds (8 or 16, >= batch); XPT = XROWS / 8
