@@ -378,6 +378,8 @@ def main():
         roofline["stream_read_ceiling_gbs"] = ceiling["gbs"]
         roofline["frac_of_stream_read_ceiling"] = round(value / ceiling["gbs"], 4)
 
+    mix = gemm_mix_ceiling(dev) if "prefill" in res else None
+
     cpu = None
     if not args.no_cpu:
         progress("oracle CPU baseline")
@@ -401,6 +403,9 @@ def main():
         "prefill_gemm_tflops": round(res["prefill"]["tflops"], 1) if "prefill" in res else None,
         "prefill_frac_of_bf16_peak": round(res["prefill"]["frac_mfma"], 4) if "prefill" in res else None,
         "prefill_down_gemm_tflops": round(res["prefill_down"]["tflops"], 1) if "prefill_down" in res else None,
+        "prefill_gemm_mix_ceiling": mix,
+        "prefill_frac_of_mix_ceiling": (round(res["prefill"]["tflops"] / mix["tflops"], 4)
+                                        if mix and "prefill" in res else None),
         "roofline": roofline,
         "hbm_stream_read_ceiling": ceiling,
         "cpu_baseline": cpu,
@@ -459,6 +464,40 @@ def stream_read_ceiling(K, warmup, rotate_gb, dev, nbytes=69_120_000):
     return dict(kernel="stream_read_kernel (libfqm_bench.so)", bytes_per_call=nbytes,
                 us_per_call=round(us, 3), gbs=round(nbytes / us * 1e-3, 1),
                 frac_of_peak=round(nbytes / us * 1e-3 / HBM_PEAK_GBS, 4))
+
+
+def gemm_mix_ceiling(dev, slices=4000):
+    """The MFMA rate that the prefill GEMM's inner-loop instruction mix allows
+    on this GPU (gemm_mix_kernel in libfqm_bench.so: the loop's MFMAs, LDS
+    operand reads, table gathers, address VALU and barriers with no global
+    memory), one workgroup per compute unit; best of three launches."""
+    import ctypes
+    import torch
+    from dequant_matmul_amd import build as fbuild
+    if not os.path.exists(fbuild.BENCH_LIB):
+        return None
+    lib = ctypes.CDLL(fbuild.BENCH_LIB)
+    fn = lib.fqm_bench_gemm_mix
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    best = None
+    for rep in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if fn(sink.data_ptr(), cus, slices, -1.0, stream.cuda_stream):
+            raise RuntimeError("gemm mix launch failed")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3
+        if rep and (best is None or us < best):
+            best = us
+    flops = cus * 8 * slices * 8 * 32768
+    tf = flops / best / 1e6
+    return dict(kernel="gemm_mix_kernel (libfqm_bench.so)", slices=slices, us_per_launch=round(best, 1),
+                tflops=round(tf, 1), frac_of_peak=round(tf / BF16_PEAK_TFLOPS, 4))
 
 
 def traffic_record():

@@ -35,6 +35,26 @@ def test_exports_every_declared_symbol(lib):
     assert lib.fqm_version() == 4
 
 
+def test_bench_library_exports_its_references():
+    """libfqm_bench.so (the benchmark's streaming-read and GEMM-mix reference
+    kernels) loads and exports both entry points; they reject bad arguments
+    on the host."""
+    from dequant_matmul_amd import build
+    if not os.path.exists(build.BENCH_LIB):
+        build.build()
+    blib = ctypes.CDLL(build.BENCH_LIB)
+    blib.fqm_bench_stream_read.restype = ctypes.c_int
+    blib.fqm_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint32,
+                                           ctypes.c_void_p]
+    blib.fqm_bench_gemm_mix.restype = ctypes.c_int
+    blib.fqm_bench_gemm_mix.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+    assert blib.fqm_bench_stream_read(None, 1024, FAKE, 0, None) == 1
+    assert blib.fqm_bench_stream_read(FAKE + 4, 1024, FAKE, 0, None) == 1
+    assert blib.fqm_bench_gemm_mix(None, 256, 10, -1.0, None) == 1
+    assert blib.fqm_bench_gemm_mix(FAKE, 0, 10, -1.0, None) == 1
+    assert blib.fqm_bench_gemm_mix(FAKE, 256, 0, -1.0, None) == 1
+
+
 def test_status_strings(lib):
     for code in E.values():
         assert lib.fqm_status_str(code)
