@@ -179,3 +179,28 @@ def test_gemm_down_shape_sampled(M):
     W = oracle.lut6.decode(inp.codes, inp.lut)
     yo = oracle.numerics.bf16_to_f64(X[pick]) @ W.T
     assert_close(to_f64(Y)[pick], yo, "bf16", f"down M={M}")
+
+
+# K of 1 to 7 steps of 64 columns.  The main loop runs in groups of three
+# steps and the prologue requests its first tiles and codes at clamped step
+# indices, so every remainder of steps / 3 and the shortest K appear, for the
+# 64-row tiles (M = 40) and the 256-row tiles (M = 300), both code widths.
+SHORT_K_FMT = {6: (synth.lut6_input, fqm.Lut6Weights, oracle.lut6),
+               4: (synth.lut4_input, fqm.Lut4Weights, oracle.lut4)}
+
+
+@pytest.mark.parametrize("bits", [6, 4])
+@pytest.mark.parametrize("cols", [64, 128, 192, 256, 320, 448])
+@pytest.mark.parametrize("M", [40, 300])
+def test_gemm_short_k(bits, cols, M):
+    gen, W, orc = SHORT_K_FMT[bits]
+    rows, seed = 300, 50 + cols // 64
+    inp = gen(rows, cols, seed)
+    w = W.from_codes(inp.codes, inp.lut, device=DEV)
+    X = synth.activations(M, cols, seed + 1)
+    buf, Y = guarded((M, rows), torch.bfloat16)
+    print(f"lut{bits} gemm {rows}x{cols} M={M}", flush=True)
+    fqm.gemm(w, bf16_dev(X), Y=Y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(Y), orc.gemv(orc.pack_codes(inp.codes), inp.lut, X, cols), "bf16", f"lut{bits} K={cols} M={M}")
