@@ -416,6 +416,11 @@ def main():
         "prefill_gemm_mix_ceiling": mix,
         "prefill_frac_of_mix_ceiling": (round(res["prefill"]["tflops"] / mix["tflops"], 4)
                                         if mix and "prefill" in res else None),
+        # the vendor peak assumes 2.4 GHz; at the shader clock measured under
+        # matrix-core load the same units deliver proportionally less
+        "prefill_frac_of_clock_adjusted_peak": (
+            round(res["prefill"]["tflops"] / (BF16_PEAK_TFLOPS * mix["sclk_mhz"] / 2400.0), 4)
+            if mix and mix.get("sclk_mhz") and "prefill" in res else None),
         "roofline": roofline,
         "hbm_stream_read_ceiling": ceiling,
         "cpu_baseline": cpu,
@@ -440,14 +445,17 @@ def stream_read_ceiling(K, warmup, rotate_gb, dev, nbytes=69_120_000):
     lib = ctypes.CDLL(fbuild.BENCH_LIB)
     fn = lib.fqm_bench_stream_read
     fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32,
+                   ctypes.c_void_p]
     n = max(int(np.ceil(rotate_gb * 1e9 / nbytes)), warmup + 2 * K + 2)
     bufs = [torch.full((nbytes,), 1, dtype=torch.uint8, device=dev) for _ in range(n)]
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    groups = (nbytes + 32767) // 32768
+    clk = torch.zeros(2 * groups, dtype=torch.int64, device=dev)  # each call's ticks; the last call's remain
     stream = torch.cuda.current_stream()
 
     def call(s):  # on the current stream (the capture stream while a graph is captured)
-        rc = fn(bufs[s % n].data_ptr(), nbytes, sink.data_ptr(), 0xDEADBEEF,
+        rc = fn(bufs[s % n].data_ptr(), nbytes, sink.data_ptr(), clk.data_ptr(), 0xDEADBEEF,
                 torch.cuda.current_stream().cuda_stream)
         if rc:
             raise RuntimeError(f"stream read launch failed ({rc})")
@@ -469,11 +477,27 @@ def stream_read_ceiling(K, warmup, rotate_gb, dev, nbytes=69_120_000):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / K
+    sclk = shader_clock_mhz(lib, clk)
     del bufs
     torch.cuda.empty_cache()
     return dict(kernel="stream_read_kernel (libfqm_bench.so)", bytes_per_call=nbytes,
                 us_per_call=round(us, 3), gbs=round(nbytes / us * 1e-3, 1),
-                frac_of_peak=round(nbytes / us * 1e-3 / HBM_PEAK_GBS, 4))
+                frac_of_peak=round(nbytes / us * 1e-3 / HBM_PEAK_GBS, 4), sclk_mhz=sclk)
+
+
+def shader_clock_mhz(lib, clk):
+    """Median over workgroups of the shader clock a reference kernel ran at:
+    its shader-clock ticks (s_memtime) over its constant-rate ticks
+    (s_memrealtime) times the constant rate."""
+    import ctypes
+    f = lib.fqm_bench_wall_clock_khz
+    f.restype = ctypes.c_int
+    khz = f()
+    v = clk.view(-1, 2).cpu().numpy().astype(np.float64)
+    v = v[v[:, 1] > 0]
+    if not khz or len(v) == 0:
+        return None
+    return round(float(np.median(v[:, 0] / v[:, 1])) * khz / 1e3, 1)
 
 
 def gemm_mix_ceiling(dev, slices=4000):
@@ -489,25 +513,26 @@ def gemm_mix_ceiling(dev, slices=4000):
     lib = ctypes.CDLL(fbuild.BENCH_LIB)
     fn = lib.fqm_bench_gemm_mix
     fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    clk = torch.zeros(2 * cus, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
-    best = None
+    best, sclk = None, None
     for rep in range(4):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        if fn(sink.data_ptr(), cus, slices, -1.0, stream.cuda_stream):
+        if fn(sink.data_ptr(), clk.data_ptr(), cus, slices, -1.0, stream.cuda_stream):
             raise RuntimeError("gemm mix launch failed")
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3
         if rep and (best is None or us < best):
-            best = us
+            best, sclk = us, shader_clock_mhz(lib, clk)
     flops = cus * 8 * slices * 8 * 32768
     tf = flops / best / 1e6
     return dict(kernel="gemm_mix_kernel (libfqm_bench.so)", slices=slices, us_per_launch=round(best, 1),
-                tflops=round(tf, 1), frac_of_peak=round(tf / BF16_PEAK_TFLOPS, 4))
+                tflops=round(tf, 1), frac_of_peak=round(tf / BF16_PEAK_TFLOPS, 4), sclk_mhz=sclk)
 
 
 def traffic_record():

@@ -8,7 +8,7 @@ is not built, importing works but every call raises ``FqmNotBuilt``.
 
 Functions mirror the C ABI names: ``pack_bits``, ``pack``, ``unpack``,
 ``dequant``, ``workspace_size``, ``gemv``, ``gemv_static``, ``gemm_workspace_size``, ``gemm``,
-``version``,
+``version``, ``set_debug``,
 ``status_str``.  Weight descriptors are built with ``Lut6Weights``,
 ``FabqWeights`` and ``MdbfWeights``; their ``from_*`` constructors upload
 unpacked host arrays and pack them on the GPU with ``fqm_pack_bits``.
@@ -29,13 +29,13 @@ FQM_CB_SCALAR16, FQM_CB_TIERED, FQM_CB_VECTOR = 0, 1, 2
 FQM_BF16, FQM_F32 = 0, 1
 
 __all__ = [
-    "FqmError", "FqmNotBuilt", "load", "version", "status_str", "pack_bits", "pack",
+    "FqmError", "FqmNotBuilt", "load", "version", "set_debug", "status_str", "pack_bits", "pack",
     "unpack", "dequant", "workspace_size", "gemv", "gemv_static", "gemm_workspace_size", "gemm", "Lut6Weights", "Lut4Weights", "FabqWeights",
     "MdbfWeights", "SYMBOLS",
 ]
 
 # Every symbol include/fqm.h declares.
-SYMBOLS = ("fqm_version", "fqm_status_str", "fqm_pack_bits", "fqm_pack", "fqm_unpack",
+SYMBOLS = ("fqm_version", "fqm_set_debug", "fqm_status_str", "fqm_pack_bits", "fqm_pack", "fqm_unpack",
            "fqm_dequant", "fqm_workspace_size", "fqm_gemv", "fqm_gemv_static",
            "fqm_gemm_workspace_size", "fqm_gemm")
 STATIC_SCRATCH_BYTES = 16 << 20  # FQM_STATIC_SCRATCH_BYTES
@@ -101,6 +101,8 @@ def load():
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     lib.fqm_version.restype = c_int32
+    lib.fqm_set_debug.restype = c_int32
+    lib.fqm_set_debug.argtypes = [c_int32]
     lib.fqm_status_str.restype = ctypes.c_char_p
     lib.fqm_status_str.argtypes = [c_int32]
     lib.fqm_pack_bits.restype = c_int32
@@ -128,6 +130,14 @@ def load():
 
 def version() -> int:
     return load().fqm_version()
+
+
+def set_debug(on: bool) -> bool:
+    """Turn the library's debug checks on or off (``fqm_set_debug``): every
+    call then checks that each buffer lies inside one device allocation of
+    its size and waits for its kernels.  Returns the previous setting; the
+    first setting comes from the environment variable ``FQM_DEBUG``."""
+    return bool(load().fqm_set_debug(1 if on else 0))
 
 
 def status_str(status: int) -> str:

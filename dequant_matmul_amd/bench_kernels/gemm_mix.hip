@@ -29,14 +29,17 @@ typedef __attribute__((address_space(3))) const u32x4_t lds128c_t;
 constexpr int kWaves = 8, kThreads = 64 * kWaves, kBlocks = 8;  // 8 x 32 rows of X per wave
 constexpr int kX = 32768, kTab = 32768;                        // one X tile, the row tables
 
-__global__ __launch_bounds__(kThreads) void gemm_mix_kernel(float* __restrict__ sink, int slices, uint32_t seed,
-                                                            float never) {
+__global__ __launch_bounds__(kThreads) void gemm_mix_kernel(float* __restrict__ sink, uint64_t* __restrict__ clk,
+                                                            int slices, uint32_t seed, float never) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kX + kTab];
     lds8_t* const X = (lds8_t*)lds;
     lds8_t* const TAB = (lds8_t*)lds + kX;
     for (int i = threadIdx.x; i < (kX + kTab) / 4; i += kThreads)
         reinterpret_cast<uint32_t*>(lds)[i] = 0x3F803F80u + ((uint32_t)i & 0x7Fu) * 0x10001u;  // bf16 pairs in [1, 2)
     __syncthreads();
+    // shader-clock and constant-rate counters around the loop (the clock the
+    // matrix cores run at under this load)
+    const uint64_t sc0 = __builtin_amdgcn_s_memtime(), rt0 = __builtin_amdgcn_s_memrealtime();
     const int lane = threadIdx.x & 63, j = lane & 31, g = lane >> 5;
     const int wave = threadIdx.x >> 6;
     // the GEMM's gather base (row j of the wave's 32, plane and half of the wave)
@@ -91,6 +94,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mix_kernel(float* __restrict__ 
         __builtin_amdgcn_sched_barrier(0);
         if ((it & 3) == 3) __syncthreads();
     }
+    if (clk && threadIdx.x == 0) {
+        const uint64_t sc1 = __builtin_amdgcn_s_memtime(), rt1 = __builtin_amdgcn_s_memrealtime();
+        clk[2 * blockIdx.x] = sc1 - sc0;
+        clk[2 * blockIdx.x + 1] = rt1 - rt0;
+    }
     float s = 0.f;
     for (int i = 0; i < kBlocks; ++i)
         for (int r = 0; r < 16; ++r) s += acc[i][r];
@@ -101,10 +109,20 @@ __global__ __launch_bounds__(kThreads) void gemm_mix_kernel(float* __restrict__ 
 
 // Launch one compute unit's worth of the mix per workgroup on `cus`
 // workgroups, `slices` slices each.  Flops per launch:
-// cus * 8 waves * slices * 8 MFMAs * 32768.
-extern "C" int fqm_bench_gemm_mix(float* sink, int cus, int slices, float never, void* stream) {
+// cus * 8 waves * slices * 8 MFMAs * 32768.  clk (nullable, 2 * cus values):
+// per workgroup, the shader-clock ticks and the constant-rate ticks of its
+// loop (fqm_bench_wall_clock_khz gives the rate of the latter).
+extern "C" int fqm_bench_gemm_mix(float* sink, uint64_t* clk, int cus, int slices, float never, void* stream) {
     if (!sink || cus <= 0 || slices <= 0) return 1;
     hipLaunchKernelGGL(gemm_mix_kernel, dim3((unsigned)cus), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream),
-                       sink, slices, 3u, never);
+                       sink, clk, slices, 3u, never);
     return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Rate of the constant-rate counter (s_memrealtime) of the current device, kHz.
+extern "C" int fqm_bench_wall_clock_khz(void) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+    return khz;
 }

@@ -1,5 +1,6 @@
 // C ABI: argument checks on the host, then stream-ordered launches.
 // Nothing here allocates, synchronises or keeps state between calls.
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -42,6 +43,97 @@ hipError_t scratch_for_current_device(void** out) {
     }
     *out = p;
     return hipSuccess;
+}
+
+// ---- debug checks --------------------------------------------------------------
+// -1 until the first call reads FQM_DEBUG; then 0 (off) or 1 (on).
+std::atomic<int> debug_state{-1};
+
+bool debug_on() {
+    int v = debug_state.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char* e = getenv("FQM_DEBUG");
+        const int from_env = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+        int expected = -1;
+        debug_state.compare_exchange_strong(expected, from_env);
+        v = debug_state.load(std::memory_order_relaxed);
+    }
+    return v > 0;
+}
+
+// [p, p + bytes) lies inside one device allocation (nothing to check when
+// bytes <= 0).
+bool in_allocation(const void* p, int64_t bytes) {
+    if (bytes <= 0) return true;
+    if (!p) return false;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+        (void)hipGetLastError();  // not device memory: clear the sticky error
+        return false;
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+    return q >= b && (uint64_t)(q - b) + (uint64_t)bytes <= (uint64_t)size;
+}
+
+// Bytes that `rows` rows `ld` apart span when the last one needs `last` bytes.
+inline int64_t span(int64_t rows, int64_t ld, int64_t last) { return rows > 0 ? (rows - 1) * ld + last : 0; }
+
+// Every buffer of a descriptor (already checked by check_weights) at the
+// extent the kernels may touch.
+fqm_status check_weight_buffers(const fqm_weights& w) {
+    const int64_t R = w.rows, C = w.cols;
+    if (R == 0) return FQM_OK;
+    bool ok = true;
+    switch (w.format) {
+        case FQM_LUT6:
+            ok = in_allocation(w.lut6.packed, span(R, w.lut6.ld, C * 3 / 4)) && in_allocation(w.lut6.lut, R * 128);
+            break;
+        case FQM_LUT4:
+            ok = in_allocation(w.lut4.packed, span(R, w.lut4.ld, C / 2)) && in_allocation(w.lut4.lut, R * 32);
+            break;
+        case FQM_FABQ: {
+            const fqm_fabq& f = w.fabq;
+            const int64_t n_lo = R - f.n_hi, nb = C / f.blocksize;
+            const int hb = f.hi_bits ? f.hi_bits : 4;
+            ok = in_allocation(f.row_of, R * 4);
+            if (f.n_hi > 0)
+                ok = ok && in_allocation(f.q4, span(f.n_hi, f.ld_q4, C * hb / 8)) && in_allocation(f.s_hi, f.n_hi * 2);
+            if (n_lo > 0) {
+                ok = ok && in_allocation(f.signs, span(n_lo, f.ld_signs, C / 8)) &&
+                     in_allocation(f.s_blk, n_lo * nb * 2) && in_allocation(f.idx, span(n_lo, f.ld_idx, (nb + 1) / 2));
+                if (f.cb_mode == FQM_CB_SCALAR16) ok = ok && in_allocation(f.codebook, 16 * 2);
+                if (f.cb_mode == FQM_CB_TIERED) ok = ok && in_allocation(f.codebook, 4 * 64 * 2);
+                if (f.cb_mode == FQM_CB_VECTOR) ok = ok && in_allocation(f.vcodebook, 4 * 64 * 128 * 4);
+                if (f.cb_mode != FQM_CB_SCALAR16) ok = ok && in_allocation(f.tier, n_lo);
+            }
+            break;
+        }
+        case FQM_MDBF: {
+            const fqm_mdbf& f = w.mdbf;
+            for (int p = 0; p < f.P && ok; ++p) {
+                const fqm_mdbf_path& q = f.path[p];
+                ok = in_allocation(q.S_A, span(R, q.ld_A, (f.r + 7) / 8)) && in_allocation(q.S_B, span(f.r, q.ld_B, C / 8)) &&
+                     in_allocation(q.A_amp, R * f.l * 2) && in_allocation(q.B_amp, C * f.l * 2) &&
+                     in_allocation(q.Q_U, (int64_t)f.r * f.l * 2) && in_allocation(q.Q_V, (int64_t)f.r * f.l * 2);
+            }
+            break;
+        }
+        default:
+            break;
+    }
+    return ok ? FQM_OK : FQM_E_BOUNDS;
+}
+
+// After a call's launches: with the checks on (and the stream not being
+// captured), wait for the stream and turn a kernel failure into FQM_E_HIP.
+fqm_status debug_finish(fqm_status st, hipStream_t s) {
+    if (st != FQM_OK || !debug_on()) return st;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return FQM_E_HIP;
+    if (cs != hipStreamCaptureStatusNone) return st;
+    if (hipStreamSynchronize(s) != hipSuccess || hipGetLastError() != hipSuccess) return FQM_E_HIP;
+    return st;
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -137,6 +229,12 @@ extern "C" {
 
 int32_t fqm_version(void) { return FQM_VERSION; }
 
+int32_t fqm_set_debug(int32_t on) {
+    const int prev = debug_on() ? 1 : 0;
+    debug_state.store(on ? 1 : 0, std::memory_order_relaxed);
+    return prev;
+}
+
 const char* fqm_status_str(int32_t status) {
     switch (status) {
         case FQM_OK: return "ok";
@@ -148,6 +246,7 @@ const char* fqm_status_str(int32_t status) {
         case FQM_E_UNSUPPORTED: return "combination not supported";
         case FQM_E_HIP: return "HIP launch failed";
         case FQM_E_SCRATCH: return "needs more scratch than fqm_gemv_static's static maximum";
+        case FQM_E_BOUNDS: return "debug checks: a buffer is not inside one device allocation of its size";
         default: return "unknown status";
     }
 }
@@ -161,7 +260,11 @@ fqm_status fqm_pack_bits(const uint8_t* vals, uint8_t* out, int64_t rows, int64_
     if (!aligned16(out)) return FQM_E_ALIGN;
     if (ld < (cols * bits + 7) / 8) return FQM_E_SHAPE;
     if (ld & 15) return FQM_E_ALIGN;
-    return hip_status(launch_pack_bits(vals, out, rows, cols, bits, ld, d_err, as_stream(stream)));
+    if (debug_on() && !(in_allocation(vals, rows * cols) && in_allocation(out, span(rows, ld, (cols * bits + 7) / 8)) &&
+                        (!d_err || in_allocation(d_err, 4))))
+        return FQM_E_BOUNDS;
+    return debug_finish(hip_status(launch_pack_bits(vals, out, rows, cols, bits, ld, d_err, as_stream(stream))),
+                        as_stream(stream));
 }
 
 fqm_status fqm_pack(const uint8_t* codes, uint8_t* packed, int64_t rows, int64_t cols, int64_t ld,
@@ -177,7 +280,9 @@ fqm_status fqm_unpack(const uint8_t* packed, uint8_t* codes, int64_t rows, int64
     if (!aligned16(packed)) return FQM_E_ALIGN;
     if (ld < cols * 3 / 4) return FQM_E_SHAPE;
     if (ld & 15) return FQM_E_ALIGN;
-    return hip_status(launch_unpack6(packed, codes, rows, cols, ld, as_stream(stream)));
+    if (debug_on() && !(in_allocation(packed, span(rows, ld, cols * 3 / 4)) && in_allocation(codes, rows * cols)))
+        return FQM_E_BOUNDS;
+    return debug_finish(hip_status(launch_unpack6(packed, codes, rows, cols, ld, as_stream(stream))), as_stream(stream));
 }
 
 fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream) {
@@ -187,9 +292,12 @@ fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream) {
     if (w->rows == 0 || w->cols == 0) return FQM_OK;
     if (!W) return FQM_E_NULL;
     if (!aligned16(W)) return FQM_E_ALIGN;
-    if (w->format == FQM_LUT6) return hip_status(launch_dequant_lut6(*w, W, as_stream(stream)));
-    if (w->format == FQM_LUT4) return hip_status(launch_dequant_lut4(*w, W, as_stream(stream)));
-    return hip_status(launch_dequant_fabq(*w, W, as_stream(stream)));
+    if (debug_on() && (check_weight_buffers(*w) != FQM_OK || !in_allocation(W, w->rows * w->cols * 2)))
+        return FQM_E_BOUNDS;
+    hipStream_t s = as_stream(stream);
+    if (w->format == FQM_LUT6) return debug_finish(hip_status(launch_dequant_lut6(*w, W, s)), s);
+    if (w->format == FQM_LUT4) return debug_finish(hip_status(launch_dequant_lut4(*w, W, s)), s);
+    return debug_finish(hip_status(launch_dequant_fabq(*w, W, s)), s);
 }
 
 size_t fqm_workspace_size(const fqm_weights* w, int32_t batch) {
@@ -199,17 +307,13 @@ size_t fqm_workspace_size(const fqm_weights* w, int32_t batch) {
     return fqm::mdbf_workspace_bytes(*w, batch);
 }
 
-fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
-                    int32_t batch, void* workspace, size_t ws_bytes, void* stream) {
-    const fqm_status st = check_weights(w);
-    if (st != FQM_OK) return st;
-    if (batch < 1 || batch > 16) return FQM_E_SHAPE;
-    if (y_dtype != FQM_BF16 && y_dtype != FQM_F32) return FQM_E_FORMAT;
-    if (w->rows == 0) return FQM_OK;
-    if (!y || (w->cols > 0 && !x)) return FQM_E_NULL;
-    if (!aligned16(y) || (x && !aligned16(x))) return FQM_E_ALIGN;
-    const int y_f32 = y_dtype == FQM_F32;
-    hipStream_t s = as_stream(stream);
+}  // extern "C"
+
+namespace {
+
+// The launches of fqm_gemv once its arguments have passed the checks.
+fqm_status gemv_launch(const fqm_weights* w, const uint16_t* x, void* y, int y_f32, int32_t batch,
+                       void* workspace, size_t ws_bytes, hipStream_t s) {
     if (w->cols == 0)  // an empty sum: y = 0 whatever the format (x is not read)
         return hip_status(launch_zero_fill(y, (int64_t)batch * w->rows, y_f32 ? 4 : 2, s));
     switch (w->format) {
@@ -239,6 +343,37 @@ fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_
     return FQM_E_FORMAT;
 }
 
+// fqm_gemv; static_ws: the workspace is fqm_gemv_static's scratch array (a
+// device symbol, not an allocation the debug checks can look up).
+fqm_status gemv_impl(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype, int32_t batch,
+                     void* workspace, size_t ws_bytes, void* stream, bool static_ws) {
+    const fqm_status st = check_weights(w);
+    if (st != FQM_OK) return st;
+    if (batch < 1 || batch > 16) return FQM_E_SHAPE;
+    if (y_dtype != FQM_BF16 && y_dtype != FQM_F32) return FQM_E_FORMAT;
+    if (w->rows == 0) return FQM_OK;
+    if (!y || (w->cols > 0 && !x)) return FQM_E_NULL;
+    if (!aligned16(y) || (x && !aligned16(x))) return FQM_E_ALIGN;
+    const int y_f32 = y_dtype == FQM_F32;
+    hipStream_t s = as_stream(stream);
+    if (!debug_on()) return gemv_launch(w, x, y, y_f32, batch, workspace, ws_bytes, s);
+    const size_t need = w->cols > 0 ? fqm_workspace_size(w, batch) : 0;
+    if (check_weight_buffers(*w) != FQM_OK || !in_allocation(x, (int64_t)batch * w->cols * 2) ||
+        !in_allocation(y, (int64_t)batch * w->rows * (y_f32 ? 4 : 2)) ||
+        (!static_ws && workspace && !in_allocation(workspace, (int64_t)need)))
+        return FQM_E_BOUNDS;
+    return debug_finish(gemv_launch(w, x, y, y_f32, batch, workspace, ws_bytes, s), s);
+}
+
+}  // namespace
+
+extern "C" {
+
+fqm_status fqm_gemv(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
+                    int32_t batch, void* workspace, size_t ws_bytes, void* stream) {
+    return gemv_impl(w, x, y, y_dtype, batch, workspace, ws_bytes, stream, false);
+}
+
 fqm_status fqm_gemv_static(const fqm_weights* w, const uint16_t* x, void* y, int32_t y_dtype,
                            int32_t batch, void* stream) {
     const fqm_status st = check_weights(w);
@@ -248,7 +383,7 @@ fqm_status fqm_gemv_static(const fqm_weights* w, const uint16_t* x, void* y, int
     if (need > FQM_STATIC_SCRATCH_BYTES) return FQM_E_SCRATCH;
     void* ws = nullptr;
     if (need && scratch_for_current_device(&ws) != hipSuccess) return FQM_E_HIP;
-    return fqm_gemv(w, x, y, y_dtype, batch, ws, need, stream);
+    return gemv_impl(w, x, y, y_dtype, batch, ws, need, stream, true);
 }
 
 // Up to 16 rows of X go to the GEMV kernels when they have a tuned kernel
@@ -284,13 +419,20 @@ fqm_status fqm_gemm(const fqm_weights* w, const uint16_t* X, uint16_t* Y, int64_
     const size_t need = fqm_gemm_workspace_size(w, M);
     if (need && (!workspace || ws_bytes < need)) return FQM_E_WORKSPACE;
     if (need && !aligned16(workspace)) return FQM_E_ALIGN;
+    hipStream_t s = as_stream(stream);
+    if (debug_on() && (check_weight_buffers(*w) != FQM_OK || !in_allocation(X, M * w->cols * 2) ||
+                       !in_allocation(Y, M * w->rows * 2) || (need && !in_allocation(workspace, (int64_t)need))))
+        return FQM_E_BOUNDS;
+    fqm_status r;
     if (w->cols == 0)  // an empty sum: Y = 0 (the tile kernels assume at least one K step)
-        return hip_status(launch_zero_fill(Y, M * w->rows, 2, as_stream(stream)));
-    float* gws = static_cast<float*>(workspace);
-    if (gemm_as_gemv(*w, M))  // Y[M][rows] bf16 is the GEMV's y[batch][rows]
-        return hip_status(w->format == FQM_LUT4 ? launch_lut4_gemv(*w, X, Y, 0, (int)M, gws, as_stream(stream))
-                                                : launch_lut6_gemv(*w, X, Y, 0, (int)M, gws, as_stream(stream)));
-    return hip_status(launch_lut_gemm(*w, X, Y, M, workspace, ws_bytes, as_stream(stream)));
+        r = hip_status(launch_zero_fill(Y, M * w->rows, 2, s));
+    else if (gemm_as_gemv(*w, M))  // Y[M][rows] bf16 is the GEMV's y[batch][rows]
+        r = hip_status(w->format == FQM_LUT4
+                           ? launch_lut4_gemv(*w, X, Y, 0, (int)M, static_cast<float*>(workspace), s)
+                           : launch_lut6_gemv(*w, X, Y, 0, (int)M, static_cast<float*>(workspace), s));
+    else
+        r = hip_status(launch_lut_gemm(*w, X, Y, M, workspace, ws_bytes, s));
+    return debug_finish(r, s);
 }
 
 }  // extern "C"

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define FQM_VERSION 4
+#define FQM_VERSION 5
 
 /* Bytes of the device scratch array fqm_gemv_static uses on each GPU. */
 #define FQM_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
@@ -97,7 +97,8 @@ typedef enum fqm_status {
     FQM_E_WORKSPACE = 5,   /* workspace missing or smaller than fqm_workspace_size */
     FQM_E_UNSUPPORTED = 6, /* valid request this build does not implement */
     FQM_E_HIP = 7,         /* a HIP launch failed */
-    FQM_E_SCRATCH = 8      /* fqm_gemv_static: needs more than FQM_STATIC_SCRATCH_BYTES */
+    FQM_E_SCRATCH = 8,     /* fqm_gemv_static: needs more than FQM_STATIC_SCRATCH_BYTES */
+    FQM_E_BOUNDS = 9       /* debug checks: a buffer is not inside one device allocation of its size */
 } fqm_status;
 
 enum fqm_format { FQM_LUT6 = 1, FQM_FABQ = 2, FQM_MDBF = 3, FQM_LUT4 = 4 };
@@ -182,6 +183,21 @@ typedef struct fqm_weights {
 
 /* Library version (FQM_VERSION). */
 int32_t fqm_version(void);
+
+/* Debug checks on (on != 0) or off for every later call in this process;
+ * returns the previous setting.  The setting starts from the environment
+ * variable FQM_DEBUG (on unless unset, empty or "0"), read on first use.
+ * With the checks on, each call also (1) checks, before enqueuing anything,
+ * that every device buffer it would read or write, at the extent its shape
+ * and strides give, lies inside one device allocation
+ * (hipMemGetAddressRange), returning FQM_E_BOUNDS otherwise; a view into a
+ * larger allocation (a caching allocator's block) passes when it stays
+ * inside that allocation, and the static scratch of fqm_gemv_static is not
+ * checked; and (2) after enqueuing, unless the stream is being captured,
+ * waits for the stream and returns FQM_E_HIP if the call's kernels failed.
+ * The checks cost a host round trip per buffer and a stream synchronisation
+ * per call: they are for finding caller bugs, not for production runs. */
+int32_t fqm_set_debug(int32_t on);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fqm_status_str(int32_t status);

@@ -9,7 +9,7 @@ import pytest
 import dequant_matmul_amd as fqm
 from conftest import ROOT
 
-E = dict(OK=0, NULL=1, ALIGN=2, SHAPE=3, FORMAT=4, WORKSPACE=5, UNSUPPORTED=6, HIP=7)
+E = dict(OK=0, NULL=1, ALIGN=2, SHAPE=3, FORMAT=4, WORKSPACE=5, UNSUPPORTED=6, HIP=7, SCRATCH=8, BOUNDS=9)
 FAKE = 0x7f0000000000  # a 16-byte-aligned address the host never dereferences
 
 
@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert decl == set(fqm.SYMBOLS)
     for name in decl:
         assert hasattr(lib, name), name
-    assert lib.fqm_version() == 4
+    assert lib.fqm_version() == 5
 
 
 def test_bench_library_exports_its_references():
@@ -44,15 +44,17 @@ def test_bench_library_exports_its_references():
         build.build()
     blib = ctypes.CDLL(build.BENCH_LIB)
     blib.fqm_bench_stream_read.restype = ctypes.c_int
-    blib.fqm_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint32,
-                                           ctypes.c_void_p]
+    blib.fqm_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_uint32, ctypes.c_void_p]
     blib.fqm_bench_gemm_mix.restype = ctypes.c_int
-    blib.fqm_bench_gemm_mix.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
-    assert blib.fqm_bench_stream_read(None, 1024, FAKE, 0, None) == 1
-    assert blib.fqm_bench_stream_read(FAKE + 4, 1024, FAKE, 0, None) == 1
-    assert blib.fqm_bench_gemm_mix(None, 256, 10, -1.0, None) == 1
-    assert blib.fqm_bench_gemm_mix(FAKE, 0, 10, -1.0, None) == 1
-    assert blib.fqm_bench_gemm_mix(FAKE, 256, 0, -1.0, None) == 1
+    blib.fqm_bench_gemm_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_void_p]
+    assert hasattr(blib, "fqm_bench_wall_clock_khz")
+    assert blib.fqm_bench_stream_read(None, 1024, FAKE, None, 0, None) == 1
+    assert blib.fqm_bench_stream_read(FAKE + 4, 1024, FAKE, None, 0, None) == 1
+    assert blib.fqm_bench_gemm_mix(None, None, 256, 10, -1.0, None) == 1
+    assert blib.fqm_bench_gemm_mix(FAKE, None, 0, 10, -1.0, None) == 1
+    assert blib.fqm_bench_gemm_mix(FAKE, None, 256, 0, -1.0, None) == 1
 
 
 def test_status_strings(lib):
@@ -359,3 +361,25 @@ def test_fabq_variant_argument_errors(lib):
     w.fabq.ld_q4 = 512
     assert gemv(lib, w) not in (E["FORMAT"], E["SHAPE"], E["NULL"], E["ALIGN"])
     assert lib.fqm_pack_bits(FAKE, FAKE, 0, 64, 8, 64, None, None) == E["OK"]  # 8-bit fields
+
+
+def test_debug_switch_and_host_pointers(lib):
+    """fqm_set_debug returns the previous setting; with the checks on, a call
+    whose buffers are not device allocations (host addresses here) returns
+    FQM_E_BOUNDS before anything is enqueued, where the same call with the
+    checks off would have been accepted by the argument checks."""
+    prev = lib.fqm_set_debug(1)
+    try:
+        assert lib.fqm_set_debug(1) == 1
+        w = lut6()
+        assert gemv(lib, w) == E["BOUNDS"]
+        assert gemm(lib, w, M=64) == E["BOUNDS"]
+        assert lib.fqm_dequant(ctypes.byref(w), FAKE, None) == E["BOUNDS"]
+        assert lib.fqm_unpack(FAKE, FAKE, 4, 64, 48, None) == E["BOUNDS"]
+        assert lib.fqm_pack(FAKE, FAKE, 4, 64, 48, None, None) == E["BOUNDS"]
+        # argument errors still come first
+        assert gemv(lib, w, batch=0) == E["SHAPE"]
+        assert lib.fqm_status_str(E["BOUNDS"]).startswith(b"debug checks")
+    finally:
+        lib.fqm_set_debug(prev)
+    assert lib.fqm_set_debug(prev) == prev
