@@ -70,14 +70,35 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // one block, part of one, or (16-column blocks) two, so its products are
 // summed per 16-column half.  VEC: the correction is a 128-float vector
 // centroid, sum_k V[k mod 128] x[k] over the half, in fp32.
-template <int B, bool VEC>
-__global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16_t* __restrict__ x,
+// XL: x (B rows, cols % 32 == 0) is staged in LDS once per workgroup, every
+// wave then reads it there instead of through the vector L1.  16-byte piece
+// n of an x row sits at piece slot (n & ~3) | ((n & 3) ^ ((n >> 4) & 3)), so
+// that both access patterns hit 16 distinct 16-byte bank slots per 16 lanes:
+// a binary row's lane p reads pieces 4p + h (h = 0..3, one instruction each),
+// an int row's lane p reads piece p.
+template <int B, bool VEC, bool XL>
+__global__ __launch_bounds__(64 * kWaves) void fabq_gemv_kernel(fqm_fabq f, const uint16_t* __restrict__ x,
                                                         void* __restrict__ y, int y_f32,
                                                         int64_t rows, int64_t cols) {
     constexpr int UI = B == 1 ? 5 : 1;             // high-row steps per group (64 dwords of fields each)
     constexpr int UB = (B == 1 && !VEC) ? 3 : 1;   // binary steps per group (64 dwords of 32 signs each)
+    extern __shared__ __attribute__((aligned(16))) uint4 s_xl[];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    const int64_t np = cols / 8;  // 16-byte x pieces per batch row
+    if constexpr (XL) {
+        const uint4* xg = reinterpret_cast<const uint4*>(x);
+        for (int64_t g = threadIdx.x; g < B * np; g += 64 * kWaves) {
+            const int64_t b = g / np, n = g - b * np;
+            s_xl[b * np + ((n & ~3) | ((n & 3) ^ ((n >> 4) & 3)))] = xg[g];
+        }
+        __syncthreads();
+    }
+    // x piece n (8 columns) of batch row b
+    auto xpiece = [&](int b, int64_t n) -> uint4 {
+        if constexpr (XL) return s_xl[b * np + ((n & ~3) | ((n & 3) ^ ((n >> 4) & 3)))];
+        else return reinterpret_cast<const uint4*>(x + (int64_t)b * cols)[min(n, np - 1)];  // past the row: unused
+    };
     const int64_t i_u = (int64_t)blockIdx.x * kWaves + wave;  // stored row
     if (i_u >= rows) return;
     const int64_t i = i_u;
@@ -108,7 +129,7 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
                 const int64_t p = min(p0 + 64 * u + lane, nw - 1);
                 d[u] = q[p];
 #pragma unroll
-                for (int b = 0; b < B; ++b) xv[u][b] = *reinterpret_cast<const uint4*>(x + (int64_t)b * cols + 8 * p);
+                for (int b = 0; b < B; ++b) xv[u][b] = xpiece(b, p);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -148,7 +169,7 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
                 const int64_t p = min(p0 + 64 * u + lane, nw - 1);
                 d[u] = q[p];
 #pragma unroll
-                for (int b = 0; b < B; ++b) xv[u][b] = *reinterpret_cast<const uint4*>(x + (int64_t)b * cols + 8 * p);
+                for (int b = 0; b < B; ++b) xv[u][b] = xpiece(b, p);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -183,7 +204,7 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
         const uint8_t* ib = f.idx + j * f.ld_idx;
         const bool bs16 = f.blocksize == 16;
         const int wshift = bs16 ? 0 : __builtin_ctz((unsigned)f.blocksize) - 5;  // log2(sign dwords per block)
-        const int nw = (int)(cols / 32);
+        const int nw = (int)((cols + 31) / 32);  // 16-column blocks: the last dword may hold one block
         const float* vrow = VEC ? f.vcodebook + (int64_t)cbase * 128 : nullptr;
         for (int p0 = 0; p0 < nw; p0 += 64 * UB) {
             uint32_t d[UB];
@@ -197,14 +218,14 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
                 const int blk = bs16 ? 2 * p : p >> wshift;  // block of the dword's first half
                 d[u] = sg[p];
                 sbits[u][0] = sb[blk];
-                sbits[u][1] = sb[bs16 ? blk + 1 : blk];
+                sbits[u][1] = sb[bs16 ? min(blk + 1, (int)nb - 1) : blk];
                 ibits[u] = ib[blk >> 1];
                 bodd[u] = blk & 1;
 #pragma unroll
                 for (int b = 0; b < B; ++b)
 #pragma unroll
                     for (int h = 0; h < 4; ++h)
-                        xv[u][b][h] = reinterpret_cast<const uint4*>(x + (int64_t)b * cols + 32 * p)[h];
+                        xv[u][b][h] = xpiece(b, 4 * (int64_t)p + h);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -252,6 +273,11 @@ __global__ __launch_bounds__(256) void fabq_gemv_kernel(fqm_fabq f, const uint16
                                 xsum[half] = dot2_bf16(ones, xs[t], xsum[half]);
                             }
                         }
+                    }
+                    if (32 * (p0 + 64 * u + lane) + 16 >= cols) {  // the dword's second half is past the row
+                        ps[1] = 0.f;
+                        xsum[1] = 0.f;
+                        vx[1] = 0.f;
                     }
                     float a = acc[b];
                     if (VEC) {
@@ -500,15 +526,27 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(HI8 ? 
     }
 }
 
+// x goes through LDS when it takes at most this many bytes (B rows).
+constexpr int64_t kMaxXL = 64 * 1024;
+
 template <int B>
 hipError_t launch_b(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
     const unsigned grid = (unsigned)((w.rows + kWaves - 1) / kWaves);
-    if (w.fabq.cb_mode == FQM_CB_VECTOR)
-        hipLaunchKernelGGL((fabq_gemv_kernel<B, true>), dim3(grid), dim3(64 * kWaves), 0, s, w.fabq, x, y, y_f32,
-                           w.rows, w.cols);
-    else
-        hipLaunchKernelGGL((fabq_gemv_kernel<B, false>), dim3(grid), dim3(64 * kWaves), 0, s, w.fabq, x, y, y_f32,
-                           w.rows, w.cols);
+    const int64_t xl = (int64_t)B * w.cols * 2;
+    // (with vector centroids the LDS copy measured slower: those rows also
+    // stream the 128 KB centroid table through the L1)
+    const bool use_xl = w.fabq.cb_mode != FQM_CB_VECTOR && w.cols % 32 == 0 && xl <= kMaxXL;
+    if (w.fabq.cb_mode == FQM_CB_VECTOR) {
+        hipLaunchKernelGGL((fabq_gemv_kernel<B, true, false>), dim3(grid), dim3(64 * kWaves), 0, s, w.fabq, x, y,
+                           y_f32, w.rows, w.cols);
+    } else {
+        if (use_xl)
+            hipLaunchKernelGGL((fabq_gemv_kernel<B, false, true>), dim3(grid), dim3(64 * kWaves), (size_t)xl, s,
+                               w.fabq, x, y, y_f32, w.rows, w.cols);
+        else
+            hipLaunchKernelGGL((fabq_gemv_kernel<B, false, false>), dim3(grid), dim3(64 * kWaves), 0, s, w.fabq, x, y,
+                               y_f32, w.rows, w.cols);
+    }
     return hipGetLastError();
 }
 

@@ -175,3 +175,26 @@ def test_variant_invariants():
         assert np.allclose(y, W[:, k], rtol=2 ** -22, atol=0), k
     x = bf16_dev(synth.activations(5, 1536, 63))
     assert torch.equal(fqm.gemv(w, x, out_dtype=torch.float32), fqm.gemv(w, x, out_dtype=torch.float32))
+
+
+@pytest.mark.parametrize("hi_bits,cb_mode", [(4, 0), (8, 1), (4, 2)])
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_blocks_of_16_with_a_half_sign_dword(hi_bits, cb_mode, batch):
+    """16-column blocks on 1040 columns (65 blocks): each binary row's last
+    sign dword holds one block, its other half lies past the row.  x goes
+    through the L1 here (1040 is not a multiple of 32); dequantisation too."""
+    rows, cols, bs = 77, 1040, 16
+    inp, p = variant(rows, cols, 63, hi_bits, cb_mode, bs, 0.1)
+    x = synth.activations(batch, cols, 64)
+    buf, y = guarded((batch, rows), torch.float32)
+    print(f"fabq 1040 cols hi{hi_bits} cb{cb_mode} batch {batch}", flush=True)
+    w = weights(inp)
+    fqm.gemv(w, bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.fabq.gemv(p, x, rows, cols, bs, inp.n_hi), "f32",
+                 f"1040 hi{hi_bits} cb{cb_mode} b{batch}")
+    if batch == 1:
+        W = fqm.dequant(w).view(torch.int16).cpu().numpy().view(np.uint16)
+        ref = oracle.numerics.bf16_bits_from_f64_rne(oracle.fabq.decode(p, rows, cols, bs, inp.n_hi))
+        assert np.array_equal(W, ref)
