@@ -383,3 +383,20 @@ def test_debug_switch_and_host_pointers(lib):
     finally:
         lib.fqm_set_debug(prev)
     assert lib.fqm_set_debug(prev) == prev
+
+
+@pytest.mark.parametrize("env,expect", [("1", 1), ("0", 0), ("", 0), (None, 0)])
+def test_debug_setting_starts_from_the_environment(lib, env, expect):
+    """The first fqm_set_debug call returns the setting FQM_DEBUG gave
+    (a fresh process, so the variable is read on first use)."""
+    import subprocess
+    import sys
+    code = ("import ctypes, sys; sys.path.insert(0, %r); import dequant_matmul_amd as f; "
+            "l = f.load(); print(l.fqm_set_debug(0))" % ROOT)
+    e = dict(os.environ)
+    e.pop("FQM_DEBUG", None)
+    if env is not None:
+        e["FQM_DEBUG"] = env
+    out = subprocess.run([sys.executable, "-c", code], env=e, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == str(expect)
