@@ -10,23 +10,35 @@
 // so neither F, G nor W is formed.
 //
 // Both inner sums are a +-1 matrix times a few dense columns (one per
-// envelope k and batch row b).  They run on the bf16 matrix cores
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulate): a sign byte expands in
-// registers to eight exact bf16 +-1.0, and each dense fp32 column v enters
-// as three bf16 columns, h0 = bf16(v), h1 = bf16(v - h0), h2 = bf16(v - h0 -
-// h1), whose sum carries the fp32 value (u is an exact fp32 product, v a
-// rounded one).  Three launches:
+// envelope k and batch row b).  They run on v_mfma_f32_16x16x32_bf16 (fp32
+// accumulate): the +-1 matrix is the 16-row A operand, one sign byte per lane
+// and k step, and the dense columns are the B operand, 16 per column block.
+// Each dense fp32 column v enters as three bf16 columns, h0 = bf16(v),
+// h1 = bf16(v - h0), h2 = bf16(v - h0 - h1), whose sum carries the fp32 value
+// (u is an exact fp32 product, v a rounded one).
+//
+// A sign byte becomes eight bf16 +-1.0 with one byte permute and, per pair of
+// elements, one packed 16-bit shift and one v_and_or_b32.  The expansion maps
+// a set bit to -1.0 (the bf16 sign bit is the stored bit itself); the sums
+// are negated once in the epilogue, which is exact.
+//
+// Three launches:
 //   prep:   D1 = parts of u_k[i], column 3 (b l + k) + t of batch slice b / bs;
 //   pass 1: sign products over S_B, then z and D2 = parts of v_k[j];
 //   pass 2: sign products over S_A for every path, then y.
-// D1 and D2 are stored fragment-major: for each batch slice, 32-column
-// block, 256-wide K block and 16-wide k slice, the 64 lanes' 16-byte MFMA
-// operand pieces are contiguous, so every operand load is one coalesced 1 KB
-// wave read.
-// A workgroup owns 32 rows and a batch slice; its waves (16 in pass 1, 8 in
-// pass 2) split K and their partial sums are added in a fixed order in LDS,
-// so results do not depend on timing.  Columns past the logical width hold zeros in D1/D2, so the sign
-// bits read there (padding, or a clamped re-read) contribute nothing.
+// D1 and D2 are stored fragment-major: for each batch slice, 16-column block,
+// 256-wide K block and 32-wide k step, the 64 lanes' 16-byte B operand pieces
+// are contiguous.  Lane (c, q) = (lane % 16, lane / 16) holds column c at
+// k = 64 q + 8 s + e (e = 0..7) of the block, and the A operand of the same
+// lane holds sign byte 8 q + s of its row's 32 bytes for the block: both
+// operands use one k order, so only the order of the fp32 sums differs from
+// plain k order.
+// A workgroup owns 16 rows and a batch slice; its waves take the K blocks in
+// turn (wave w: blocks w, w + nw, ...), loading the next half block while
+// the current one issues its MFMAs.  The waves' partial sums are added in
+// wave order in LDS, so results do not depend on timing.  Columns past the
+// logical width hold zeros in D1/D2, so sign bits read there (the padding of
+// the last byte, or a clamped row) contribute nothing.
 #include <algorithm>
 
 #include "fqm_internal.h"
@@ -35,47 +47,47 @@ namespace fqm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NW1 = 16;      // waves per pass-1 workgroup (K split)
-constexpr int NW2 = 8;       // waves per pass-2 workgroup
-constexpr int KB = 256;      // columns per K block
+constexpr int KB = 256;      // columns per K block (8 MFMA k steps of 32)
+constexpr int BLK = 4096;    // elements of one (column block, K block) operand piece: 8 steps x 64 lanes x 8
 
 __host__ __device__ inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-// batch rows per workgroup so that its 3 l bs dense columns fit two MFMA blocks
+// batch rows per workgroup: their 3 l bs dense columns fit four 16-column blocks
 __host__ __device__ inline int batch_slice(int l) { return 3 * l >= 64 ? 1 : 64 / (3 * l); }
 
 struct MdbfDims {
     int64_t m_pad, r_pad;     // padded K widths of D1 and D2
-    int64_t nsg;              // batch slices
+    int nsg, ncb, bs;         // batch slices, 16-column blocks per slice, batch rows per slice
     int64_t d1_path, d2_path; // elements of one path's D1 / D2
     size_t d1_elems, d2_elems;
 };
 
 __host__ __device__ inline MdbfDims mdbf_dims(int64_t m, int64_t r, int l, int P, int batch) {
     MdbfDims d;
+    d.bs = batch_slice(l);
     d.m_pad = round_up(m, KB);
     d.r_pad = round_up(r, KB);
-    d.nsg = (batch + batch_slice(l) - 1) / batch_slice(l);
-    d.d1_path = d.nsg * (d.m_pad / KB) * 16384;
-    d.d2_path = d.nsg * (d.r_pad / KB) * 16384;
+    d.nsg = (batch + d.bs - 1) / d.bs;
+    d.ncb = (3 * l * std::min(d.bs, batch) + 15) / 16;
+    d.d1_path = (int64_t)d.nsg * d.ncb * d.m_pad * 16;
+    d.d2_path = (int64_t)d.nsg * d.ncb * d.r_pad * 16;
     d.d1_elems = (size_t)P * d.d1_path;
     d.d2_elems = (size_t)P * d.d2_path;
     return d;
 }
 
-// Element index of column lc (0..63) of batch slice sg at k in a fragment-major
-// operand with nkb 256-wide K blocks: slice s, lane half g, element e of k
-// within its K block follow the MFMA k order (k = 128 g + 8 s + e).
-__host__ __device__ inline int64_t dfrag_index(int64_t sg, int lc, int64_t k, int64_t nkb) {
-    const int nb = lc >> 5;
+// Element index of column col of batch slice sg at k in a fragment-major
+// operand (ncb column blocks, nkb K blocks).
+__device__ __forceinline__ int64_t dfrag_index(int sg, int ncb, int col, int64_t k, int64_t nkb) {
+    const int cb = col >> 4, c = col & 15;
     const int64_t kb = k >> 8;
     const int rem = (int)(k & 255);
-    const int g = rem >> 7, s = (rem & 127) >> 3, e = rem & 7;
-    const int lane = (lc & 31) + 32 * g;
-    return ((((sg * 2 + nb) * nkb + kb) * 16 + s) * 64 + lane) * 8 + e;
+    const int q = rem >> 6, s = (rem >> 3) & 7, e = rem & 7;
+    return (((int64_t)(sg * ncb + cb) * nkb + kb) * 8 + s) * 512 + (c + 16 * q) * 8 + e;
 }
 
 // v = h0 + h1 + h2 (bf16 parts; each remainder is exact in fp32)
@@ -86,184 +98,231 @@ __device__ __forceinline__ void split3_bf16(float v, uint16_t (&h)[3]) {
     h[2] = f32_to_bf16(r1 - bf16_to_f32(h[1]));
 }
 
-// Eight bf16 +-1.0 from one sign byte: bit e set -> +1, clear -> -1 (element e
-// of the fragment).  Dword d holds elements 2d (low half) and 2d + 1.
-__device__ __forceinline__ bf16x8 expand_signs(uint32_t byte) {
-    const uint32_t nb = ~byte;
+// Eight bf16 +-1.0 from byte S of the dword w: element e is -1.0 where bit e
+// is set, +1.0 where it is clear.  The byte goes to both 16-bit halves; for
+// the dword of elements 2d (low half) and 2d + 1 (high half) a packed shift
+// by (15 - 2d, 14 - 2d) puts those two bits at bits 15 and 31, the bf16 sign
+// bits, and v_and_or_b32 keeps them (mask = 0x80008000) and adds the
+// exponent of 1.0 (ones = 0x3F803F80).  With mask = ones = 0 the operand is
+// all zeros.  ones is held in a VGPR so that the mask can be the
+// instruction's one scalar operand.
+template <int S>
+__device__ __forceinline__ bf16x8 expand_signs_neg(uint32_t w, uint32_t mask, uint32_t ones) {
+    constexpr uint32_t sel = 0x0C000C00u | (uint32_t)(S << 16) | (uint32_t)S;
+    const u16x2 p = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(w, w, sel));
     u32x4 v;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const uint32_t t = (nb >> (2 * d)) & 3u;
-        v[d] = 0x3F803F80u | (((t | (t << 15)) & 0x10001u) << 15);
+        const u16x2 t = p << (u16x2){(unsigned short)(15 - 2 * d), (unsigned short)(14 - 2 * d)};
+        v[d] = (__builtin_bit_cast(uint32_t, t) & mask) | ones;
     }
     return __builtin_bit_cast(bf16x8, v);
 }
 
 // D1 of path p: parts of u_k[i] at column 3 (b l + k) + t of batch slice
-// b / bs; zero for i >= m.
+// b / bs; zero for i >= m.  One thread writes one lane's 16-byte piece of one
+// k step: grid (2 nkb, nsg ncb, P), 256 threads = 4 k steps x 64 lanes.
 __global__ __launch_bounds__(256) void mdbf_prep(fqm_mdbf md, const uint16_t* __restrict__ x,
-                                                 uint16_t* __restrict__ D1, int64_t m, int batch,
-                                                 int64_t m_pad, int64_t d1_path) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (p, b, k, i)
-    const int l = md.l;
-    const int64_t per_p = (int64_t)batch * l * m_pad;
-    if (t >= per_p * md.P) return;
-    const int p = (int)(t / per_p);
-    int64_t rem = t - p * per_p;
-    const int b = (int)(rem / ((int64_t)l * m_pad));
-    rem -= (int64_t)b * l * m_pad;
-    const int k = (int)(rem / m_pad);
-    const int64_t i = rem - (int64_t)k * m_pad;
-    // the two paths' pointers are selected as values (p varies per thread)
+                                                 uint16_t* __restrict__ D1, int64_t m, int batch, int nsg,
+                                                 int ncb, int64_t nkb, int64_t d1_path) {
+    const int lane = threadIdx.x & 63;
+    const int64_t kb = blockIdx.x >> 1;
+    const int s = 4 * (blockIdx.x & 1) + (threadIdx.x >> 6);
+    const int sg = blockIdx.y / ncb, cb = blockIdx.y - sg * ncb;
+    const int p = blockIdx.z;
+    const int l = md.l, bs = batch_slice(l);
+    const int c = lane & 15, q = lane >> 4;
+    const int col = 16 * cb + c;
+    const int nrows = min(bs, batch - sg * bs);
+    if (col >= 3 * l * nrows) return;  // never read
+    const int bl = col / (3 * l), rem = col - bl * 3 * l, k = rem / 3, t3 = rem - 3 * k;
+    const int64_t b = (int64_t)sg * bs + bl;
+    const int64_t i0 = kb * KB + 64 * q + 8 * s;
     const uint16_t* bamp = p == 0 ? md.path[0].B_amp : md.path[1].B_amp;
-    uint16_t h[3] = {0, 0, 0};
-    if (i < m) split3_bf16(fp16_to_f32(bamp[i * l + k]) * bf16_to_f32(x[(int64_t)b * m + i]), h);
-    const int bs = batch_slice(l);
-    const int sg = b / bs, bl = b - sg * bs;
-    uint16_t* dp = D1 + (int64_t)p * d1_path;
+    u32x4 out;
 #pragma unroll
-    for (int t3 = 0; t3 < 3; ++t3) dp[dfrag_index(sg, 3 * (bl * l + k) + t3, i, m_pad / KB)] = h[t3];
+    for (int e = 0; e < 8; e += 2) {
+        uint16_t h0[3] = {0, 0, 0}, h1[3] = {0, 0, 0};
+        const int64_t i = i0 + e;
+        if (i < m) {  // m is a multiple of 32, so i + 1 < m as well
+            split3_bf16(fp16_to_f32(bamp[i * l + k]) * bf16_to_f32(x[b * m + i]), h0);
+            split3_bf16(fp16_to_f32(bamp[(i + 1) * l + k]) * bf16_to_f32(x[b * m + i + 1]), h1);
+        }
+        const uint16_t lo = t3 == 0 ? h0[0] : t3 == 1 ? h0[1] : h0[2];
+        const uint16_t hi = t3 == 0 ? h1[0] : t3 == 1 ? h1[1] : h1[2];
+        out[e >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    uint16_t* dp = D1 + (int64_t)p * d1_path + (((int64_t)(sg * ncb + cb) * nkb + kb) * 8 + s) * 512 + 8 * lane;
+    *reinterpret_cast<u32x4*>(dp) = out;
 }
 
-// Sign products for one path: acc[nb] = S[row0 .. row0 + 31][:] * (dense columns 32 nb + (0..31) of
-// batch slice sg)^T over this wave's K blocks.  k order inside a 256-column block: slice s, lane
-// half g, element e -> column 128 g + 8 s + e (the same order for both operands).
+// The dense pieces of one half block (4 k steps) of NB column blocks.
 template <int NB>
+struct Half {
+    u32x4 d[NB][4];
+};
+
+// Sign products for one path: acc[nb] = -(S[row0 .. row0 + 15][:] * (dense
+// columns 16 nb + (0..15) of batch slice sg)^T) over this wave's K blocks,
+// wave, wave + nw, ..., in chunks of BPW blocks.  A chunk is straight-line
+// code with no branch between a load and its use, so the loads stay where
+// they are written and the waits before the MFMAs are exact:
+// - the sign dwords of the whole chunk (the stream from HBM) go out first;
+// - the dense pieces (L2) run AHEAD half blocks ahead of their MFMAs;
+// - a block past nkb re-reads block nkb - 1 and its A operand is all zeros
+//   (the launch picks BPW so that such blocks are rare).
+// Reads stay inside the operands:
+// - a row's signs are its first kbytes = ceil(K / 8) bytes; a dword piece at
+//   or past them is read at the last dword that starts inside them (at most
+//   3 bytes past kbytes, inside the row's ld), and the dense operand is zero
+//   for every k >= K, so whatever those bits hold adds nothing;
+// - a lane whose column is at or past cend reads the piece of column
+//   cend - 1 (the same bytes as a live lane of the instruction) and only
+//   feeds result columns that are never read.
+template <int NB, int BPW>
 __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int64_t ldS, int64_t rows,
-                                              const uint16_t* __restrict__ D, int64_t nkb, int64_t sg,
-                                              int64_t row0, int cend, int blk0, int blk1, f32x16 (&acc)[NB]) {
-    const int lane = threadIdx.x & 63, g = lane >> 5, j = lane & 31;
-    const uint8_t* srow = S + min(row0 + j, rows - 1) * ldS;
-    const int64_t last16 = ldS - 16;  // the last 16-byte piece inside a row
-    // this lane's 16-byte pieces of column block nb (columns past cend read as zeros)
+                                              int64_t kbytes, const uint16_t* __restrict__ D, int64_t nkb,
+                                              int sg, int ncb, int64_t row0, int cend, int wave, int nw,
+                                              f32x4 (&acc)[NB]) {
+    constexpr int T = 2 * BPW;                                  // half blocks per chunk
+    constexpr int AHEAD = T == 2 || NB > 1 || BPW > 4 ? 1 : 2;  // dense half blocks in flight ahead (fits the VGPRs)
+    constexpr int NBUF = AHEAD + 1;
+    const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
+    const uint8_t* srow = S + min(row0 + c, rows - 1) * ldS;
+    const int64_t klast = (kbytes - 1) & ~(int64_t)3;
     const uint16_t* dcol[NB];
-    bool dvalid[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        dvalid[nb] = 32 * nb + j < cend;
-        dcol[nb] = D + (sg * 2 + nb) * nkb * 8192 + 8 * lane;
+        const int col = min(16 * nb + c, cend - 1);
+        dcol[nb] = D + (int64_t)(sg * ncb + (col >> 4)) * nkb * BLK + 8 * ((col & 15) + 16 * q);
     }
-    for (int blk = blk0; blk < blk1; ++blk) {
-        const u32x4 sb = *reinterpret_cast<const u32x4*>(srow + min((int64_t)(32 * blk + 16 * g), last16));
-        // a clamped re-read only happens where the dense columns are zero;
-        // lanes of columns past cend fetch nothing; the 16 k slices go in
-        // groups of 8 / NB to bound the live operands
-        constexpr int SG = 8 / NB;
+    uint32_t ones;
+    asm("v_mov_b32 %0, 0x3f803f80" : "=v"(ones));
+    for (int64_t base = wave; base < nkb; base += (int64_t)BPW * nw) {
+        int64_t blk[BPW];
+        uint32_t sgn[T];
 #pragma unroll
-        for (int s0 = 0; s0 < 16; s0 += SG) {
-            bf16x8 bf[NB][SG];
+        for (int j = 0; j < BPW; ++j) {
+            blk[j] = min(base + (int64_t)j * nw, nkb - 1);
+            const int64_t off = 32 * blk[j] + 8 * q;
+            sgn[2 * j] = *reinterpret_cast<const uint32_t*>(srow + min(off, klast));
+            sgn[2 * j + 1] = *reinterpret_cast<const uint32_t*>(srow + min(off + 4, klast));
+        }
+        Half<NB> hb[NBUF];
+        auto load_d = [&](int t) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int s = 0; s < SG; ++s) {
-                    u32x4 v = {0u, 0u, 0u, 0u};
-                    if (dvalid[nb]) v = *reinterpret_cast<const u32x4*>(dcol[nb] + (int64_t)8192 * blk + 512 * (s0 + s));
-                    bf[nb][s] = __builtin_bit_cast(bf16x8, v);
-                }
+                for (int s = 0; s < 4; ++s)
+                    hb[t % NBUF].d[nb][s] =
+                        *reinterpret_cast<const u32x4*>(dcol[nb] + blk[t / 2] * BLK + 512 * (4 * (t % 2) + s));
+        };
 #pragma unroll
-            for (int s = 0; s < SG; ++s) {
-                const int ss = s0 + s;
-                const bf16x8 a = expand_signs((sb[ss >> 2] >> (8 * (ss & 3))) & 255u);
+        for (int t = 0; t < AHEAD; ++t) load_d(t);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            if (t + AHEAD < T) load_d(t + AHEAD);
+            // the machine scheduler would otherwise move each load down to
+            // its first use (to lower register pressure), so that every MFMA
+            // waited for its own load
+            __builtin_amdgcn_sched_barrier(0);
+            const bool live = base + (int64_t)(t / 2) * nw < nkb;  // uniform over the wave
+            const uint32_t mask = live ? 0x80008000u : 0u, one = live ? ones : 0u;
+            bf16x8 a[4];
+            a[0] = expand_signs_neg<0>(sgn[t], mask, one);
+            a[1] = expand_signs_neg<1>(sgn[t], mask, one);
+            a[2] = expand_signs_neg<2>(sgn[t], mask, one);
+            a[3] = expand_signs_neg<3>(sgn[t], mask, one);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[nb][s], acc[nb], 0, 0, 0);
-            }
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a[s], __builtin_bit_cast(bf16x8, hb[t % NBUF].d[nb][s]), acc[nb], 0, 0, 0);
         }
     }
 }
 
-// Sum of the NW waves' partial blocks in a fixed tree order (waves w and
-// w + h for h = NW / 2, ..., 2, 1) into red[nb][row][col] (LDS).  D layout of a 32x32
-// block: lane l, item q -> row (q % 4) + 8 (q / 4) + 4 (l / 32), column l % 32.
-template <int NB, int NW>
-__device__ __forceinline__ void reduce_waves(f32x16 (&acc)[NB], float* buf, float* red) {
+// Sum of the nw waves' 16 x 16NB partial blocks in wave order into tot
+// (LDS), negated: D layout of a 16x16 block is lane l, item i -> row
+// 4 (l / 16) + i, column l % 16.  red holds nw x NB x 64 float4.
+template <int NB>
+__device__ __forceinline__ void reduce_waves(const f32x4 (&acc)[NB], f32x4* red, float* tot, int nw) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-    for (int h = NW / 2; h >= 1; h >>= 1) {
-        if (wave >= h && wave < 2 * h) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) buf[(((wave - h) * NB + nb) * 16 + q) * 64 + lane] = acc[nb][q];
-        }
-        __syncthreads();
-        if (wave < h) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[nb][q] += buf[((wave * NB + nb) * 16 + q) * 64 + lane];
-        }
-        __syncthreads();
-    }
-    if (wave == 0) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int row = (q & 3) + 8 * (q >> 2) + 4 * (lane >> 5), col = lane & 31;
-                red[(nb * 32 + row) * 32 + col] = acc[nb][q];
-            }
+    for (int nb = 0; nb < NB; ++nb) red[(wave * NB + nb) * 64 + lane] = acc[nb];
+    __syncthreads();
+    for (int e = tid; e < NB * 256; e += 64 * nw) {
+        const int nb = e >> 8, ln = (e >> 2) & 63, i = e & 3;
+        float v = 0.f;
+        for (int w = 0; w < nw; ++w) v += red[(w * NB + nb) * 64 + ln][i];
+        tot[e] = -v;
     }
     __syncthreads();
 }
 
-// Pass 1: rows j of S_B; D1 columns of batch slice [b0, b0 + bs).  Writes
-// D2[p][c][j] = parts of Q_U[j][k] z[j] (zero for j >= r, which the grid
+// Column col, row (0..15) of the reduced tile.
+__device__ __forceinline__ float tot_at(const float* tot, int col, int row) {
+    return tot[(col >> 4) * 256 + ((col & 15) + 16 * (row >> 2)) * 4 + (row & 3)];
+}
+
+// Most waves per workgroup: pass 1 with one column block 16 (its operands
+// fit the 128 VGPRs of a 16-wave group), else 8.  The launch keeps every
+// floor on the wave count (at most 6) under this.
+template <int NB, int PASS>
+constexpr int nw_max() { return NB == 1 && PASS == 1 ? 16 : 8; }
+
+// Pass 1: rows j of S_B; D1 columns of batch slice blockIdx.y.  Writes
+// D2[p][.][j] = parts of Q_U[j][k] z[j] (zero for j >= r, which the grid
 // covers up to r_pad).
-template <int NB>
-__global__ __launch_bounds__(64 * NW1) void mdbf_pass1(fqm_mdbf md, const uint16_t* __restrict__ D1,
-                                                      uint16_t* __restrict__ D2, int64_t m, int batch,
-                                                      int64_t m_pad, int64_t r_pad, int64_t d1_path,
-                                                      int64_t d2_path) {
-    __shared__ float red_buf[NW1 / 2 * NB * 1024];
-    __shared__ float red[NB * 1024];
-    __shared__ float qv_s[32 * 16], qu_s[32 * 16];  // Q_V, Q_U rows j0 .. j0 + 31
+template <int NB, int BPW>
+__global__ __launch_bounds__((64 * nw_max<NB, 1>())) void mdbf_pass1(fqm_mdbf md, const uint16_t* __restrict__ D1,
+                                                        uint16_t* __restrict__ D2, int64_t m, int batch, int ncb,
+                                                        int64_t m_pad, int64_t r_pad, int64_t d1_path,
+                                                        int64_t d2_path) {
+    __shared__ f32x4 red[nw_max<NB, 1>() * NB * 64];
+    __shared__ float tot[NB * 256];
+    __shared__ float qv_s[16 * 16], qu_s[16 * 16];  // Q_V, Q_U rows j0 .. j0 + 15
     const int p = blockIdx.z;
     const fqm_mdbf_path path = p == 0 ? md.path[0] : md.path[1];
     const int l = md.l;
     const int64_t r = md.r;
     const int bs = batch_slice(l);
-    const int b0 = blockIdx.y * bs, nb_rows = min(bs, batch - b0);
-    const int64_t j0 = (int64_t)blockIdx.x * 32;
-    // the epilogue's envelope values, fetched before the long sign products
-    // (rows j0 .. j0 + 31 of the [r][l] arrays are one contiguous run)
+    const int sg = blockIdx.y;
+    const int b0 = sg * bs, nb_rows = min(bs, batch - b0);
+    const int64_t j0 = (int64_t)blockIdx.x * 16;
+    const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
+    // the epilogue's envelope values, fetched before the sign products
     // (unconditional loads at a clamped index, so that no wait lands here)
     const int64_t qo = j0 * l + threadIdx.x;
-    const bool qin = threadIdx.x < 32 * l && qo < r * l;
+    const bool qin = threadIdx.x < 16 * l && qo < r * l;
     const int64_t qoc = min(qo, r * l - 1);
     const uint16_t qv_l = path.Q_V[qoc], qu_l = path.Q_U[qoc];
     const uint16_t qv_h = qin ? qv_l : 0, qu_h = qin ? qu_l : 0;
-    const uint16_t* Dp = D1 + (int64_t)p * d1_path;
-    const int wave = threadIdx.x >> 6;
-    const int nblk = (int)(m_pad / KB);
-    const int per = (nblk + NW1 - 1) / NW1;
-    const int blk0 = min(wave * per, nblk), blk1 = min(blk0 + per, nblk);
 
-    f32x16 acc[NB];
+    f32x4 acc[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[nb][q] = 0.f;
-    sign_products<NB>(path.S_B, path.ld_B, r, Dp, nblk, blockIdx.y, j0, 3 * l * nb_rows, blk0, blk1, acc);
-    if (threadIdx.x < 32 * l) {
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (j0 < r)
+        sign_products<NB, BPW>(path.S_B, path.ld_B, r, m / 8, D1 + (int64_t)p * d1_path, m_pad / KB, sg, ncb, j0,
+                          3 * l * nb_rows, wave, nw, acc);
+    if (threadIdx.x < 16 * l) {
         qv_s[threadIdx.x] = fp16_to_f32(qv_h);
         qu_s[threadIdx.x] = fp16_to_f32(qu_h);
     }
-    reduce_waves<NB, NW1>(acc, red_buf, red);  // ends with a barrier
+    reduce_waves<NB>(acc, red, tot, nw);  // ends with a barrier
 
     // one thread per (row, batch row of the slice)
     uint16_t* D2p = D2 + (int64_t)p * d2_path;
-    for (int e = threadIdx.x; e < 32 * bs; e += 64 * NW1) {
-        const int jr = e & 31, bl = e >> 5;
+    const int64_t nkb2 = r_pad / KB;
+    for (int e = threadIdx.x; e < 16 * nb_rows; e += blockDim.x) {
+        const int jr = e & 15, bl = e >> 4;
         const int64_t jj = j0 + jr;
-        if (bl >= nb_rows) continue;
         float z = 0.f;
         if (jj < r) {
             for (int k = 0; k < l; ++k) {
                 const int cl = 3 * (bl * l + k);
-                float t = 0.f;
-#pragma unroll
-                for (int t3 = 0; t3 < 3; ++t3) t += red[((cl + t3) >> 5) * 1024 + jr * 32 + ((cl + t3) & 31)];
+                const float t = tot_at(tot, cl, jr) + tot_at(tot, cl + 1, jr) + tot_at(tot, cl + 2, jr);
                 z = fmaf(qv_s[jr * l + k], t, z);
             }
         }
@@ -271,101 +330,134 @@ __global__ __launch_bounds__(64 * NW1) void mdbf_pass1(fqm_mdbf md, const uint16
             uint16_t h[3] = {0, 0, 0};
             if (jj < r) split3_bf16(qu_s[jr * l + k] * z, h);
 #pragma unroll
-            for (int t3 = 0; t3 < 3; ++t3) D2p[dfrag_index(blockIdx.y, 3 * (bl * l + k) + t3, jj, r_pad / KB)] = h[t3];
+            for (int t3 = 0; t3 < 3; ++t3) D2p[dfrag_index(sg, ncb, 3 * (bl * l + k) + t3, jj, nkb2)] = h[t3];
         }
     }
 }
 
-// Pass 2: rows i of S_A, summed over the paths; D2 columns of batch slice [b0, b0 + bs).
-template <int NB>
-__global__ __launch_bounds__(64 * NW2) void mdbf_pass2(fqm_mdbf md, const uint16_t* __restrict__ D2,
-                                                      void* __restrict__ y, int y_f32, int64_t n, int batch,
-                                                      int64_t r_pad, int64_t d2_path) {
-    __shared__ float red_buf[NW2 / 2 * NB * 1024];
-    __shared__ float red[NB * 1024];
-    __shared__ float amp_s[2][32 * 16];  // A_amp rows i0 .. i0 + 31 of each path
+// Pass 2: rows i of S_A, summed over the paths; D2 columns of batch slice blockIdx.y.
+template <int NB, int BPW>
+__global__ __launch_bounds__((64 * nw_max<NB, 2>())) void mdbf_pass2(fqm_mdbf md, const uint16_t* __restrict__ D2,
+                                                        void* __restrict__ y, int y_f32, int64_t n, int batch,
+                                                        int ncb, int64_t r_pad, int64_t d2_path) {
+    __shared__ f32x4 red[nw_max<NB, 2>() * NB * 64];
+    __shared__ float tot[NB * 256];
+    __shared__ float amp_s[2][16 * 16];  // A_amp rows i0 .. i0 + 15 of each path
     const int l = md.l;
     const int64_t r = md.r;
     const int bs = batch_slice(l);
-    const int b0 = blockIdx.y * bs, nb_rows = min(bs, batch - b0);
-    const int64_t i0 = (int64_t)blockIdx.x * 32;
-    // the epilogue's envelope values, fetched before the long sign products
+    const int sg = blockIdx.y;
+    const int b0 = sg * bs, nb_rows = min(bs, batch - b0);
+    const int64_t i0 = (int64_t)blockIdx.x * 16;
+    const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
+    // the epilogue's envelope values, fetched before the sign products
     // (unconditional loads at a clamped index, path 0 standing in for a
     // missing path 1, so that no wait lands here)
     uint16_t amp_h[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int64_t ao = i0 * l + threadIdx.x;
-        const bool ain = p < md.P && threadIdx.x < 32 * l && ao < n * l;
+        const bool ain = p < md.P && threadIdx.x < 16 * l && ao < n * l;
         const uint16_t* ap = p < md.P ? md.path[p].A_amp : md.path[0].A_amp;
         const uint16_t a_l = ap[min(ao, n * l - 1)];
         amp_h[p] = ain ? a_l : 0;
     }
-    const int wave = threadIdx.x >> 6;
-    const int nblk = (int)(r_pad / KB);
-    const int per = (nblk + NW2 - 1) / NW2;
-    const int blk0 = min(wave * per, nblk), blk1 = min(blk0 + per, nblk);
+    const int64_t nkb = r_pad / KB;
 
-    float out[2] = {0.f, 0.f};  // (row, batch row) pairs e = tid, tid + 512 of this thread
+    float out = 0.f;  // (row, batch row) pair e = tid of this thread (the launch gives 64 nw >= 16 bs)
+    const int ir = threadIdx.x & 15, bl = threadIdx.x >> 4;
     for (int p = 0; p < md.P; ++p) {
         const fqm_mdbf_path path = p == 0 ? md.path[0] : md.path[1];
-        f32x16 acc[NB];
+        f32x4 acc[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[nb][q] = 0.f;
-        sign_products<NB>(path.S_A, path.ld_A, n, D2 + (int64_t)p * d2_path, nblk, blockIdx.y, i0, 3 * l * nb_rows,
-                          blk0, blk1, acc);
-        if (p == 0 && threadIdx.x < 32 * l) {
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        sign_products<NB, BPW>(path.S_A, path.ld_A, n, (r + 7) / 8, D2 + (int64_t)p * d2_path, nkb, sg, ncb, i0,
+                          3 * l * nb_rows, wave, nw, acc);
+        if (p == 0 && threadIdx.x < 16 * l) {
             amp_s[0][threadIdx.x] = fp16_to_f32(amp_h[0]);
             amp_s[1][threadIdx.x] = fp16_to_f32(amp_h[1]);
         }
-        reduce_waves<NB, NW2>(acc, red_buf, red);  // ends with a barrier
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int e = threadIdx.x + 64 * NW2 * h;
-            const int ir = e & 31, bl = e >> 5;
-            const int64_t ii = i0 + ir;
-            if (bl >= nb_rows || ii >= n) continue;
-            float v = out[h];
+        reduce_waves<NB>(acc, red, tot, nw);  // ends with a barrier
+        if (bl < nb_rows && i0 + ir < n) {
+            float v = out;
             for (int k = 0; k < l; ++k) {
                 const int cl = 3 * (bl * l + k);
-                float t = 0.f;
-#pragma unroll
-                for (int t3 = 0; t3 < 3; ++t3) t += red[((cl + t3) >> 5) * 1024 + ir * 32 + ((cl + t3) & 31)];
+                const float t = tot_at(tot, cl, ir) + tot_at(tot, cl + 1, ir) + tot_at(tot, cl + 2, ir);
                 v = fmaf(amp_s[p][ir * l + k], t, v);
             }
-            out[h] = v;
+            out = v;
         }
-        __syncthreads();  // red is rewritten by the next path
+        __syncthreads();  // red and tot are rewritten by the next path
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int e = threadIdx.x + 64 * NW2 * h;
-        const int ir = e & 31, bl = e >> 5;
-        const int64_t ii = i0 + ir;
-        if (bl >= nb_rows || ii >= n) continue;
-        const int64_t o = (int64_t)(b0 + bl) * n + ii;
+    if (bl < nb_rows && i0 + ir < n) {
+        const int64_t o = (int64_t)(b0 + bl) * n + i0 + ir;
         if (y_f32)
-            reinterpret_cast<float*>(y)[o] = out[h];
+            reinterpret_cast<float*>(y)[o] = out;
         else
-            reinterpret_cast<uint16_t*>(y)[o] = f32_to_bf16(out[h]);
+            reinterpret_cast<uint16_t*>(y)[o] = f32_to_bf16(out);
     }
 }
 
-template <int NB>
-hipError_t launch_nb(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch, uint16_t* D1,
-                     uint16_t* D2, const MdbfDims& d, hipStream_t s) {
-    const fqm_mdbf& md = w.mdbf;
-    const int bs = batch_slice(md.l);
-    const unsigned gy = (unsigned)((batch + bs - 1) / bs);
-    hipLaunchKernelGGL((mdbf_pass1<NB>), dim3((unsigned)(d.r_pad / 32), gy, (unsigned)md.P), dim3(64 * NW1), 0, s,
-                       md, D1, D2, w.cols, batch, d.m_pad, d.r_pad, d.d1_path, d.d2_path);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mdbf_pass2<NB>), dim3((unsigned)((w.rows + 31) / 32), gy), dim3(64 * NW2), 0, s, md, D2, y,
-                       y_f32, w.rows, batch, d.r_pad, d.d2_path);
+// Blocks per wave and chunk (1, 2, 4 or 8) and waves per workgroup for nkb
+// K blocks with at most cap waves: per = ceil(nkb / cap) blocks each, rounded
+// up to a power of two, then as few waves as hold nkb blocks (at least floor);
+// past 8 blocks per wave the waves go over their blocks in chunks of 8.
+struct Split {
+    int bpw, nw;
+};
+inline Split split_k(int64_t nkb, int cap, int floor) {
+    const int64_t per = (nkb + cap - 1) / cap;
+    const int bpw = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
+    const int64_t nw = std::min<int64_t>(cap, (nkb + bpw - 1) / bpw);
+    return {bpw, (int)std::max<int64_t>(floor, nw)};
+}
+
+template <int NB, int BPW>
+hipError_t launch_pass1(const fqm_weights& w, int batch, uint16_t* D1, uint16_t* D2, const MdbfDims& d, int nw,
+                        hipStream_t s) {
+    hipLaunchKernelGGL((mdbf_pass1<NB, BPW>), dim3((unsigned)(d.r_pad / 16), (unsigned)d.nsg, (unsigned)w.mdbf.P),
+                       dim3(64 * nw), 0, s, w.mdbf, D1, D2, w.cols, batch, d.ncb, d.m_pad, d.r_pad, d.d1_path,
+                       d.d2_path);
     return hipGetLastError();
+}
+
+template <int NB, int BPW>
+hipError_t launch_pass2(const fqm_weights& w, void* y, int y_f32, int batch, uint16_t* D2, const MdbfDims& d,
+                        int nw, hipStream_t s) {
+    hipLaunchKernelGGL((mdbf_pass2<NB, BPW>), dim3((unsigned)((w.rows + 15) / 16), (unsigned)d.nsg), dim3(64 * nw),
+                       0, s, w.mdbf, D2, y, y_f32, w.rows, batch, d.ncb, d.r_pad, d.d2_path);
+    return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_nb(const fqm_weights& w, void* y, int y_f32, int batch, uint16_t* D1, uint16_t* D2,
+                     const MdbfDims& d, hipStream_t s) {
+    const fqm_mdbf& md = w.mdbf;
+    constexpr int NWM1 = nw_max<NB, 1>(), NWM2 = nw_max<NB, 2>();
+    // At least one thread per envelope value of the tile's 16 rows (16 l <=
+    // 256), and in pass 2 one per (row, batch row) of the slice (16 bs <=
+    // 16 * 21).  At most enough waves per tile that tiles x waves is about
+    // 4096 (16 waves per CU, all resident at once), and NWM1 / NWM2.
+    const int env = (16 * md.l + 63) / 64;
+    const int64_t t1 = d.r_pad / 16 * d.nsg * md.P, t2 = (w.rows + 15) / 16 * d.nsg;
+    const int f2 = std::max(env, (16 * std::min(d.bs, batch) + 63) / 64);
+    const int c1 = (int)std::min<int64_t>(NWM1, std::max<int64_t>(env, (4096 + t1 - 1) / t1));
+    const int c2 = (int)std::min<int64_t>(NWM2, std::max<int64_t>(f2, (4096 + t2 - 1) / t2));
+    const Split k1 = split_k(d.m_pad / KB, c1, env), k2 = split_k(d.r_pad / KB, c2, f2);
+    hipError_t e;
+    switch (k1.bpw) {
+        case 1: e = launch_pass1<NB, 1>(w, batch, D1, D2, d, k1.nw, s); break;
+        case 2: e = launch_pass1<NB, 2>(w, batch, D1, D2, d, k1.nw, s); break;
+        case 4: e = launch_pass1<NB, 4>(w, batch, D1, D2, d, k1.nw, s); break;
+        default: e = launch_pass1<NB, 8>(w, batch, D1, D2, d, k1.nw, s); break;
+    }
+    if (e != hipSuccess) return e;
+    switch (k2.bpw) {
+        case 1: return launch_pass2<NB, 1>(w, y, y_f32, batch, D2, d, k2.nw, s);
+        case 2: return launch_pass2<NB, 2>(w, y, y_f32, batch, D2, d, k2.nw, s);
+        case 4: return launch_pass2<NB, 4>(w, y, y_f32, batch, D2, d, k2.nw, s);
+        default: return launch_pass2<NB, 8>(w, y, y_f32, batch, D2, d, k2.nw, s);
+    }
 }
 
 }  // namespace
@@ -381,15 +473,14 @@ hipError_t launch_mdbf_gemv(const fqm_weights& w, const uint16_t* x, void* y, in
     const MdbfDims d = mdbf_dims(w.cols, md.r, md.l, md.P, batch);
     uint16_t* D1 = static_cast<uint16_t*>(ws);
     uint16_t* D2 = D1 + d.d1_elems;
-    const int64_t nprep = (int64_t)md.P * batch * md.l * d.m_pad;
-    hipLaunchKernelGGL(mdbf_prep, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, s, md, x, D1, w.cols, batch,
-                       d.m_pad, d.d1_path);
+    hipLaunchKernelGGL(mdbf_prep, dim3((unsigned)(2 * d.m_pad / KB), (unsigned)(d.nsg * d.ncb), (unsigned)md.P),
+                       dim3(256), 0, s, md, x, D1, w.cols, batch, d.nsg, d.ncb, d.m_pad / KB, d.d1_path);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int bs = batch_slice(md.l);
-    const int cols_per_wg = 3 * md.l * std::min(bs, batch);
-    return cols_per_wg <= 32 ? launch_nb<1>(w, x, y, y_f32, batch, D1, D2, d, s)
-                             : launch_nb<2>(w, x, y, y_f32, batch, D1, D2, d, s);
+    // two to four column blocks share the four-block kernels (a block past
+    // ncb re-reads a live column and its results are not read)
+    return d.ncb == 1 ? launch_nb<1>(w, y, y_f32, batch, D1, D2, d, s)
+                      : launch_nb<4>(w, y, y_f32, batch, D1, D2, d, s);
 }
 
 }  // namespace fqm

@@ -153,7 +153,8 @@ typedef struct fqm_fabq {
 
 /* One MDBF path (rows = n outputs, cols = m inputs, rank r, envelope rank l). */
 typedef struct fqm_mdbf_path {
-    const uint8_t* S_A;         /* [n][ld_A], 1-bit fields along r */
+    const uint8_t* S_A;         /* [n][ld_A], 1-bit fields along r; each row is read up to
+                                   ceil(r/8) rounded up to a multiple of 4 bytes */
     int64_t ld_A;               /* >= ceil(r/8) */
     const uint8_t* S_B;         /* [r][ld_B], 1-bit fields along m */
     int64_t ld_B;               /* >= m/8 */
@@ -238,10 +239,10 @@ fqm_status fqm_unpack(const uint8_t* packed, uint8_t* codes, int64_t rows, int64
 fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
 
 /* Bytes of device workspace fqm_gemv needs for this descriptor and batch:
- * MDBF 128*P*S*(roundup(m,256) + roundup(r,256)) with S = ceil(batch / bs),
- * bs = 1 if 3*l >= 64 else floor(64 / (3*l)) (the dense operands of both
- * passes: each fp32 value as three bf16 parts, 64 columns per batch slice of
- * bs rows); LUT6 and LUT4 with batch >= 2 and
+ * MDBF 32*P*S*C*(roundup(m,256) + roundup(r,256)) with S = ceil(batch / bs),
+ * bs = 1 if 3*l >= 64 else floor(64 / (3*l)) and C = ceil(3*l*min(bs, batch) / 16)
+ * (the dense operands of both passes: each fp32 value as three bf16 parts,
+ * in C blocks of 16 columns per batch slice of bs rows); LUT6 and LUT4 with batch >= 2 and
  * cols a multiple of 512 split K over workgroups unless rows > 16368, and
  * then need S*batch*rows*4 (S fp32 partial sums per output, S <= cols / 512,
  * a function of rows and cols only, the same for both formats), else 0;

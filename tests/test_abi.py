@@ -225,8 +225,9 @@ def mdbf(r=2000, l=2, P=1, n=4096, m=4096):
 def test_mdbf_argument_errors_and_workspace(lib):
     w = mdbf()
     need = lib.fqm_workspace_size(ctypes.byref(w), 16)
-    # both passes' dense operands, 64 bf16 columns per batch slice (slices of
-    # 64 // (3 l) = 10 batch rows -> 2 slices), K padded to 256
+    # both passes' dense operands: batch slices of 64 // (3 l) = 10 batch
+    # rows (2 slices), each with the first slice's 3 l x 10 = 60 columns in
+    # 16-column blocks (64), K padded to 256; 2 bytes each
     assert need == 2 * 1 * 2 * 64 * (4096 + 2048)
     assert gemv(lib, w, batch=16, ws=None, wsb=0) == E["WORKSPACE"]
     assert gemv(lib, w, batch=16, ws=FAKE, wsb=need - 4) == E["WORKSPACE"]
@@ -237,7 +238,10 @@ def test_mdbf_argument_errors_and_workspace(lib):
     w = mdbf()
     w.mdbf.path[0].ld_A = 240   # < ceil(2000/8)
     assert gemv(lib, w) == E["SHAPE"]
-    assert lib.fqm_workspace_size(ctypes.byref(mdbf(P=2)), 3) == 2 * 2 * 1 * 64 * (4096 + 2048)
+    # batch 3: one slice of 18 columns -> two 16-column blocks, per path
+    assert lib.fqm_workspace_size(ctypes.byref(mdbf(P=2)), 3) == 2 * 2 * 1 * 32 * (4096 + 2048)
+    # batch 1: one 16-column block
+    assert lib.fqm_workspace_size(ctypes.byref(mdbf()), 1) == 2 * 1 * 1 * 16 * (4096 + 2048)
     assert lib.fqm_dequant(ctypes.byref(mdbf()), FAKE, None) == E["UNSUPPORTED"]
     assert gemm(lib, mdbf(), M=1) == E["UNSUPPORTED"]
 
@@ -315,7 +319,8 @@ def test_fabq_row_map_must_be_a_permutation(row_of):
 def test_gemv_static_rejects_more_than_its_scratch(lib):
     """fqm_gemv_static refuses, before any device call, a request whose
     workspace exceeds the static array (16 MiB): MDBF with 16 envelopes and
-    two paths at batch 16 on the 5120 x 17408 shape needs 88 MB."""
+    two paths at batch 16 on the 5120 x 17408 shape needs 66 MB (16 slices
+    of one batch row, 48 columns each)."""
     w = fqm._Weights()
     w.format, w.rows, w.cols = fqm.FQM_MDBF, 5120, 17408
     w.mdbf.r, w.mdbf.l, w.mdbf.P = 4096, 16, 2
@@ -324,7 +329,7 @@ def test_gemv_static_rejects_more_than_its_scratch(lib):
         q.S_A, q.ld_A, q.S_B, q.ld_B = FAKE, 512, FAKE, 2176
         q.A_amp = q.B_amp = q.Q_U = q.Q_V = FAKE
     need = lib.fqm_workspace_size(ctypes.byref(w), 16)
-    assert need == 128 * 2 * 16 * (17408 + 4096) > fqm.STATIC_SCRATCH_BYTES
+    assert need == 2 * 2 * 16 * 48 * (17408 + 4096) > fqm.STATIC_SCRATCH_BYTES
     rc = lib.fqm_gemv_static(ctypes.byref(w), FAKE, FAKE, 0, 16, None)
     assert rc == 8 and lib.fqm_status_str(rc).startswith(b"needs more scratch")
     assert lib.fqm_gemv_static(ctypes.byref(w), FAKE, FAKE, 0, 17, None) == E["SHAPE"]
