@@ -113,7 +113,8 @@ fqm_status check_weight_buffers(const fqm_weights& w) {
             const fqm_mdbf& f = w.mdbf;
             for (int p = 0; p < f.P && ok; ++p) {
                 const fqm_mdbf_path& q = f.path[p];
-                ok = in_allocation(q.S_A, span(R, q.ld_A, ((f.r + 7) / 8 + 3) & ~3)) && in_allocation(q.S_B, span(f.r, q.ld_B, C / 8)) &&
+                ok = in_allocation(q.S_A, span(R, q.ld_A, ((f.r + 7) / 8 + 15) & ~15)) &&
+                     in_allocation(q.S_B, span(f.r, q.ld_B, (C / 8 + 15) & ~15)) &&
                      in_allocation(q.A_amp, R * f.l * 2) && in_allocation(q.B_amp, C * f.l * 2) &&
                      in_allocation(q.Q_U, (int64_t)f.r * f.l * 2) && in_allocation(q.Q_V, (int64_t)f.r * f.l * 2);
             }

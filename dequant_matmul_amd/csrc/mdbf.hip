@@ -27,12 +27,13 @@
 //   pass 1: sign products over S_B, then z and D2 = parts of v_k[j];
 //   pass 2: sign products over S_A for every path, then y.
 // D1 and D2 are stored fragment-major: for each batch slice, 16-column block,
-// 256-wide K block and 32-wide k step, the 64 lanes' 16-byte B operand pieces
-// are contiguous.  Lane (c, q) = (lane % 16, lane / 16) holds column c at
-// k = 64 q + 8 s + e (e = 0..7) of the block, and the A operand of the same
-// lane holds sign byte 8 q + s of its row's 32 bytes for the block: both
-// operands use one k order, so only the order of the fp32 sums differs from
-// plain k order.
+// 512-wide K block and 32-wide k step s (0..15), the 64 lanes' 16-byte B
+// operand pieces are contiguous.  Lane (c, q) = (lane % 16, lane / 16) holds
+// column c at k = 128 q + 8 s + e (e = 0..7) of the block, and the A operand
+// of the same lane holds sign byte 16 q + s of its row's 64 bytes for the
+// block, so one 16-byte load gives a lane its signs for the whole block.
+// Both operands use one k order, so only the order of the fp32 sums differs
+// from plain k order.
 // A workgroup owns 16 rows and a batch slice; its waves take the K blocks in
 // turn (wave w: blocks w, w + nw, ...), loading the next half block while
 // the current one issues its MFMAs.  The waves' partial sums are added in
@@ -51,8 +52,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int KB = 256;      // columns per K block (8 MFMA k steps of 32)
-constexpr int BLK = 4096;    // elements of one (column block, K block) operand piece: 8 steps x 64 lanes x 8
+constexpr int KB = 512;      // columns per K block (16 MFMA k steps of 32)
+constexpr int BLK = 8192;    // elements of one (column block, K block) operand piece: 16 steps x 64 lanes x 8
 
 __host__ __device__ inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -84,10 +85,10 @@ __host__ __device__ inline MdbfDims mdbf_dims(int64_t m, int64_t r, int l, int P
 // operand (ncb column blocks, nkb K blocks).
 __device__ __forceinline__ int64_t dfrag_index(int sg, int ncb, int col, int64_t k, int64_t nkb) {
     const int cb = col >> 4, c = col & 15;
-    const int64_t kb = k >> 8;
-    const int rem = (int)(k & 255);
-    const int q = rem >> 6, s = (rem >> 3) & 7, e = rem & 7;
-    return (((int64_t)(sg * ncb + cb) * nkb + kb) * 8 + s) * 512 + (c + 16 * q) * 8 + e;
+    const int64_t kb = k >> 9;
+    const int rem = (int)(k & 511);
+    const int q = rem >> 7, s = (rem >> 3) & 15, e = rem & 7;
+    return (((int64_t)(sg * ncb + cb) * nkb + kb) * 16 + s) * 512 + (c + 16 * q) * 8 + e;
 }
 
 // v = h0 + h1 + h2 (bf16 parts; each remainder is exact in fp32)
@@ -121,13 +122,13 @@ __device__ __forceinline__ bf16x8 expand_signs_neg(uint32_t w, uint32_t mask, ui
 
 // D1 of path p: parts of u_k[i] at column 3 (b l + k) + t of batch slice
 // b / bs; zero for i >= m.  One thread writes one lane's 16-byte piece of one
-// k step: grid (2 nkb, nsg ncb, P), 256 threads = 4 k steps x 64 lanes.
+// k step: grid (4 nkb, nsg ncb, P), 256 threads = 4 k steps x 64 lanes.
 __global__ __launch_bounds__(256) void mdbf_prep(fqm_mdbf md, const uint16_t* __restrict__ x,
                                                  uint16_t* __restrict__ D1, int64_t m, int batch, int nsg,
                                                  int ncb, int64_t nkb, int64_t d1_path) {
     const int lane = threadIdx.x & 63;
-    const int64_t kb = blockIdx.x >> 1;
-    const int s = 4 * (blockIdx.x & 1) + (threadIdx.x >> 6);
+    const int64_t kb = blockIdx.x >> 2;
+    const int s = 4 * (blockIdx.x & 3) + (threadIdx.x >> 6);
     const int sg = blockIdx.y / ncb, cb = blockIdx.y - sg * ncb;
     const int p = blockIdx.z;
     const int l = md.l, bs = batch_slice(l);
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void mdbf_prep(fqm_mdbf md, const uint16_t* __
     if (col >= 3 * l * nrows) return;  // never read
     const int bl = col / (3 * l), rem = col - bl * 3 * l, k = rem / 3, t3 = rem - 3 * k;
     const int64_t b = (int64_t)sg * bs + bl;
-    const int64_t i0 = kb * KB + 64 * q + 8 * s;
+    const int64_t i0 = kb * KB + 128 * q + 8 * s;
     const uint16_t* bamp = p == 0 ? md.path[0].B_amp : md.path[1].B_amp;
     u32x4 out;
 #pragma unroll
@@ -152,11 +153,11 @@ __global__ __launch_bounds__(256) void mdbf_prep(fqm_mdbf md, const uint16_t* __
         const uint16_t hi = t3 == 0 ? h1[0] : t3 == 1 ? h1[1] : h1[2];
         out[e >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
-    uint16_t* dp = D1 + (int64_t)p * d1_path + (((int64_t)(sg * ncb + cb) * nkb + kb) * 8 + s) * 512 + 8 * lane;
+    uint16_t* dp = D1 + (int64_t)p * d1_path + (((int64_t)(sg * ncb + cb) * nkb + kb) * 16 + s) * 512 + 8 * lane;
     *reinterpret_cast<u32x4*>(dp) = out;
 }
 
-// The dense pieces of one half block (4 k steps) of NB column blocks.
+// The dense pieces of one quarter block (4 k steps) of NB column blocks.
 template <int NB>
 struct Half {
     u32x4 d[NB][4];
@@ -167,15 +168,17 @@ struct Half {
 // wave, wave + nw, ..., in chunks of BPW blocks.  A chunk is straight-line
 // code with no branch between a load and its use, so the loads stay where
 // they are written and the waits before the MFMAs are exact:
-// - the sign dwords of the whole chunk (the stream from HBM) go out first;
-// - the dense pieces (L2) run AHEAD half blocks ahead of their MFMAs;
+// - the signs of the whole chunk (the stream from HBM, 16 bytes per lane and
+//   block) go out first;
+// - the dense pieces (L2) run AHEAD quarter blocks ahead of their MFMAs;
 // - a block past nkb re-reads block nkb - 1 and its A operand is all zeros
 //   (the launch picks BPW so that such blocks are rare).
 // Reads stay inside the operands:
-// - a row's signs are its first kbytes = ceil(K / 8) bytes; a dword piece at
-//   or past them is read at the last dword that starts inside them (at most
-//   3 bytes past kbytes, inside the row's ld), and the dense operand is zero
-//   for every k >= K, so whatever those bits hold adds nothing;
+// - a row's signs are its first kbytes = ceil(K / 8) bytes; a 16-byte piece
+//   that starts at or past them is read at the last 16-byte piece that
+//   starts inside them, so a row is read up to kbytes rounded up to 16 (at
+//   most 15 bytes past kbytes, inside the row's ld), and the dense operand is
+//   zero for every k >= K, so whatever those bits hold adds nothing;
 // - a lane whose column is at or past cend reads the piece of column
 //   cend - 1 (the same bytes as a live lane of the instruction) and only
 //   feeds result columns that are never read.
@@ -184,12 +187,12 @@ __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int
                                               int64_t kbytes, const uint16_t* __restrict__ D, int64_t nkb,
                                               int sg, int ncb, int64_t row0, int cend, int wave, int nw,
                                               f32x4 (&acc)[NB]) {
-    constexpr int T = 2 * BPW;                                  // half blocks per chunk
-    constexpr int AHEAD = T == 2 || NB > 1 || BPW > 4 ? 1 : 2;  // dense half blocks in flight ahead (fits the VGPRs)
+    constexpr int T = 4 * BPW;                     // quarter blocks per chunk
+    constexpr int AHEAD = NB > 1 ? 1 : BPW >= 4 ? 3 : 2;  // dense quarter blocks in flight ahead (fits the VGPRs)
     constexpr int NBUF = AHEAD + 1;
     const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
     const uint8_t* srow = S + min(row0 + c, rows - 1) * ldS;
-    const int64_t klast = (kbytes - 1) & ~(int64_t)3;
+    const int64_t klast = (kbytes - 1) & ~(int64_t)15;
     const uint16_t* dcol[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -200,13 +203,11 @@ __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int
     asm("v_mov_b32 %0, 0x3f803f80" : "=v"(ones));
     for (int64_t base = wave; base < nkb; base += (int64_t)BPW * nw) {
         int64_t blk[BPW];
-        uint32_t sgn[T];
+        u32x4 sgn[BPW];
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
             blk[j] = min(base + (int64_t)j * nw, nkb - 1);
-            const int64_t off = 32 * blk[j] + 8 * q;
-            sgn[2 * j] = *reinterpret_cast<const uint32_t*>(srow + min(off, klast));
-            sgn[2 * j + 1] = *reinterpret_cast<const uint32_t*>(srow + min(off + 4, klast));
+            sgn[j] = *reinterpret_cast<const u32x4*>(srow + min(64 * blk[j] + 16 * q, klast));
         }
         Half<NB> hb[NBUF];
         auto load_d = [&](int t) {
@@ -215,7 +216,7 @@ __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
                     hb[t % NBUF].d[nb][s] =
-                        *reinterpret_cast<const u32x4*>(dcol[nb] + blk[t / 2] * BLK + 512 * (4 * (t % 2) + s));
+                        *reinterpret_cast<const u32x4*>(dcol[nb] + blk[t / 4] * BLK + 512 * (4 * (t % 4) + s));
         };
 #pragma unroll
         for (int t = 0; t < AHEAD; ++t) load_d(t);
@@ -226,13 +227,14 @@ __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int
             // its first use (to lower register pressure), so that every MFMA
             // waited for its own load
             __builtin_amdgcn_sched_barrier(0);
-            const bool live = base + (int64_t)(t / 2) * nw < nkb;  // uniform over the wave
+            const bool live = base + (int64_t)(t / 4) * nw < nkb;  // uniform over the wave
             const uint32_t mask = live ? 0x80008000u : 0u, one = live ? ones : 0u;
             bf16x8 a[4];
-            a[0] = expand_signs_neg<0>(sgn[t], mask, one);
-            a[1] = expand_signs_neg<1>(sgn[t], mask, one);
-            a[2] = expand_signs_neg<2>(sgn[t], mask, one);
-            a[3] = expand_signs_neg<3>(sgn[t], mask, one);
+            const uint32_t sw = sgn[t / 4][t % 4];
+            a[0] = expand_signs_neg<0>(sw, mask, one);
+            a[1] = expand_signs_neg<1>(sw, mask, one);
+            a[2] = expand_signs_neg<2>(sw, mask, one);
+            a[3] = expand_signs_neg<3>(sw, mask, one);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -266,21 +268,19 @@ __device__ __forceinline__ float tot_at(const float* tot, int col, int row) {
     return tot[(col >> 4) * 256 + ((col & 15) + 16 * (row >> 2)) * 4 + (row & 3)];
 }
 
-// Most waves per workgroup: pass 1 with one column block 16 (its operands
-// fit the 128 VGPRs of a 16-wave group), else 8.  The launch keeps every
-// floor on the wave count (at most 6) under this.
-template <int NB, int PASS>
-constexpr int nw_max() { return NB == 1 && PASS == 1 ? 16 : 8; }
+// Most waves per workgroup (a 512-thread group may use 256 VGPRs).  The
+// launch keeps every floor on the wave count (at most 6) under this.
+constexpr int NWM = 8;
 
 // Pass 1: rows j of S_B; D1 columns of batch slice blockIdx.y.  Writes
 // D2[p][.][j] = parts of Q_U[j][k] z[j] (zero for j >= r, which the grid
 // covers up to r_pad).
 template <int NB, int BPW>
-__global__ __launch_bounds__((64 * nw_max<NB, 1>())) void mdbf_pass1(fqm_mdbf md, const uint16_t* __restrict__ D1,
+__global__ __launch_bounds__(64 * NWM) void mdbf_pass1(fqm_mdbf md, const uint16_t* __restrict__ D1,
                                                         uint16_t* __restrict__ D2, int64_t m, int batch, int ncb,
                                                         int64_t m_pad, int64_t r_pad, int64_t d1_path,
                                                         int64_t d2_path) {
-    __shared__ f32x4 red[nw_max<NB, 1>() * NB * 64];
+    __shared__ f32x4 red[NWM * NB * 64];
     __shared__ float tot[NB * 256];
     __shared__ float qv_s[16 * 16], qu_s[16 * 16];  // Q_V, Q_U rows j0 .. j0 + 15
     const int p = blockIdx.z;
@@ -337,10 +337,10 @@ __global__ __launch_bounds__((64 * nw_max<NB, 1>())) void mdbf_pass1(fqm_mdbf md
 
 // Pass 2: rows i of S_A, summed over the paths; D2 columns of batch slice blockIdx.y.
 template <int NB, int BPW>
-__global__ __launch_bounds__((64 * nw_max<NB, 2>())) void mdbf_pass2(fqm_mdbf md, const uint16_t* __restrict__ D2,
+__global__ __launch_bounds__(64 * NWM) void mdbf_pass2(fqm_mdbf md, const uint16_t* __restrict__ D2,
                                                         void* __restrict__ y, int y_f32, int64_t n, int batch,
                                                         int ncb, int64_t r_pad, int64_t d2_path) {
-    __shared__ f32x4 red[nw_max<NB, 2>() * NB * 64];
+    __shared__ f32x4 red[NWM * NB * 64];
     __shared__ float tot[NB * 256];
     __shared__ float amp_s[2][16 * 16];  // A_amp rows i0 .. i0 + 15 of each path
     const int l = md.l;
@@ -398,16 +398,15 @@ __global__ __launch_bounds__((64 * nw_max<NB, 2>())) void mdbf_pass2(fqm_mdbf md
     }
 }
 
-// Blocks per wave and chunk (1, 2, 4 or 8) and waves per workgroup for nkb
-// K blocks with at most cap waves: per = ceil(nkb / cap) blocks each, rounded
-// up to a power of two, then as few waves as hold nkb blocks (at least floor);
-// past 8 blocks per wave the waves go over their blocks in chunks of 8.
+// Blocks per wave and chunk (bpw <= maxb) and waves per workgroup for nkb K
+// blocks with at most cap waves: bpw = ceil(nkb / cap) blocks each, then as
+// few waves as hold nkb blocks (at least floor); past maxb blocks per wave
+// the waves go over their blocks in chunks of maxb.
 struct Split {
     int bpw, nw;
 };
-inline Split split_k(int64_t nkb, int cap, int floor) {
-    const int64_t per = (nkb + cap - 1) / cap;
-    const int bpw = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
+inline Split split_k(int64_t nkb, int cap, int floor, int maxb) {
+    const int bpw = (int)std::min<int64_t>(maxb, (nkb + cap - 1) / cap);
     const int64_t nw = std::min<int64_t>(cap, (nkb + bpw - 1) / bpw);
     return {bpw, (int)std::max<int64_t>(floor, nw)};
 }
@@ -433,30 +432,39 @@ template <int NB>
 hipError_t launch_nb(const fqm_weights& w, void* y, int y_f32, int batch, uint16_t* D1, uint16_t* D2,
                      const MdbfDims& d, hipStream_t s) {
     const fqm_mdbf& md = w.mdbf;
-    constexpr int NWM1 = nw_max<NB, 1>(), NWM2 = nw_max<NB, 2>();
     // At least one thread per envelope value of the tile's 16 rows (16 l <=
     // 256), and in pass 2 one per (row, batch row) of the slice (16 bs <=
     // 16 * 21).  At most enough waves per tile that tiles x waves is about
-    // 4096 (16 waves per CU, all resident at once), and NWM1 / NWM2.
+    // 4096 (16 waves per CU, all resident at once), and NWM.  Four column
+    // blocks take chunks of at most 4 K blocks (their operands fill the VGPRs).
+    constexpr int MAXB = NB == 1 ? 8 : 4;
     const int env = (16 * md.l + 63) / 64;
     const int64_t t1 = d.r_pad / 16 * d.nsg * md.P, t2 = (w.rows + 15) / 16 * d.nsg;
     const int f2 = std::max(env, (16 * std::min(d.bs, batch) + 63) / 64);
-    const int c1 = (int)std::min<int64_t>(NWM1, std::max<int64_t>(env, (4096 + t1 - 1) / t1));
-    const int c2 = (int)std::min<int64_t>(NWM2, std::max<int64_t>(f2, (4096 + t2 - 1) / t2));
-    const Split k1 = split_k(d.m_pad / KB, c1, env), k2 = split_k(d.r_pad / KB, c2, f2);
+    const int c1 = (int)std::min<int64_t>(NWM, std::max<int64_t>(env, (4096 + t1 - 1) / t1));
+    const int c2 = (int)std::min<int64_t>(NWM, std::max<int64_t>(f2, (4096 + t2 - 1) / t2));
+    const Split k1 = split_k(d.m_pad / KB, c1, env, MAXB), k2 = split_k(d.r_pad / KB, c2, f2, MAXB);
     hipError_t e;
     switch (k1.bpw) {
         case 1: e = launch_pass1<NB, 1>(w, batch, D1, D2, d, k1.nw, s); break;
         case 2: e = launch_pass1<NB, 2>(w, batch, D1, D2, d, k1.nw, s); break;
+        case 3: e = launch_pass1<NB, 3>(w, batch, D1, D2, d, k1.nw, s); break;
         case 4: e = launch_pass1<NB, 4>(w, batch, D1, D2, d, k1.nw, s); break;
-        default: e = launch_pass1<NB, 8>(w, batch, D1, D2, d, k1.nw, s); break;
+        case 5: e = launch_pass1<NB, NB == 1 ? 5 : 4>(w, batch, D1, D2, d, k1.nw, s); break;
+        case 6: e = launch_pass1<NB, NB == 1 ? 6 : 4>(w, batch, D1, D2, d, k1.nw, s); break;
+        case 7: e = launch_pass1<NB, NB == 1 ? 7 : 4>(w, batch, D1, D2, d, k1.nw, s); break;
+        default: e = launch_pass1<NB, MAXB>(w, batch, D1, D2, d, k1.nw, s); break;
     }
     if (e != hipSuccess) return e;
     switch (k2.bpw) {
         case 1: return launch_pass2<NB, 1>(w, y, y_f32, batch, D2, d, k2.nw, s);
         case 2: return launch_pass2<NB, 2>(w, y, y_f32, batch, D2, d, k2.nw, s);
+        case 3: return launch_pass2<NB, 3>(w, y, y_f32, batch, D2, d, k2.nw, s);
         case 4: return launch_pass2<NB, 4>(w, y, y_f32, batch, D2, d, k2.nw, s);
-        default: return launch_pass2<NB, 8>(w, y, y_f32, batch, D2, d, k2.nw, s);
+        case 5: return launch_pass2<NB, NB == 1 ? 5 : 4>(w, y, y_f32, batch, D2, d, k2.nw, s);
+        case 6: return launch_pass2<NB, NB == 1 ? 6 : 4>(w, y, y_f32, batch, D2, d, k2.nw, s);
+        case 7: return launch_pass2<NB, NB == 1 ? 7 : 4>(w, y, y_f32, batch, D2, d, k2.nw, s);
+        default: return launch_pass2<NB, MAXB>(w, y, y_f32, batch, D2, d, k2.nw, s);
     }
 }
 
@@ -473,7 +481,7 @@ hipError_t launch_mdbf_gemv(const fqm_weights& w, const uint16_t* x, void* y, in
     const MdbfDims d = mdbf_dims(w.cols, md.r, md.l, md.P, batch);
     uint16_t* D1 = static_cast<uint16_t*>(ws);
     uint16_t* D2 = D1 + d.d1_elems;
-    hipLaunchKernelGGL(mdbf_prep, dim3((unsigned)(2 * d.m_pad / KB), (unsigned)(d.nsg * d.ncb), (unsigned)md.P),
+    hipLaunchKernelGGL(mdbf_prep, dim3((unsigned)(4 * d.m_pad / KB), (unsigned)(d.nsg * d.ncb), (unsigned)md.P),
                        dim3(256), 0, s, md, x, D1, w.cols, batch, d.nsg, d.ncb, d.m_pad / KB, d.d1_path);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

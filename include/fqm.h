@@ -154,9 +154,10 @@ typedef struct fqm_fabq {
 /* One MDBF path (rows = n outputs, cols = m inputs, rank r, envelope rank l). */
 typedef struct fqm_mdbf_path {
     const uint8_t* S_A;         /* [n][ld_A], 1-bit fields along r; each row is read up to
-                                   ceil(r/8) rounded up to a multiple of 4 bytes */
+                                   ceil(r/8) rounded up to a multiple of 16 bytes */
     int64_t ld_A;               /* >= ceil(r/8) */
-    const uint8_t* S_B;         /* [r][ld_B], 1-bit fields along m */
+    const uint8_t* S_B;         /* [r][ld_B], 1-bit fields along m; each row is read up to
+                                   m/8 rounded up to a multiple of 16 bytes */
     int64_t ld_B;               /* >= m/8 */
     const uint16_t* A_amp;      /* [n][l] fp16 */
     const uint16_t* B_amp;      /* [m][l] fp16 */
@@ -239,7 +240,7 @@ fqm_status fqm_unpack(const uint8_t* packed, uint8_t* codes, int64_t rows, int64
 fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
 
 /* Bytes of device workspace fqm_gemv needs for this descriptor and batch:
- * MDBF 32*P*S*C*(roundup(m,256) + roundup(r,256)) with S = ceil(batch / bs),
+ * MDBF 32*P*S*C*(roundup(m,512) + roundup(r,512)) with S = ceil(batch / bs),
  * bs = 1 if 3*l >= 64 else floor(64 / (3*l)) and C = ceil(3*l*min(bs, batch) / 16)
  * (the dense operands of both passes: each fp32 value as three bf16 parts,
  * in C blocks of 16 columns per batch slice of bs rows); LUT6 and LUT4 with batch >= 2 and

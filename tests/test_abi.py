@@ -227,7 +227,7 @@ def test_mdbf_argument_errors_and_workspace(lib):
     need = lib.fqm_workspace_size(ctypes.byref(w), 16)
     # both passes' dense operands: batch slices of 64 // (3 l) = 10 batch
     # rows (2 slices), each with the first slice's 3 l x 10 = 60 columns in
-    # 16-column blocks (64), K padded to 256; 2 bytes each
+    # 16-column blocks (64), K padded to 512; 2 bytes each
     assert need == 2 * 1 * 2 * 64 * (4096 + 2048)
     assert gemv(lib, w, batch=16, ws=None, wsb=0) == E["WORKSPACE"]
     assert gemv(lib, w, batch=16, ws=FAKE, wsb=need - 4) == E["WORKSPACE"]
