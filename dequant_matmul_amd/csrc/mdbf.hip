@@ -51,6 +51,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds8;
+typedef __attribute__((address_space(3))) const u32x4 lds128c;
+typedef __attribute__((address_space(3))) uint32_t lds32;
 
 constexpr int KB = 512;      // columns per K block (16 MFMA k steps of 32)
 constexpr int BLK = 8192;    // elements of one (column block, K block) operand piece: 16 steps x 64 lanes x 8
@@ -169,10 +172,15 @@ struct Half {
 // code with no branch between a load and its use, so the loads stay where
 // they are written and the waits before the MFMAs are exact:
 // - the signs of the whole chunk (the stream from HBM, 16 bytes per lane and
-//   block) go out first;
-// - the dense pieces (L2) run AHEAD quarter blocks ahead of their MFMAs;
+//   block) go out first, the next chunk's after this one's MFMAs;
+// - the dense pieces run AHEAD quarter blocks ahead of their MFMAs;
 // - a block past nkb re-reads block nkb - 1 and its A operand is all zeros
 //   (the launch picks BPW so that such blocks are rare).
+// The dense pieces come from D (global, fragment-major) or, with LDSD, from
+// the compact copy at LDS byte address dl: for each K block and k step, the
+// four lane quarters q of ce live columns, 16 bytes each.
+// pre() runs once in every wave, after its first chunk's sign loads are
+// issued and before any dense piece is read.
 // Reads stay inside the operands:
 // - a row's signs are its first kbytes = ceil(K / 8) bytes; a 16-byte piece
 //   that starts at or past them is read at the last 16-byte piece that
@@ -182,11 +190,12 @@ struct Half {
 // - a lane whose column is at or past cend reads the piece of column
 //   cend - 1 (the same bytes as a live lane of the instruction) and only
 //   feeds result columns that are never read.
-template <int NB, int BPW>
+template <int NB, int BPW, bool LDSD = false, typename Pre>
 __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int64_t ldS, int64_t rows,
-                                              int64_t kbytes, const uint16_t* __restrict__ D, int64_t nkb,
-                                              int sg, int ncb, int64_t row0, int cend, int wave, int nw,
-                                              f32x4 (&acc)[NB]) {
+                                              int64_t kbytes, const uint16_t* __restrict__ D, uint32_t dl,
+                                              int64_t nkb, int sg, int ncb, int64_t row0, int cend, int wave,
+                                              int nw, f32x4 (&acc)[NB], Pre pre) {
+    static_assert(!LDSD || NB == 1, "the LDS copy holds one column block");
     constexpr int T = 4 * BPW;                     // quarter blocks per chunk
     constexpr int AHEAD = NB > 1 ? 1 : BPW >= 4 ? 3 : 2;  // dense quarter blocks in flight ahead (fits the VGPRs)
     constexpr int NBUF = AHEAD + 1;
@@ -199,24 +208,34 @@ __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int
         const int col = min(16 * nb + c, cend - 1);
         dcol[nb] = D + (int64_t)(sg * ncb + (col >> 4)) * nkb * BLK + 8 * ((col & 15) + 16 * q);
     }
+    const uint32_t dlane = dl + 16u * (uint32_t)(q * cend + min(c, cend - 1));
     uint32_t ones;
     asm("v_mov_b32 %0, 0x3f803f80" : "=v"(ones));
-    for (int64_t base = wave; base < nkb; base += (int64_t)BPW * nw) {
-        int64_t blk[BPW];
-        u32x4 sgn[BPW];
+    int64_t blk[BPW];
+    u32x4 sgn[BPW];
+    auto load_signs = [&](int64_t base) {
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
             blk[j] = min(base + (int64_t)j * nw, nkb - 1);
             sgn[j] = *reinterpret_cast<const u32x4*>(srow + min(64 * blk[j] + 16 * q, klast));
         }
+    };
+    load_signs(wave);
+    pre();
+    for (int64_t base = wave; base < nkb; base += (int64_t)BPW * nw) {
         Half<NB> hb[NBUF];
         auto load_d = [&](int t) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    hb[t % NBUF].d[nb][s] =
-                        *reinterpret_cast<const u32x4*>(dcol[nb] + blk[t / 4] * BLK + 512 * (4 * (t % 4) + s));
+                for (int s = 0; s < 4; ++s) {
+                    const int ks = 4 * (t % 4) + s;  // k step within the block
+                    if constexpr (LDSD)
+                        hb[t % NBUF].d[nb][s] =
+                            *(lds128c*)(uintptr_t)(dlane + 64u * (uint32_t)cend * (uint32_t)(blk[t / 4] * 16 + ks));
+                    else
+                        hb[t % NBUF].d[nb][s] = *reinterpret_cast<const u32x4*>(dcol[nb] + blk[t / 4] * BLK + 512 * ks);
+                }
         };
 #pragma unroll
         for (int t = 0; t < AHEAD; ++t) load_d(t);
@@ -242,6 +261,7 @@ __device__ __forceinline__ void sign_products(const uint8_t* __restrict__ S, int
                     acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         a[s], __builtin_bit_cast(bf16x8, hb[t % NBUF].d[nb][s]), acc[nb], 0, 0, 0);
         }
+        if (base + (int64_t)BPW * nw < nkb) load_signs(base + (int64_t)BPW * nw);
     }
 }
 
@@ -275,11 +295,20 @@ constexpr int NWM = 8;
 // Pass 1: rows j of S_B; D1 columns of batch slice blockIdx.y.  Writes
 // D2[p][.][j] = parts of Q_U[j][k] z[j] (zero for j >= r, which the grid
 // covers up to r_pad).
-template <int NB, int BPW>
-__global__ __launch_bounds__(64 * NWM) void mdbf_pass1(fqm_mdbf md, const uint16_t* __restrict__ D1,
+// FUSE (one column block, ce m_pad 2 bytes <= FUSE_LDS): the workgroup forms
+// the parts of u_k itself, from x and B_amp, in a compact LDS copy (the ce =
+// 3 l rows live columns of its slice in the fragment order), and reads its
+// dense operand there; D1 and the prep launch are not used.
+constexpr int FUSE_LDS = 65536;
+constexpr int FILL_PAIRS = 8;  // pairs of k per thread whose loads go out together in the fill
+
+template <int NB, int BPW, bool FUSE>
+__global__ __launch_bounds__(64 * NWM) void mdbf_pass1(fqm_mdbf md, const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ D1,
                                                         uint16_t* __restrict__ D2, int64_t m, int batch, int ncb,
                                                         int64_t m_pad, int64_t r_pad, int64_t d1_path,
                                                         int64_t d2_path) {
+    __shared__ uint32_t dlds[FUSE ? FUSE_LDS / 4 : 1];
     __shared__ f32x4 red[NWM * NB * 64];
     __shared__ float tot[NB * 256];
     __shared__ float qv_s[16 * 16], qu_s[16 * 16];  // Q_V, Q_U rows j0 .. j0 + 15
@@ -303,9 +332,56 @@ __global__ __launch_bounds__(64 * NWM) void mdbf_pass1(fqm_mdbf md, const uint16
     f32x4 acc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    if (j0 < r)
-        sign_products<NB, BPW>(path.S_B, path.ld_B, r, m / 8, D1 + (int64_t)p * d1_path, m_pad / KB, sg, ncb, j0,
-                          3 * l * nb_rows, wave, nw, acc);
+    const int ce = 3 * l * nb_rows;
+    if (j0 < r) {
+        const uint32_t dl = (uint32_t)(uintptr_t)(lds8*)dlds;
+        // the parts of u_k[i] = B_amp[i][k] x[b][i] for this slice: item
+        // (bk = bl l + k, pair of i), written as two bf16 per dword at column
+        // 3 bk + t of k step (i % 512) / 8 of K block i / 512; zero for i >= m
+        auto fill = [&]() {
+            if constexpr (FUSE) {
+                const uint16_t* bamp = p == 0 ? md.path[0].B_amp : md.path[1].B_amp;
+                const int64_t npair = m_pad / 2;
+                constexpr int FP = FILL_PAIRS;
+                for (int bk = 0; bk < l * nb_rows; ++bk) {
+                    const int bl = bk / l, k = bk - bl * l;
+                    const uint16_t* xr = x + (int64_t)(b0 + bl) * m;
+                    for (int64_t p0 = threadIdx.x; p0 < npair; p0 += (int64_t)FP * blockDim.x) {
+                        uint16_t xv[FP][2], bv[FP][2];
+#pragma unroll
+                        for (int j = 0; j < FP; ++j) {
+                            const int64_t i = 2 * (p0 + (int64_t)j * blockDim.x);
+                            const int64_t ic = i < m ? i : 0;  // m is a multiple of 32: i < m means i + 1 < m
+                            xv[j][0] = xr[ic];
+                            xv[j][1] = xr[ic + 1];
+                            bv[j][0] = bamp[ic * l + k];
+                            bv[j][1] = bamp[(ic + 1) * l + k];
+                        }
+#pragma unroll
+                        for (int j = 0; j < FP; ++j) {
+                            const int64_t i = 2 * (p0 + (int64_t)j * blockDim.x);
+                            if (i >= m_pad) break;
+                            uint16_t h0[3] = {0, 0, 0}, h1[3] = {0, 0, 0};
+                            if (i < m) {
+                                split3_bf16(fp16_to_f32(bv[j][0]) * bf16_to_f32(xv[j][0]), h0);
+                                split3_bf16(fp16_to_f32(bv[j][1]) * bf16_to_f32(xv[j][1]), h1);
+                            }
+                            const int rem = (int)(i & 511), qq = rem >> 7, ks = (rem >> 3) & 15, e = rem & 7;
+                            const uint32_t at =
+                                dl + 16u * (uint32_t)((((i >> 9) * 16 + ks) * 4 + qq) * ce) + 2u * e;
+#pragma unroll
+                            for (int t3 = 0; t3 < 3; ++t3)
+                                *(lds32*)(uintptr_t)(at + 16u * (uint32_t)(3 * bk + t3)) =
+                                    (uint32_t)h0[t3] | ((uint32_t)h1[t3] << 16);
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        };
+        sign_products<NB, BPW, FUSE>(path.S_B, path.ld_B, r, m / 8, D1 + (int64_t)p * d1_path, dl, m_pad / KB, sg,
+                                     ncb, j0, ce, wave, nw, acc, fill);
+    }
     if (threadIdx.x < 16 * l) {
         qv_s[threadIdx.x] = fp16_to_f32(qv_h);
         qu_s[threadIdx.x] = fp16_to_f32(qu_h);
@@ -371,8 +447,8 @@ __global__ __launch_bounds__(64 * NWM) void mdbf_pass2(fqm_mdbf md, const uint16
         f32x4 acc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        sign_products<NB, BPW>(path.S_A, path.ld_A, n, (r + 7) / 8, D2 + (int64_t)p * d2_path, nkb, sg, ncb, i0,
-                          3 * l * nb_rows, wave, nw, acc);
+        sign_products<NB, BPW>(path.S_A, path.ld_A, n, (r + 7) / 8, D2 + (int64_t)p * d2_path, 0u, nkb, sg, ncb, i0,
+                          3 * l * nb_rows, wave, nw, acc, [] {});
         if (p == 0 && threadIdx.x < 16 * l) {
             amp_s[0][threadIdx.x] = fp16_to_f32(amp_h[0]);
             amp_s[1][threadIdx.x] = fp16_to_f32(amp_h[1]);
@@ -411,12 +487,12 @@ inline Split split_k(int64_t nkb, int cap, int floor, int maxb) {
     return {bpw, (int)std::max<int64_t>(floor, nw)};
 }
 
-template <int NB, int BPW>
-hipError_t launch_pass1(const fqm_weights& w, int batch, uint16_t* D1, uint16_t* D2, const MdbfDims& d, int nw,
-                        hipStream_t s) {
-    hipLaunchKernelGGL((mdbf_pass1<NB, BPW>), dim3((unsigned)(d.r_pad / 16), (unsigned)d.nsg, (unsigned)w.mdbf.P),
-                       dim3(64 * nw), 0, s, w.mdbf, D1, D2, w.cols, batch, d.ncb, d.m_pad, d.r_pad, d.d1_path,
-                       d.d2_path);
+template <int NB, int BPW, bool FUSE>
+hipError_t launch_pass1(const fqm_weights& w, const uint16_t* x, int batch, uint16_t* D1, uint16_t* D2,
+                        const MdbfDims& d, int nw, hipStream_t s) {
+    hipLaunchKernelGGL((mdbf_pass1<NB, BPW, FUSE>),
+                       dim3((unsigned)(d.r_pad / 16), (unsigned)d.nsg, (unsigned)w.mdbf.P), dim3(64 * nw), 0, s,
+                       w.mdbf, x, D1, D2, w.cols, batch, d.ncb, d.m_pad, d.r_pad, d.d1_path, d.d2_path);
     return hipGetLastError();
 }
 
@@ -428,9 +504,23 @@ hipError_t launch_pass2(const fqm_weights& w, void* y, int y_f32, int batch, uin
     return hipGetLastError();
 }
 
+// Whether pass 1 forms its dense operand in LDS (no prep launch): one column
+// block whose live columns over the padded K fit FUSE_LDS, and few enough
+// products that every thread of a nw-wave group fills its share with one
+// batch of loads (as a separate launch, prep costs less than a longer fill).
+inline bool fuse_prep(const MdbfDims& d, int l, int batch, int nw) {
+    const int64_t cols = (int64_t)3 * l * std::min(d.bs, batch);
+    return d.ncb == 1 && cols * d.m_pad * 2 <= FUSE_LDS &&
+           (int64_t)l * std::min(d.bs, batch) * (d.m_pad / 2) <= (int64_t)FILL_PAIRS * 64 * nw;
+}
+
+// Waves per workgroup (pass 1, pass 2) and blocks per wave chunk.
+struct Plan {
+    Split k1, k2;
+};
+
 template <int NB>
-hipError_t launch_nb(const fqm_weights& w, void* y, int y_f32, int batch, uint16_t* D1, uint16_t* D2,
-                     const MdbfDims& d, hipStream_t s) {
+Plan plan_passes(const fqm_weights& w, int batch, const MdbfDims& d) {
     const fqm_mdbf& md = w.mdbf;
     // At least one thread per envelope value of the tile's 16 rows (16 l <=
     // 256), and in pass 2 one per (row, batch row) of the slice (16 bs <=
@@ -443,17 +533,24 @@ hipError_t launch_nb(const fqm_weights& w, void* y, int y_f32, int batch, uint16
     const int f2 = std::max(env, (16 * std::min(d.bs, batch) + 63) / 64);
     const int c1 = (int)std::min<int64_t>(NWM, std::max<int64_t>(env, (4096 + t1 - 1) / t1));
     const int c2 = (int)std::min<int64_t>(NWM, std::max<int64_t>(f2, (4096 + t2 - 1) / t2));
-    const Split k1 = split_k(d.m_pad / KB, c1, env, MAXB), k2 = split_k(d.r_pad / KB, c2, f2, MAXB);
+    return {split_k(d.m_pad / KB, c1, env, MAXB), split_k(d.r_pad / KB, c2, f2, MAXB)};
+}
+
+template <int NB, bool FUSE>
+hipError_t launch_nb(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch, uint16_t* D1,
+                     uint16_t* D2, const MdbfDims& d, const Plan& pl, hipStream_t s) {
+    constexpr int MAXB = NB == 1 ? 8 : 4;
+    const Split k1 = pl.k1, k2 = pl.k2;
     hipError_t e;
     switch (k1.bpw) {
-        case 1: e = launch_pass1<NB, 1>(w, batch, D1, D2, d, k1.nw, s); break;
-        case 2: e = launch_pass1<NB, 2>(w, batch, D1, D2, d, k1.nw, s); break;
-        case 3: e = launch_pass1<NB, 3>(w, batch, D1, D2, d, k1.nw, s); break;
-        case 4: e = launch_pass1<NB, 4>(w, batch, D1, D2, d, k1.nw, s); break;
-        case 5: e = launch_pass1<NB, NB == 1 ? 5 : 4>(w, batch, D1, D2, d, k1.nw, s); break;
-        case 6: e = launch_pass1<NB, NB == 1 ? 6 : 4>(w, batch, D1, D2, d, k1.nw, s); break;
-        case 7: e = launch_pass1<NB, NB == 1 ? 7 : 4>(w, batch, D1, D2, d, k1.nw, s); break;
-        default: e = launch_pass1<NB, MAXB>(w, batch, D1, D2, d, k1.nw, s); break;
+        case 1: e = launch_pass1<NB, 1, FUSE>(w, x, batch, D1, D2, d, k1.nw, s); break;
+        case 2: e = launch_pass1<NB, 2, FUSE>(w, x, batch, D1, D2, d, k1.nw, s); break;
+        case 3: e = launch_pass1<NB, 3, FUSE>(w, x, batch, D1, D2, d, k1.nw, s); break;
+        case 4: e = launch_pass1<NB, 4, FUSE>(w, x, batch, D1, D2, d, k1.nw, s); break;
+        case 5: e = launch_pass1<NB, NB == 1 ? 5 : 4, FUSE>(w, x, batch, D1, D2, d, k1.nw, s); break;
+        case 6: e = launch_pass1<NB, NB == 1 ? 6 : 4, FUSE>(w, x, batch, D1, D2, d, k1.nw, s); break;
+        case 7: e = launch_pass1<NB, NB == 1 ? 7 : 4, FUSE>(w, x, batch, D1, D2, d, k1.nw, s); break;
+        default: e = launch_pass1<NB, MAXB, FUSE>(w, x, batch, D1, D2, d, k1.nw, s); break;
     }
     if (e != hipSuccess) return e;
     switch (k2.bpw) {
@@ -481,14 +578,16 @@ hipError_t launch_mdbf_gemv(const fqm_weights& w, const uint16_t* x, void* y, in
     const MdbfDims d = mdbf_dims(w.cols, md.r, md.l, md.P, batch);
     uint16_t* D1 = static_cast<uint16_t*>(ws);
     uint16_t* D2 = D1 + d.d1_elems;
+    const Plan pl = d.ncb == 1 ? plan_passes<1>(w, batch, d) : plan_passes<4>(w, batch, d);
+    if (fuse_prep(d, md.l, batch, pl.k1.nw)) return launch_nb<1, true>(w, x, y, y_f32, batch, D1, D2, d, pl, s);
     hipLaunchKernelGGL(mdbf_prep, dim3((unsigned)(4 * d.m_pad / KB), (unsigned)(d.nsg * d.ncb), (unsigned)md.P),
                        dim3(256), 0, s, md, x, D1, w.cols, batch, d.nsg, d.ncb, d.m_pad / KB, d.d1_path);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // two to four column blocks share the four-block kernels (a block past
     // ncb re-reads a live column and its results are not read)
-    return d.ncb == 1 ? launch_nb<1>(w, y, y_f32, batch, D1, D2, d, s)
-                      : launch_nb<4>(w, y, y_f32, batch, D1, D2, d, s);
+    return d.ncb == 1 ? launch_nb<1, false>(w, x, y, y_f32, batch, D1, D2, d, pl, s)
+                      : launch_nb<4, false>(w, x, y, y_f32, batch, D1, D2, d, pl, s);
 }
 
 }  // namespace fqm

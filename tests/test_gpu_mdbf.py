@@ -48,10 +48,10 @@ def test_variants(l, P):
 
 
 # A batch slice is floor(64 / (3 l)) rows, at least 1 (three bf16 parts of
-# each of l envelopes per row fill the 64 operand columns): l = 16 splits a
-# batch of 16 into sixteen slices of one row, l = 3 into slices of 7, 7 and 2
-# (a partly empty last slice); m = 544 and r = 300 are not multiples of the
-# 256-column K block.
+# each of l envelopes per row fill at most four 16-column operand blocks):
+# l = 16 splits a batch of 16 into sixteen slices of one row, l = 3 into
+# slices of 7, 7 and 2 (a partly empty last slice); m = 544 and r = 300 are
+# not multiples of the 512-column K block.
 @pytest.mark.parametrize("l,P,batch", [(16, 1, 16), (3, 2, 16), (2, 1, 7), (1, 2, 1)])
 def test_batch_slices_and_padding(l, P, batch):
     n, m, r = 333, 544, 300
@@ -63,6 +63,23 @@ def test_batch_slices_and_padding(l, P, batch):
     torch.cuda.synchronize()
     assert canaries_intact(buf)
     assert_close(to_f64(y), oracle.mdbf.gemv_dense(paths, x, n, m, r), "f32", f"l={l} P={P} b={batch}")
+
+
+# The smallest shapes: m = 32 inputs (one 512-wide K block, 480 of its
+# columns padding), r = 5 (one sign byte per row of S_A, 3 of its bits
+# padding), two paths.  At batch 1 pass 1 forms its dense operand in LDS
+# itself; at batch 2 it reads the one that the prep launch wrote.
+@pytest.mark.parametrize("batch", [1, 2])
+def test_smallest_shapes(batch):
+    n, m, r, l, P = 40, 32, 5, 2, 2
+    inp, paths = case(n, m, r, l, P, 90)
+    x = synth.activations(batch, m, 91)
+    buf, y = guarded((batch, n), torch.float32)
+    print(f"mdbf n={n} m={m} r={r} l={l} P={P} batch {batch}", flush=True)
+    fqm.gemv(weights(inp), bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.mdbf.gemv_dense(paths, x, n, m, r), "f32", f"smallest b={batch}")
 
 
 def test_deterministic_and_batch_independent():
