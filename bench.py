@@ -286,7 +286,7 @@ def main():
                 fn=lambda s, ws=mcopies, x=x, y=y, wsp=wsp: fqm.gemv(ws[s % len(ws)], x, y=y, workspace=wsp),
                 bytes=mcopies[0].nbytes() + x.numel() * 2 + y.numel() * 2,
                 flops=2 * b * 2 * cfg["l"] * cfg["r"] * (cfg["n"] + cfg["m"]), bound="alu",
-                kernel=f"mdbf_gemv batch {b} (3 launches)")
+                kernel=f"mdbf_gemv batch {b} (passes 1 and 2, after a prep launch unless pass 1 forms its own operand)")
     t_gen = time.time() - t_gen
     if args.profile and not need <= set(rows):
         print(f"unknown row in {args.profile}; rows: {sorted(rows)}", file=sys.stderr)
