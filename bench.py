@@ -260,8 +260,11 @@ def main():
         for b in batches:
             x = bf16(synth.activations(b, cfg["cols"], cfg["seed"]))
             y = torch.empty((b, cfg["rows"]), dtype=torch.bfloat16, device=dev)
+            # vector centroids fold x into per-block terms in a workspace
+            nws = fqm.workspace_size(f0, b)
+            wsp = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
             rows[f"{key}_b{b}"] = dict(
-                fn=lambda s, ws=fcopies, x=x, y=y: fqm.gemv(ws[s % len(ws)], x, y=y),
+                fn=lambda s, ws=fcopies, x=x, y=y, wsp=wsp: fqm.gemv(ws[s % len(ws)], x, y=y, workspace=wsp),
                 bytes=f0.nbytes() + x.numel() * 2 + y.numel() * 2,
                 flops=2 * b * cfg["rows"] * cfg["cols"], bound="alu",
                 kernel=f"fabq_gemv {key[5:]} (block {inp.blocksize}, int{inp.hi_bits} rows) batch {b}")

@@ -304,6 +304,7 @@ fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream) {
 size_t fqm_workspace_size(const fqm_weights* w, int32_t batch) {
     if (check_weights(w) != FQM_OK || batch < 1 || batch > 16) return 0;
     if (w->format == FQM_LUT6 || w->format == FQM_LUT4) return fqm::lut_gemv_mfma_workspace(*w, batch);
+    if (w->format == FQM_FABQ) return fqm::fabq_workspace_bytes(*w, batch);
     if (w->format != FQM_MDBF) return 0;
     return fqm::mdbf_workspace_bytes(*w, batch);
 }
@@ -332,7 +333,12 @@ fqm_status gemv_launch(const fqm_weights* w, const uint16_t* x, void* y, int y_f
             return hip_status(
                 launch_lut4_gemv(*w, x, y, y_f32, batch, static_cast<float*>(workspace), s));
         }
-        case FQM_FABQ: return hip_status(launch_fabq_gemv(*w, x, y, y_f32, batch, s));
+        case FQM_FABQ: {
+            const size_t need = fqm_workspace_size(w, batch);
+            if (need && (!workspace || ws_bytes < need)) return FQM_E_WORKSPACE;
+            if (need && !aligned16(workspace)) return FQM_E_ALIGN;
+            return hip_status(launch_fabq_gemv(*w, x, y, y_f32, batch, static_cast<float*>(workspace), s));
+        }
         case FQM_MDBF: {
             const size_t need = fqm_workspace_size(w, batch);
             if (!workspace || ws_bytes < need) return FQM_E_WORKSPACE;

@@ -11,6 +11,14 @@
 //                                               + c[idx_b] * sum_{k in b} x[k] )
 // The second form is the per-weight decode s_b*(+-1) + c[idx_b] summed block
 // by block; the decoded weights are never rounded to bf16.
+//
+// With vector centroids (corr = V[tier][cb_base + idx_b][k mod 128]) the
+// correction of a block does not factor into c * sum x, but it depends on
+// the row only through (tier, idx_b): the block's term is
+//   G[b][blk][16 tier + idx] = sum_{k in blk} V[tier][cb_base + idx][k mod 128] x[b][k],
+// one value per batch row, block and active centroid (4 tiers x 16).  A first
+// launch folds x into G (the workspace); the GEMV then adds one G value per
+// binary row and block, so no centroid vector is read per weight.
 #include "fqm_internal.h"
 
 namespace fqm {
@@ -60,6 +68,57 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                           false);
 }
 
+// G (vector centroids): one workgroup per (batch row, block).  The 64 active
+// centroid vectors' residues the block touches (all 128 for blocks of 128
+// columns or more, else the block's own bs) are staged transposed in LDS
+// (s_v[j][e], rows of 65 floats: conflict-free stores and reads) and the
+// block's x in fp32; thread (q, e) sums the quarter q of the block's columns
+// for centroid e, and the four quarters are added in order.
+__global__ __launch_bounds__(256) void fabq_vec_fold(fqm_fabq f, const uint16_t* __restrict__ x,
+                                                     float* __restrict__ G, int64_t cols, int nblk) {
+    __shared__ float s_v[128 * 65];
+    __shared__ float s_x[512];
+    __shared__ float s_p[4][64];
+    const int tid = threadIdx.x, bs = f.blocksize;
+    const int blk = blockIdx.x % nblk, b = blockIdx.x / nblk;
+    const int64_t k0 = (int64_t)blk * bs;
+    const int nj = min(bs, 128);        // residues touched: j0 .. j0 + nj - 1
+    const int j0 = (int)(k0 & 127);     // 0 when bs >= 128; bs divides 128 otherwise, so no wrap
+    // every load goes out before the first store: float4 piece i = tid + 256 u
+    // of the 64 x nj slice (indices past it repeat the last piece), and x
+    // elements tid, tid + 256 of the block (clamped likewise)
+    const int n4 = 16 * nj;  // float4 pieces
+    float4 vv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int i = min(tid + 256 * u, n4 - 1), e = (4 * i) / nj, jj = 4 * i - e * nj;
+        vv[u] = *reinterpret_cast<const float4*>(
+            f.vcodebook + (int64_t)(64 * (e >> 4) + f.cb_base + (e & 15)) * 128 + j0 + jj);
+    }
+    uint16_t xb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) xb[u] = x[(int64_t)b * cols + k0 + min(tid + 256 * u, bs - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int i = min(tid + 256 * u, n4 - 1), e = (4 * i) / nj, jj = 4 * i - e * nj;
+        s_v[(jj + 0) * 65 + e] = vv[u].x;
+        s_v[(jj + 1) * 65 + e] = vv[u].y;
+        s_v[(jj + 2) * 65 + e] = vv[u].z;
+        s_v[(jj + 3) * 65 + e] = vv[u].w;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) s_x[min(tid + 256 * u, bs - 1)] = bf16_to_f32(xb[u]);
+    __syncthreads();
+    const int e = tid & 63, q = tid >> 6;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int k = q; k < bs; k += 4) acc = fmaf(s_v[(k & (nj - 1)) * 65 + e], s_x[k], acc);
+    s_p[q][e] = acc;
+    __syncthreads();
+    if (tid < 64)
+        G[((int64_t)b * nblk + blk) * 64 + tid] = ((s_p[0][tid] + s_p[1][tid]) + s_p[2][tid]) + s_p[3][tid];
+}
+
 // Vector-ALU kernel, one stored row per wave (batch 1..3, and every batch
 // for blocks of 16 columns or vector centroids).  Every lane runs the same
 // number of steps (indices past the row are clamped and their results dropped
@@ -68,8 +127,8 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // centroids (one pair per lane, looked up across lanes; the tier's window in
 // the tiered mode) are requested up front.  A sign dword covers 32 columns:
 // one block, part of one, or (16-column blocks) two, so its products are
-// summed per 16-column half.  VEC: the correction is a 128-float vector
-// centroid, sum_k V[k mod 128] x[k] over the half, in fp32.
+// summed per 16-column half.  VEC: the correction of each block is its G
+// value, added by the lane whose dword starts the block.
 // XL: x (B rows, cols % 32 == 0) is staged in LDS once per workgroup, every
 // wave then reads it there instead of through the vector L1.  16-byte piece
 // n of an x row sits at piece slot (n & ~3) | ((n & 3) ^ ((n >> 4) & 3)), so
@@ -79,9 +138,9 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 template <int B, bool VEC, bool XL>
 __global__ __launch_bounds__(64 * kWaves) void fabq_gemv_kernel(fqm_fabq f, const uint16_t* __restrict__ x,
                                                         void* __restrict__ y, int y_f32,
-                                                        int64_t rows, int64_t cols) {
+                                                        int64_t rows, int64_t cols, const float* __restrict__ G) {
     constexpr int UI = B == 1 ? 5 : 1;             // high-row steps per group (64 dwords of fields each)
-    constexpr int UB = (B == 1 && !VEC) ? 3 : 1;   // binary steps per group (64 dwords of 32 signs each)
+    constexpr int UB = B == 1 ? 3 : 1;             // binary steps per group (64 dwords of 32 signs each)
     extern __shared__ __attribute__((aligned(16))) uint4 s_xl[];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -205,7 +264,6 @@ __global__ __launch_bounds__(64 * kWaves) void fabq_gemv_kernel(fqm_fabq f, cons
         const bool bs16 = f.blocksize == 16;
         const int wshift = bs16 ? 0 : __builtin_ctz((unsigned)f.blocksize) - 5;  // log2(sign dwords per block)
         const int nw = (int)((cols + 31) / 32);  // 16-column blocks: the last dword may hold one block
-        const float* vrow = VEC ? f.vcodebook + (int64_t)cbase * 128 : nullptr;
         for (int p0 = 0; p0 < nw; p0 += 64 * UB) {
             uint32_t d[UB];
             uint16_t sbits[UB][2];
@@ -236,16 +294,15 @@ __global__ __launch_bounds__(64 * kWaves) void fabq_gemv_kernel(fqm_fabq f, cons
                 const int id0 = bs16 ? (ibits[u] & 15) : (ibits[u] >> (4 * bodd[u])) & 15;
                 const int id1 = bs16 ? (ibits[u] >> 4) : id0;
                 float c0 = 0.f, c1 = 0.f;
-                float4 v[2][4];
+                // VEC: this dword starts block blk0 (always with 16-column
+                // blocks, whose second half is block blk0 + 1 when it exists)
+                int blk0 = 0;
+                bool first = false, second = false;
                 if (VEC) {
                     const int p = min(p0 + 64 * u + lane, nw - 1);
-                    const float* v0 = vrow + id0 * 128 + ((32 * p) & 127);
-                    const float* v1 = vrow + id1 * 128 + ((32 * p) & 127) + 16;
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        v[0][q4] = reinterpret_cast<const float4*>(v0)[q4];
-                        v[1][q4] = reinterpret_cast<const float4*>(v1)[q4];
-                    }
+                    blk0 = bs16 ? 2 * p : p >> wshift;
+                    first = bs16 || (p & ((1 << wshift) - 1)) == 0;
+                    second = bs16 && 32 * (int64_t)p + 16 < cols;
                 } else {
                     const uint32_t cp0 = (uint32_t)__shfl((int)cbits, id0 >> 1);
                     const uint32_t cp1 = (uint32_t)__shfl((int)cbits, id1 >> 1);
@@ -257,7 +314,13 @@ __global__ __launch_bounds__(64 * kWaves) void fabq_gemv_kernel(fqm_fabq f, cons
                 signs32_to_bf16(d[u], ones, sv);
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
-                    float ps[2] = {0.f, 0.f}, xsum[2] = {0.f, 0.f}, vx[2] = {0.f, 0.f};
+                    float ps[2] = {0.f, 0.f}, xsum[2] = {0.f, 0.f};
+                    float g0 = 0.f, g1 = 0.f;
+                    if (VEC) {
+                        const float* gb = G + (int64_t)b * nb * 64 + 16 * (tier & 3);
+                        if (first) g0 = gb[(int64_t)blk0 * 64 + id0];
+                        if (second) g1 = gb[(int64_t)(blk0 + 1) * 64 + id1];
+                    }
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
                         const int half = h >> 1;
@@ -265,23 +328,16 @@ __global__ __launch_bounds__(64 * kWaves) void fabq_gemv_kernel(fqm_fabq f, cons
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
                             ps[half] = dot2_bf16(sv[4 * h + t], xs[t], ps[half]);
-                            if (VEC) {
-                                const float4 vv = v[half][2 * (h & 1) + (t >> 1)];
-                                const float vl = (t & 1) ? vv.z : vv.x, vh = (t & 1) ? vv.w : vv.y;
-                                vx[half] = fmaf(vl, bf16lo(xs[t]), fmaf(vh, bf16hi(xs[t]), vx[half]));
-                            } else {
-                                xsum[half] = dot2_bf16(ones, xs[t], xsum[half]);
-                            }
+                            if (!VEC) xsum[half] = dot2_bf16(ones, xs[t], xsum[half]);
                         }
                     }
                     if (32 * (p0 + 64 * u + lane) + 16 >= cols) {  // the dword's second half is past the row
                         ps[1] = 0.f;
                         xsum[1] = 0.f;
-                        vx[1] = 0.f;
                     }
                     float a = acc[b];
                     if (VEC) {
-                        a = fmaf(s0, ps[0], fmaf(s1, ps[1], a + (vx[0] + vx[1])));
+                        a = fmaf(s0, ps[0], fmaf(s1, ps[1], a + (g0 + g1)));
                     } else {
                         a = fmaf(s0, ps[0], fmaf(c0, xsum[0], a));
                         a = fmaf(s1, ps[1], fmaf(c1, xsum[1], a));
@@ -359,9 +415,10 @@ __device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t d) {
 template <bool HI8>
 __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(HI8 ? 2 : 4))) void fabq_gemv_mfma_kernel(fqm_fabq f, const uint16_t* __restrict__ x,
                                                                   void* __restrict__ y, int y_f32, int rows,
-                                                                  int cols, int batch) {
+                                                                  int cols, int batch, const float* __restrict__ G) {
     __shared__ float s_sc[16 * kMaxNB];     // [row][blk]: s_b (binary) or 1 (high rows)
-    __shared__ float s_cv[16 * kMaxNB];     // [row][blk]: the block's centroid (binary) or 0 (high rows)
+    __shared__ float s_cv[16 * kMaxNB];     // [row][blk]: the block's centroid (binary) or 0 (high rows, vector centroids)
+    __shared__ uint8_t s_e[16 * kMaxNB];    // vector centroids: [row][blk] the G entry 16 tier + idx of binary rows
     __shared__ f32x4_t s_red[kMW * 64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -416,8 +473,8 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(HI8 ? 
     const int64_t ejb = max(esr - f.n_hi, 0);
     const uint16_t* ps = has_bin ? f.s_blk + ejb * nblk + eb : x;
     const uint8_t* pi = has_bin ? f.idx + ejb * f.ld_idx + (eb >> 1) : reinterpret_cast<const uint8_t*>(x);
-    const bool tiered = f.cb_mode == FQM_CB_TIERED;
-    const uint8_t* pt = (has_bin && tiered) ? f.tier + ejb : reinterpret_cast<const uint8_t*>(x);
+    const bool tiered = f.cb_mode == FQM_CB_TIERED, vec = f.cb_mode == FQM_CB_VECTOR;
+    const uint8_t* pt = (has_bin && f.cb_mode != FQM_CB_SCALAR16) ? f.tier + ejb : reinterpret_cast<const uint8_t*>(x);
     const uint16_t sraw = *ps;
     const uint8_t iraw = *pi, traw = *pt;
     __builtin_amdgcn_sched_barrier(0);
@@ -430,25 +487,31 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(HI8 ? 
     // centroid of binary row jb's block: the codebook entry, or the row's
     // tier window entry
     auto centroid = [&](int64_t jb, uint32_t id, uint32_t t) {
-        return fp16_to_f32(f.codebook[(tiered ? 64 * t + f.cb_base : 0) + id]);
+        return vec ? 0.f : fp16_to_f32(f.codebook[(tiered ? 64 * t + f.cb_base : 0) + id]);
     };
     if (tid < ne) {
         const bool bin = esr >= f.n_hi;
+        const uint32_t id = (iraw >> ((eb & 1) * 4)) & 15u;
         s_sc[er * kMaxNB + eb] = bin ? fp16_to_f32(sraw) : 1.f;
-        s_cv[er * kMaxNB + eb] = bin ? centroid(ejb, (iraw >> ((eb & 1) * 4)) & 15u, traw) : 0.f;
+        s_cv[er * kMaxNB + eb] = bin ? centroid(ejb, id, traw) : 0.f;
+        s_e[er * kMaxNB + eb] = (uint8_t)(16 * (traw & 3u) + id);
     }
     for (int e = tid + 64 * kMW; e < ne; e += 64 * kMW) {  // blocks shorter than 5120 / 32 columns
         const int r = e / nblk, blk = e - r * nblk;
         const int sr = min(r0 + r, rows - 1);
         float sc = 1.f, cv = 0.f;
+        uint32_t ge = 0;
         if (sr >= f.n_hi) {
             const int64_t jb = sr - f.n_hi;
+            const uint32_t id = (f.idx[jb * f.ld_idx + (blk >> 1)] >> ((blk & 1) * 4)) & 15u;
+            const uint32_t t = f.cb_mode != FQM_CB_SCALAR16 ? f.tier[jb] : 0u;
             sc = fp16_to_f32(f.s_blk[jb * nblk + blk]);
-            cv = centroid(jb, (f.idx[jb * f.ld_idx + (blk >> 1)] >> ((blk & 1) * 4)) & 15u,
-                          tiered ? f.tier[jb] : 0u);
+            cv = centroid(jb, id, t);
+            ge = 16 * (t & 3u) + id;
         }
         s_sc[r * kMaxNB + blk] = sc;
         s_cv[r * kMaxNB + blk] = cv;
+        s_e[r * kMaxNB + blk] = (uint8_t)ge;
     }
     __syncthreads();  // tables
 
@@ -517,6 +580,12 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(HI8 ? 
         const int sr = r0 + row;
         if (sr < rows && col < batch) {
             v *= srow < f.n_hi ? fp16_to_f32(hraw) : 1.f;
+            if (vec && srow >= f.n_hi) {  // vector centroids: the binary row's G values, block by block
+                const float* gb = G + (int64_t)col * nblk * 64;
+                float gs = 0.f;
+                for (int blk = 0; blk < nblk; ++blk) gs += gb[(int64_t)blk * 64 + s_e[row * kMaxNB + blk]];
+                v += gs;
+            }
             const int64_t o = (int64_t)col * rows + out_row;
             if (y_f32)
                 reinterpret_cast<float*>(y)[o] = v;
@@ -530,66 +599,86 @@ __global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(HI8 ? 
 constexpr int64_t kMaxXL = 64 * 1024;
 
 template <int B>
-hipError_t launch_b(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
+hipError_t launch_b(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, const float* G, hipStream_t s) {
     const unsigned grid = (unsigned)((w.rows + kWaves - 1) / kWaves);
     const int64_t xl = (int64_t)B * w.cols * 2;
-    // (with vector centroids the LDS copy measured slower: those rows also
-    // stream the 128 KB centroid table through the L1)
-    const bool use_xl = w.fabq.cb_mode != FQM_CB_VECTOR && w.cols % 32 == 0 && xl <= kMaxXL;
+    const bool use_xl = w.cols % 32 == 0 && xl <= kMaxXL;
     if (w.fabq.cb_mode == FQM_CB_VECTOR) {
-        hipLaunchKernelGGL((fabq_gemv_kernel<B, true, false>), dim3(grid), dim3(64 * kWaves), 0, s, w.fabq, x, y,
-                           y_f32, w.rows, w.cols);
+        if (use_xl)
+            hipLaunchKernelGGL((fabq_gemv_kernel<B, true, true>), dim3(grid), dim3(64 * kWaves), (size_t)xl, s,
+                               w.fabq, x, y, y_f32, w.rows, w.cols, G);
+        else
+            hipLaunchKernelGGL((fabq_gemv_kernel<B, true, false>), dim3(grid), dim3(64 * kWaves), 0, s, w.fabq, x,
+                               y, y_f32, w.rows, w.cols, G);
     } else {
         if (use_xl)
             hipLaunchKernelGGL((fabq_gemv_kernel<B, false, true>), dim3(grid), dim3(64 * kWaves), (size_t)xl, s,
-                               w.fabq, x, y, y_f32, w.rows, w.cols);
+                               w.fabq, x, y, y_f32, w.rows, w.cols, G);
         else
             hipLaunchKernelGGL((fabq_gemv_kernel<B, false, false>), dim3(grid), dim3(64 * kWaves), 0, s, w.fabq, x, y,
-                               y_f32, w.rows, w.cols);
+                               y_f32, w.rows, w.cols, G);
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Vector centroids need G: batch x blocks x 64 fp32 in the workspace, when
+// the layer has binary rows.
+size_t fabq_workspace_bytes(const fqm_weights& w, int batch) {
+    const fqm_fabq& f = w.fabq;
+    if (f.cb_mode != FQM_CB_VECTOR || w.rows <= f.n_hi || w.cols <= 0 || f.blocksize <= 0) return 0;
+    const size_t n = (size_t)batch * (size_t)(w.cols / f.blocksize) * 64 * sizeof(float);
+    return (n + 15) / 16 * 16;
+}
+
 // The matrix-core kernel takes batch >= 4 when blocks are at least 32 columns
-// (a 32-wide k slice never holds two blocks), the centroids are scalars, the
-// per-block tables of 16 rows fit its LDS (cols / blocksize <= 256) and the
-// sizes fit 32 bits; the VALU kernel takes the rest (at batch 1 it is the
-// faster one: 8.8 against 19 us on the 5120 x 5120 layer, where 8 batch rows
-// take 31 against 23 us).
+// (a 32-wide k slice never holds two blocks), the per-block tables of 16 rows
+// fit its LDS (cols / blocksize <= 256) and the sizes fit 32 bits; the VALU
+// kernel takes the rest (at batch 1 it is the faster one: 8.8 against 19 us on
+// the 5120 x 5120 layer, where 8 batch rows take 31 against 23 us).
 hipError_t launch_fabq_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
-                            int batch, hipStream_t s) {
+                            int batch, float* ws, hipStream_t s) {
     fqm_weights v = w;
     if (!v.fabq.hi_bits) v.fabq.hi_bits = 4;
     const fqm_fabq& f = v.fabq;
-    if (batch >= 4 && f.blocksize >= 32 && f.cb_mode != FQM_CB_VECTOR && v.cols / f.blocksize <= kMaxNB &&
-        v.rows <= 0x7fffffff && v.cols <= 0x7fffffff) {
+    const float* G = nullptr;
+    if (fabq_workspace_bytes(v, batch)) {
+        if (!ws || v.cols / f.blocksize > 0x7fffffff / 16 || (int64_t)batch * (v.cols / f.blocksize) > 0x7fffffff)
+            return hipErrorInvalidValue;
+        const int nblk = (int)(v.cols / f.blocksize);
+        hipLaunchKernelGGL(fabq_vec_fold, dim3((unsigned)(batch * nblk)), dim3(256), 0, s, f, x, ws, v.cols, nblk);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        G = ws;
+    }
+    if (batch >= 4 && f.blocksize >= 32 && v.cols / f.blocksize <= kMaxNB && v.rows <= 0x7fffffff &&
+        v.cols <= 0x7fffffff) {
         if (f.hi_bits == 8)
             hipLaunchKernelGGL(fabq_gemv_mfma_kernel<true>, dim3((unsigned)((v.rows + 15) / 16)), dim3(64 * kMW), 0, s,
-                               f, x, y, y_f32, (int)v.rows, (int)v.cols, batch);
+                               f, x, y, y_f32, (int)v.rows, (int)v.cols, batch, G);
         else
             hipLaunchKernelGGL(fabq_gemv_mfma_kernel<false>, dim3((unsigned)((v.rows + 15) / 16)), dim3(64 * kMW), 0,
-                               s, f, x, y, y_f32, (int)v.rows, (int)v.cols, batch);
+                               s, f, x, y, y_f32, (int)v.rows, (int)v.cols, batch, G);
         return hipGetLastError();
     }
     switch (batch) {
-        case 1: return launch_b<1>(v, x, y, y_f32, s);
-        case 2: return launch_b<2>(v, x, y, y_f32, s);
-        case 3: return launch_b<3>(v, x, y, y_f32, s);
-        case 4: return launch_b<4>(v, x, y, y_f32, s);
-        case 5: return launch_b<5>(v, x, y, y_f32, s);
-        case 6: return launch_b<6>(v, x, y, y_f32, s);
-        case 7: return launch_b<7>(v, x, y, y_f32, s);
-        case 8: return launch_b<8>(v, x, y, y_f32, s);
-        case 9: return launch_b<9>(v, x, y, y_f32, s);
-        case 10: return launch_b<10>(v, x, y, y_f32, s);
-        case 11: return launch_b<11>(v, x, y, y_f32, s);
-        case 12: return launch_b<12>(v, x, y, y_f32, s);
-        case 13: return launch_b<13>(v, x, y, y_f32, s);
-        case 14: return launch_b<14>(v, x, y, y_f32, s);
-        case 15: return launch_b<15>(v, x, y, y_f32, s);
-        case 16: return launch_b<16>(v, x, y, y_f32, s);
+        case 1: return launch_b<1>(v, x, y, y_f32, G, s);
+        case 2: return launch_b<2>(v, x, y, y_f32, G, s);
+        case 3: return launch_b<3>(v, x, y, y_f32, G, s);
+        case 4: return launch_b<4>(v, x, y, y_f32, G, s);
+        case 5: return launch_b<5>(v, x, y, y_f32, G, s);
+        case 6: return launch_b<6>(v, x, y, y_f32, G, s);
+        case 7: return launch_b<7>(v, x, y, y_f32, G, s);
+        case 8: return launch_b<8>(v, x, y, y_f32, G, s);
+        case 9: return launch_b<9>(v, x, y, y_f32, G, s);
+        case 10: return launch_b<10>(v, x, y, y_f32, G, s);
+        case 11: return launch_b<11>(v, x, y, y_f32, G, s);
+        case 12: return launch_b<12>(v, x, y, y_f32, G, s);
+        case 13: return launch_b<13>(v, x, y, y_f32, G, s);
+        case 14: return launch_b<14>(v, x, y, y_f32, G, s);
+        case 15: return launch_b<15>(v, x, y, y_f32, G, s);
+        case 16: return launch_b<16>(v, x, y, y_f32, G, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -104,8 +104,11 @@ hipError_t launch_lut_gemv_mfma(const fqm_weights& w, const uint16_t* x, void* y
 size_t lut_gemm_workspace(const fqm_weights& w, int64_t M);
 hipError_t launch_lut_gemm(const fqm_weights& w, const uint16_t* X, uint16_t* Y, int64_t M, void* ws,
                            size_t ws_bytes, hipStream_t s);
+// FABQ: ws holds the vector-centroid terms G (fabq_workspace_bytes; other
+// codebook modes need none and ws may be null).
+size_t fabq_workspace_bytes(const fqm_weights& w, int batch);
 hipError_t launch_fabq_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
-                            int batch, hipStream_t s);
+                            int batch, float* ws, hipStream_t s);
 // MDBF: workspace holds the bf16 hi/lo dense operands of both passes.
 size_t mdbf_workspace_bytes(const fqm_weights& w, int batch);
 hipError_t launch_mdbf_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch, void* ws,

@@ -247,7 +247,12 @@ fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
  * cols a multiple of 512 split K over workgroups unless rows > 16368, and
  * then need S*batch*rows*4 (S fp32 partial sums per output, S <= cols / 512,
  * a function of rows and cols only, the same for both formats), else 0;
- * 0 for FABQ.
+ * FABQ with FQM_CB_VECTOR and at least one binary row
+ * batch*(cols/blocksize)*64*4 rounded up to 16 (per batch row, block and
+ * active centroid 16*tier + idx, the block's sum over its columns k of
+ * vcodebook[tier][cb_base + idx][k % 128] * x[k] in fp32, formed by a first
+ * launch; the GEMV then adds one such term per binary row and block), other
+ * FABQ modes 0.
  * Returns 0 for an invalid descriptor. */
 size_t fqm_workspace_size(const fqm_weights* w, int32_t batch);
 

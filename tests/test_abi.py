@@ -228,6 +228,33 @@ def test_fabq_argument_errors(lib):
     assert lib.fqm_workspace_size(ctypes.byref(fabq()), 4) == 0
 
 
+def test_fabq_vector_workspace(lib):
+    """Vector centroids fold x into one fp32 term per batch row, block and
+    active centroid (4 tiers x 16) before the GEMV: batch x blocks x 64 x 4
+    bytes of workspace, none without binary rows; a missing or short
+    workspace is refused before anything is enqueued."""
+    w = fabq()
+    w.fabq.cb_mode, w.fabq.tier, w.fabq.vcodebook = 2, FAKE, FAKE
+    assert lib.fqm_workspace_size(ctypes.byref(w), 1) == 4 * 64 * 4
+    assert lib.fqm_workspace_size(ctypes.byref(w), 5) == 5 * 4 * 64 * 4
+    w16 = fabq(bs=16, cols=1040)
+    w16.fabq.cb_mode, w16.fabq.tier, w16.fabq.vcodebook = 2, FAKE, FAKE
+    w16.fabq.ld_q4, w16.fabq.ld_signs, w16.fabq.ld_idx = 528, 144, 48
+    assert lib.fqm_workspace_size(ctypes.byref(w16), 3) == 3 * 65 * 64 * 4
+    hi = fabq(n_hi=64)
+    hi.fabq.cb_mode, hi.fabq.tier, hi.fabq.vcodebook = 2, FAKE, FAKE
+    assert lib.fqm_workspace_size(ctypes.byref(hi), 4) == 0
+    for mode in (0, 1):
+        t = fabq()
+        t.fabq.cb_mode, t.fabq.tier = mode, FAKE
+        assert lib.fqm_workspace_size(ctypes.byref(t), 8) == 0
+    need = lib.fqm_workspace_size(ctypes.byref(w), 2)
+    assert gemv(lib, w, batch=2) == E["WORKSPACE"]
+    assert gemv(lib, w, batch=2, ws=FAKE, wsb=need - 16) == E["WORKSPACE"]
+    assert gemv(lib, w, batch=2, ws=FAKE + 8, wsb=need) == E["ALIGN"]
+    assert refused_before_launch(lib, lambda: gemv(lib, w, batch=2, ws=FAKE, wsb=need)) == E["BOUNDS"]
+
+
 def mdbf(r=2000, l=2, P=1, n=4096, m=4096):
     w = fqm._Weights()
     w.format, w.rows, w.cols = fqm.FQM_MDBF, n, m

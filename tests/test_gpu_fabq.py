@@ -113,7 +113,8 @@ def test_int4_minus_eight_gemv(hi_frac, batch):
 # (README's sweep), tiered codebooks of 4 x 64 centroids with 16 active per
 # layer and 128-float vector centroids (model card "Residual Codebook
 # Architecture").  Batches 1-3 run the VALU kernel; batch >= 4 the
-# matrix-core kernel except for 16-column blocks and vector centroids.
+# matrix-core kernel except for 16-column blocks.  Vector centroids first
+# fold x into per-block terms (a second launch, workspace).
 VARIANTS = [  # (hi_bits, cb_mode, blocksize)
     (8, 0, 64), (4, 0, 16), (4, 0, 32), (4, 1, 128), (8, 1, 32), (4, 1, 16),
     (4, 2, 128), (8, 2, 16), (4, 2, 512), (8, 2, 32)]

@@ -1,6 +1,6 @@
 """fqm_gemv_static (no workspace argument, for callers that cannot allocate)
 against fqm_gemv with a caller workspace, on the paths that use scratch: the
-K-split batch 2-16 LUT GEMV and MDBF.  Two calls in a row share the library's
+K-split batch 2-16 LUT GEMV, FABQ with vector centroids and MDBF.  Two calls in a row share the library's
 static scratch, the second with a smaller input, so a kernel reading scratch
 it did not write in the same call would show up as a mismatch."""
 import numpy as np
@@ -48,6 +48,21 @@ def test_lut4_two_calls_second_smaller():
         y_ws, y_st = _both(w, bf16_dev(x), torch.bfloat16)
         assert torch.equal(y_st.view(torch.int16), y_ws.view(torch.int16))
         assert_close(to_f64(y_st), oracle.lut4.gemv(packed, inp.lut, x, cols), "bf16", f"{rows}x{cols}")
+
+
+def test_fabq_vector_two_calls_second_smaller():
+    for rows, cols, seed, batch, bs in ((301, 1536, 61, 3, 16), (5120, 5120, 5, 8, 512)):
+        inp = synth.fabq_input(rows, cols, seed, blocksize=bs, cb_mode=2)
+        p = oracle.fabq.pack(inp)
+        w = fqm.FabqWeights.from_arrays(inp.rows, inp.cols, inp.blocksize, inp.n_hi, inp.row_of, inp.q4,
+                                        inp.s_hi, inp.signs, inp.s_blk, inp.idx, inp.codebook, device=DEV,
+                                        hi_bits=inp.hi_bits, cb_mode=inp.cb_mode, cb_base=inp.cb_base,
+                                        tier=inp.tier, vcodebook=inp.vcodebook)
+        x = synth.activations(batch, cols, seed + 7)
+        print(f"gemv_static fabq vector {rows}x{cols} block {bs} batch {batch}", flush=True)
+        y_ws, y_st = _both(w, bf16_dev(x), torch.float32)
+        assert torch.equal(y_st, y_ws)
+        assert_close(to_f64(y_st), oracle.fabq.gemv(p, x, rows, cols, bs, inp.n_hi), "f32", f"fabq {rows}x{cols}")
 
 
 def test_mdbf_two_calls_second_smaller():
