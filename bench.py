@@ -4,6 +4,7 @@ A step is one pass over every row of the path, each on its own seeded
 synthetic input already resident in HBM:
 
   lut6_up_b1, lut6_down_b1   LUT6 GEMV, batch 1 (W 17408x5120 and 5120x17408)
+  lut6_up_b2                 LUT6 GEMV, batch 2 (one decode for both batch rows)
   lut6_up_b8, lut6_down_b8   LUT6 GEMV, batch 8
   prefill                    LUT6 GEMM, X 2048x5120 times the up weights
   prefill_down               LUT6 GEMM, X 2048x17408 times the down weights (5120x17408)
@@ -155,7 +156,8 @@ def main():
                 fn=(lambda s, ws=lut6[name], x=x, y=y, off=off, wsp=wsp:
                     fqm.gemv(ws[(s + off) % len(ws)], x, y=y, workspace=wsp)),
                 bytes=nbytes, flops=2 * b * cfg["rows"] * cfg["cols"], bound="hbm",
-                kernel="lut6_gemv_rows, batch 1" if b == 1 else f"lut6_gemv_mfma, batch {b}")
+                kernel=("lut6_gemv_rows, batch 1" if b == 1 else
+                        "lut6_gemv_rows_batch, batch 2" if b == 2 else f"lut6_gemv_mfma, batch {b}"))
     if wanted("prefill"):
         M = C["prefill"]["M"]
         ws = lut6["up"]

@@ -244,6 +244,113 @@ __global__ __launch_bounds__(64 * WPG) void lut6_gemv_rows(const uint8_t* __rest
     }
 }
 
+// Batch rows B > 1 on the same layout: the workgroup stages B x blocks in LDS
+// (batch row b at piece offset b * CPR * 128, swizzled as above), every
+// pair of gathered weights meets the B x pairs in B v_dot2 (one decode for
+// all batch rows), and each wave reduces B row sums.  A scheduling barrier
+// closes every chunk, so the unrolled loop does not hoist later chunks' x
+// reads (their registers would multiply with B).
+template <int CPR, int WPG, int PC, int B>
+__global__ __launch_bounds__(64 * WPG) void lut6_gemv_rows_batch(const uint8_t* __restrict__ packed,
+                                                                 int64_t ld,
+                                                                 const uint16_t* __restrict__ lut,
+                                                                 const uint16_t* __restrict__ x,
+                                                                 void* __restrict__ y, int y_f32,
+                                                                 int rows) {
+    constexpr int NX = CPR * 128;                              // x of one batch row in 16-byte pieces
+    constexpr int XS = (B * NX + 64 * WPG - 1) / (64 * WPG);   // staging pieces per thread
+    __shared__ __attribute__((aligned(16))) u32x4_t s_x[B * NX];
+    __shared__ __attribute__((aligned(16))) uint32_t s_tab[WPG][32];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row_u = blockIdx.x * WPG + wv;
+    const int row = min(row_u, rows - 1);  // rows past the end repeat the last row (not stored)
+    const uint8_t* rowp = packed + (int64_t)row * ld + 12 * lane;
+
+    u32x4_t xs[XS];
+#pragma unroll
+    for (int u = 0; u < XS; ++u)
+        xs[u] = reinterpret_cast<const u32x4_t*>(x)[min(tid + u * 64 * WPG, B * NX - 1)];
+    const uint32_t tv = reinterpret_cast<const uint32_t*>(lut + (int64_t)row * 64)[lane & 31];
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint32_t cr[PC + 1][3];
+    auto load_codes = [&](int c) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(rowp + 768 * c);
+        cr[c % (PC + 1)][0] = __builtin_nontemporal_load(q);
+        cr[c % (PC + 1)][1] = __builtin_nontemporal_load(q + 1);
+        cr[c % (PC + 1)][2] = __builtin_nontemporal_load(q + 2);
+    };
+#pragma unroll
+    for (int c = 0; c < PC && c < CPR; ++c) load_codes(c);
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int u = 0; u < XS; ++u) {
+        const int t = min(tid + u * 64 * WPG, B * NX - 1), k = t % NX;  // batch row t / NX, piece k
+        s_x[(t - k) + (((k >> 7) << 7) | ((k & 1) << 6) | ((k >> 1) & 63))] = xs[u];
+    }
+    s_tab[wv][lane & 31] = tv;
+    __syncthreads();
+
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_u8*)s_tab + 128u * wv;
+    uint32_t mask = 0x7Eu;
+    asm volatile("" : "+v"(mask));
+    const uint32_t xb = (uint32_t)(uintptr_t)(lds_u8*)s_x + 16u * lane;
+    float acc0[B], acc1[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc0[b] = acc1[b] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) {
+        if (c + PC < CPR) load_codes(c + PC);
+        const uint32_t d0 = cr[c % (PC + 1)][0], d1 = cr[c % (PC + 1)][1], d2 = cr[c % (PC + 1)][2];
+        uint32_t a[16];
+        a[0] = (code_x2<0>(d0, d1, d2) & mask) | base;
+        a[1] = (code_x2<1>(d0, d1, d2) & mask) | base;
+        a[2] = (code_x2<2>(d0, d1, d2) & mask) | base;
+        a[3] = (code_x2<3>(d0, d1, d2) & mask) | base;
+        a[4] = (code_x2<4>(d0, d1, d2) & mask) | base;
+        a[5] = (code_x2<5>(d0, d1, d2) & mask) | base;
+        a[6] = (code_x2<6>(d0, d1, d2) & mask) | base;
+        a[7] = (code_x2<7>(d0, d1, d2) & mask) | base;
+        a[8] = (code_x2<8>(d0, d1, d2) & mask) | base;
+        a[9] = (code_x2<9>(d0, d1, d2) & mask) | base;
+        a[10] = (code_x2<10>(d0, d1, d2) & mask) | base;
+        a[11] = (code_x2<11>(d0, d1, d2) & mask) | base;
+        a[12] = (code_x2<12>(d0, d1, d2) & mask) | base;
+        a[13] = (code_x2<13>(d0, d1, d2) & mask) | base;
+        a[14] = (code_x2<14>(d0, d1, d2) & mask) | base;
+        a[15] = (code_x2<15>(d0, d1, d2) & mask) | base;
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            w[j] = __builtin_amdgcn_perm(*(lds_u16*)(uintptr_t)a[2 * j + 1], *(lds_u16*)(uintptr_t)a[2 * j],
+                                         0x05040100u);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const u32x4_t xl = *(lds_u4*)(uintptr_t)(xb + 16u * NX * b + 2048u * c);
+            const u32x4_t xh = *(lds_u4*)(uintptr_t)(xb + 16u * NX * b + 2048u * c + 1024u);
+            const uint32_t xv[8] = {xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]};
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                acc0[b] = dot2(w[j], xv[j], acc0[b]);
+                acc1[b] = dot2(w[j + 1], xv[j + 1], acc1[b]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float sum = wave_sum_lane63(acc0[b] + acc1[b]);
+        if (lane == 63 && row_u < rows) {
+            if (y_f32)
+                reinterpret_cast<float*>(y)[(int64_t)b * rows + row_u] = sum;
+            else
+                reinterpret_cast<uint16_t*>(y)[(int64_t)b * rows + row_u] = f32_to_bf16(sum);
+        }
+    }
+}
+
 template <int CPR, int S, int WPG, int PC>
 hipError_t launch_rows(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
     constexpr int RPG = WPG / S;
@@ -287,15 +394,52 @@ hipError_t launch_b1(const fqm_weights& w, const uint16_t* x, void* y, int y_f32
     return launch_cells<1>(w, x, y, y_f32, s);
 }
 
+// Batch 2 takes the batch-row kernel on rows of at most 8 cells (4-wave
+// groups; in 10-wave groups its registers spill).  Measured on the
+// 17408 x 5120 layer against the matrix-core kernel: batch 2 18.4-18.9 us
+// against 26.6 us, batch 3 23.8-24.2 against 25.1 us, batch 4 29.3-29.8
+// against 24.7 us; so batches 3-16 stay on the matrix cores.
+constexpr int kRowsMaxBatch = 2;
+constexpr int batch_max_cells(int) { return 8; }
+
+bool rows_batch_supported(const fqm_weights& w, int batch) {
+    return batch >= 2 && batch <= kRowsMaxBatch && rows_supported(w) && (w.cols >> 10) <= batch_max_cells(batch);
+}
+
+template <int CPR, int B>
+hipError_t launch_cells_batch(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
+    if constexpr (CPR > batch_max_cells(B)) {
+        return hipErrorInvalidValue;
+    } else {
+        if ((w.cols >> 10) != CPR) return launch_cells_batch<CPR + 1, B>(w, x, y, y_f32, s);
+        constexpr int WPG = 4;
+        const unsigned grid = (unsigned)((w.rows + WPG - 1) / WPG);
+        hipLaunchKernelGGL((lut6_gemv_rows_batch<CPR, WPG, 4, B>), dim3(grid), dim3(64 * WPG), 0, s,
+                           w.lut6.packed, w.lut6.ld, w.lut6.lut, x, y, y_f32, (int)w.rows);
+        return hipGetLastError();
+    }
+}
+
+hipError_t launch_rows_batch(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
+                             hipStream_t s) {
+    if (batch == 2) return launch_cells_batch<1, 2>(w, x, y, y_f32, s);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
+bool lut6_gemv_rows_path(const fqm_weights& w, int batch) {
+    return batch == 1 ? rows_supported(w) : rows_batch_supported(w, batch);
+}
+
 bool lut6_gemv_fast_path(const fqm_weights& w, int batch) {
-    return batch == 1 ? rows_supported(w) : lut_gemv_mfma_supported(w, batch);
+    return lut6_gemv_rows_path(w, batch) || (batch > 1 && lut_gemv_mfma_supported(w, batch));
 }
 
 hipError_t launch_lut6_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,
                             int batch, float* ws, hipStream_t s) {
     if (batch == 1 && rows_supported(w)) return launch_b1(w, x, y, y_f32, s);
+    if (rows_batch_supported(w, batch)) return launch_rows_batch(w, x, y, y_f32, batch, s);
     if (lut_gemv_mfma_supported(w, batch)) return launch_lut_gemv_mfma(w, x, y, y_f32, batch, ws, s);
     switch (batch) {
         case 1: return launch_b<1>(w, x, y, y_f32, s);

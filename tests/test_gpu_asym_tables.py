@@ -60,10 +60,11 @@ def test_dequant_bit_exact(bits):
 # (rows, cols, batch, seed): batch-1 cells (4- and 10-wave groups, the full
 # layers), generic widths (1088 is not whole cells), batch 2-16 on the matrix
 # cores with the K split (300 x 4096, the down layer) and without it (the up
-# layer, 1088 row blocks).
+# layer, 1088 row blocks), and batch 2 on whole cells (the one-row-per-wave
+# kernel for 6-bit codes).
 GEMV_CASES = [(1000, 3072, 1, 32), (5120, 17408, 1, 33), (17408, 5120, 1, 34),
               (1000, 1088, 1, 35), (1000, 1088, 3, 35), (300, 4096, 8, 36),
-              (300, 4096, 16, 36), (17408, 5120, 8, 34), (5120, 17408, 8, 33)]
+              (300, 4096, 16, 36), (17408, 5120, 8, 34), (5120, 17408, 8, 33), (1000, 3072, 2, 32)]
 
 
 @pytest.mark.parametrize("bits", [6, 4])

@@ -40,6 +40,30 @@ def test_gemv_mfma_cases(rows, cols, seed, batches, out):
         assert_close(to_f64(y), oracle.lut6.gemv(packed, inp.lut, x, cols), out, f"{rows}x{cols} b{b} {out}")
 
 
+# Batch 2 on 1-8 whole 1024-column cells takes the one-row-per-wave kernel
+# (both batch rows' x blocks in LDS, one decode per weight for the two rows):
+# every cell count, a last 4-row group that is partly past the end, and the
+# 17408 x 5120 layer.
+@pytest.mark.parametrize("rows,cols,seed", [(5, 1024, 40), (77, 3072, 41), (130, 8192, 42), (17408, 5120, 43)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemv_batch2_rows_kernel(rows, cols, seed, out):
+    inp, packed = lut6_case(rows, cols, seed)
+    w = lut6_weights(rows, cols, seed)
+    assert fqm.workspace_size(w, 2) == 0
+    x = synth.activations(2, cols, seed + 1)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    buf, y = guarded((2, rows), dt)
+    print(f"lut6 batch-2 rows kernel {rows}x{cols} {out}", flush=True)
+    fqm.gemv(w, bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.lut6.gemv(packed, inp.lut, x, cols), out, f"{rows}x{cols} b2 {out}")
+    if out == "f32" and rows < 1000:
+        # each batch row as its own batch-1 call: the same decode, the same sums
+        y1 = torch.stack([fqm.gemv(w, bf16_dev(x[b:b + 1]), out_dtype=torch.float32)[0] for b in range(2)])
+        assert torch.allclose(y, y1, rtol=1e-6, atol=0)
+
+
 def test_gemv_mfma_workspace_rule():
     # K is split while there are fewer than 1024 row blocks of 16
     assert fqm.workspace_size(lut6_weights(300, 4096, 21), 8) == 8 * 8 * 300 * 4
