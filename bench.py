@@ -4,7 +4,7 @@ A step is one pass over every row of the path, each on its own seeded
 synthetic input already resident in HBM:
 
   lut6_up_b1, lut6_down_b1   LUT6 GEMV, batch 1 (W 17408x5120 and 5120x17408)
-  lut6_up_b2                 LUT6 GEMV, batch 2 (one decode for both batch rows)
+  lut6_up_b2, lut6_down_b2   LUT6 GEMV, batch 2 (one decode for both batch rows)
   lut6_up_b8, lut6_down_b8   LUT6 GEMV, batch 8
   prefill                    LUT6 GEMM, X 2048x5120 times the up weights
   prefill_down               LUT6 GEMM, X 2048x17408 times the down weights (5120x17408)

@@ -97,7 +97,8 @@ bool lut_gemv_mfma_supported(const fqm_weights& w, int batch);
 // (the cell kernel at batch 1, the matrix-core kernel at 2..16)
 bool lut6_gemv_fast_path(const fqm_weights& w, int batch);
 // true when launch_lut6_gemv takes the one-row-per-wave kernels (batch 1 on
-// 1-31 whole 1024-column cells, batch 2 on 1-8 cells); they need no workspace
+// 1-31 whole 1024-column cells, batch 2 on 1-19, batch 3 on 1-12); they need
+// no workspace
 bool lut6_gemv_rows_path(const fqm_weights& w, int batch);
 size_t lut_gemv_mfma_workspace(const fqm_weights& w, int batch);
 hipError_t launch_lut_gemv_mfma(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,

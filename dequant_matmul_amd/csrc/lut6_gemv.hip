@@ -248,8 +248,8 @@ __global__ __launch_bounds__(64 * WPG) void lut6_gemv_rows(const uint8_t* __rest
 // (batch row b at piece offset b * CPR * 128, swizzled as above), every
 // pair of gathered weights meets the B x pairs in B v_dot2 (one decode for
 // all batch rows), and each wave reduces B row sums.  A scheduling barrier
-// closes every chunk, so the unrolled loop does not hoist later chunks' x
-// reads (their registers would multiply with B).
+// closes every chunk and the sums are pinned there, so the unrolled loop
+// keeps one chunk's operands live at a time.
 template <int CPR, int WPG, int PC, int B>
 __global__ __launch_bounds__(64 * WPG) void lut6_gemv_rows_batch(const uint8_t* __restrict__ packed,
                                                                  int64_t ld,
@@ -336,6 +336,10 @@ __global__ __launch_bounds__(64 * WPG) void lut6_gemv_rows_batch(const uint8_t* 
                 acc0[b] = dot2(w[j], xv[j], acc0[b]);
                 acc1[b] = dot2(w[j + 1], xv[j + 1], acc1[b]);
             }
+            // the sums pass through an empty asm at every chunk: without it the
+            // compiler sank whole dot2 chains to their last use, keeping every
+            // chunk's gathered weights and x live (registers grew with the chunks)
+            asm volatile("" : "+v"(acc0[b]), "+v"(acc1[b]));
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -394,13 +398,14 @@ hipError_t launch_b1(const fqm_weights& w, const uint16_t* x, void* y, int y_f32
     return launch_cells<1>(w, x, y, y_f32, s);
 }
 
-// Batch 2 takes the batch-row kernel on rows of at most 8 cells (4-wave
-// groups; in 10-wave groups its registers spill).  Measured on the
-// 17408 x 5120 layer against the matrix-core kernel: batch 2 18.4-18.9 us
-// against 26.6 us, batch 3 23.8-24.2 against 25.1 us, batch 4 29.3-29.8
-// against 24.7 us; so batches 3-16 stay on the matrix cores.
-constexpr int kRowsMaxBatch = 2;
-constexpr int batch_max_cells(int) { return 8; }
+// Batches 2 and 3 take the batch-row kernel while two 10-wave groups still
+// fit a CU (B * cells <= 38, at most 76 KB of x per group).  Measured against
+// the matrix-core kernel (same box, graph replays): 17408 x 5120 batch 2
+// 17.7-19.8 us against 26.5 us, batch 3 22.1-22.8 against 26.5-27.2 us, batch
+// 4 28.6-28.9 against 25.1 us; 5120 x 17408 batch 2 19.7-21.8 against
+// 26.0-27.4 us.  Batches 4-16 stay on the matrix cores.
+constexpr int kRowsMaxBatch = 3;
+constexpr int batch_max_cells(int b) { return 38 / b; }
 
 bool rows_batch_supported(const fqm_weights& w, int batch) {
     return batch >= 2 && batch <= kRowsMaxBatch && rows_supported(w) && (w.cols >> 10) <= batch_max_cells(batch);
@@ -412,7 +417,7 @@ hipError_t launch_cells_batch(const fqm_weights& w, const uint16_t* x, void* y, 
         return hipErrorInvalidValue;
     } else {
         if ((w.cols >> 10) != CPR) return launch_cells_batch<CPR + 1, B>(w, x, y, y_f32, s);
-        constexpr int WPG = 4;
+        constexpr int WPG = CPR <= 8 ? 4 : 10;
         const unsigned grid = (unsigned)((w.rows + WPG - 1) / WPG);
         hipLaunchKernelGGL((lut6_gemv_rows_batch<CPR, WPG, 4, B>), dim3(grid), dim3(64 * WPG), 0, s,
                            w.lut6.packed, w.lut6.ld, w.lut6.lut, x, y, y_f32, (int)w.rows);
@@ -423,6 +428,7 @@ hipError_t launch_cells_batch(const fqm_weights& w, const uint16_t* x, void* y, 
 hipError_t launch_rows_batch(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
                              hipStream_t s) {
     if (batch == 2) return launch_cells_batch<1, 2>(w, x, y, y_f32, s);
+    if (batch == 3) return launch_cells_batch<1, 3>(w, x, y, y_f32, s);
     return hipErrorInvalidValue;
 }
 

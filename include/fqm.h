@@ -247,8 +247,8 @@ fqm_status fqm_dequant(const fqm_weights* w, uint16_t* W, void* stream);
  * cols a multiple of 512 split K over workgroups unless rows > 16368, and
  * then need S*batch*rows*4 (S fp32 partial sums per output, S <= cols / 512,
  * a function of rows and cols only, the same for both formats), else 0;
- * LUT6 at batch 2 with cols = 1024*c, 1 <= c <= 8, needs none (one row per
- * wave, both batch rows from one decode);
+ * LUT6 at batch 2 with cols = 1024*c, 1 <= c <= 19, and at batch 3 with
+ * 1 <= c <= 12 needs none (one row per wave, every batch row from one decode);
  * FABQ with FQM_CB_VECTOR and at least one binary row
  * batch*(cols/blocksize)*64*4 rounded up to 16 (per batch row, block and
  * active centroid 16*tier + idx, the block's sum over its columns k of

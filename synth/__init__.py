@@ -431,7 +431,7 @@ def mdbf_input(n: int, m: int, r: int, l: int, P: int, seed: int,
 CONFIGS = {
     "tiny_lut6": dict(rows=256, cols=512, seed=1, batches=(1,), y="f32"),
     "lut6_up": dict(rows=17408, cols=5120, seed=2, batches=(1, 2, 8), y="bf16"),
-    "lut6_down": dict(rows=5120, cols=17408, seed=3, batches=(1, 8), y="bf16"),
+    "lut6_down": dict(rows=5120, cols=17408, seed=3, batches=(1, 2, 8), y="bf16"),
     "lut4_up": dict(rows=17408, cols=5120, seed=7, batches=(1, 8), y="bf16"),
     "lut4_down": dict(rows=5120, cols=17408, seed=8, batches=(1, 8), y="bf16"),
     "prefill": dict(M=2048, weights="lut6_up", seed=4),

@@ -153,12 +153,12 @@ def test_lut4_argument_errors(lib):
 def test_lut4_batch_workspace_follows_the_lut6_rule(lib):
     """Batches 2..16 of both LUT formats share the matrix-core kernel's K
     split, so the workspace depends on the shape and batch only."""
-    for rows, cols, batch in ((5120, 17408, 8), (5120, 17408, 16), (17408, 5120, 8), (300, 4096, 3),
-                              (5120, 17408, 1), (64, 1088, 4), (300, 17408, 2)):
+    for rows, cols, batch in ((5120, 17408, 8), (5120, 17408, 16), (17408, 5120, 8), (300, 4096, 4),
+                              (5120, 17408, 1), (64, 1088, 4), (300, 20480, 2)):
         a = lib.fqm_workspace_size(ctypes.byref(lut4(rows, cols, ld=cols // 2)), batch)
         b = lib.fqm_workspace_size(ctypes.byref(lut6(rows, cols, ld=cols * 3 // 4)), batch)
         assert a == b, (rows, cols, batch)
-    # except LUT6 at batch 2 on 1-8 whole 1024-column cells: one row per wave, no K split
+    # except LUT6 at batch 2 (3) on 1-19 (1-12) whole 1024-column cells: one row per wave, no K split
     assert lib.fqm_workspace_size(ctypes.byref(lut4(300, 4096, ld=2048)), 2) > 0
     assert lib.fqm_workspace_size(ctypes.byref(lut6(300, 4096, ld=3072)), 2) == 0
     need = lib.fqm_workspace_size(ctypes.byref(lut4(5120, 17408, ld=8704)), 8)
@@ -187,11 +187,14 @@ def test_lut6_workspace_rule(lib):
     assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=16368, cols=1024, ld=768)), 8) == 2 * 8 * 16368 * 4
     assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=4096, ld=3072)), 1) == 0
     assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=4032, ld=3024)), 8) == 0
-    # batch 2 on 1-8 whole 1024-column cells runs one row per wave: no workspace;
-    # 17 cells keep the matrix-core kernel and its K split
+    # batch 2 on 1-19 and batch 3 on 1-12 whole 1024-column cells run one row
+    # per wave: no workspace; past that the matrix-core kernel splits K
     assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=4096, ld=3072)), 2) == 0
-    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=8192, ld=6144)), 2) == 0
-    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=17408, ld=13056)), 2) > 0
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=17408, ld=13056)), 2) == 0
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=20480, ld=15360)), 2) > 0
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=12288, ld=9216)), 3) == 0
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=13312, ld=9984)), 3) > 0
+    assert lib.fqm_workspace_size(ctypes.byref(lut6(rows=300, cols=4096, ld=3072)), 4) > 0
     # a missing workspace is refused before anything is enqueued
     assert gemv(lib, lut6(rows=300, cols=4096, ld=3072), batch=8) == E["WORKSPACE"]
 

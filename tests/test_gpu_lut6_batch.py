@@ -40,27 +40,30 @@ def test_gemv_mfma_cases(rows, cols, seed, batches, out):
         assert_close(to_f64(y), oracle.lut6.gemv(packed, inp.lut, x, cols), out, f"{rows}x{cols} b{b} {out}")
 
 
-# Batch 2 on 1-8 whole 1024-column cells takes the one-row-per-wave kernel
-# (both batch rows' x blocks in LDS, one decode per weight for the two rows):
-# every cell count, a last 4-row group that is partly past the end, and the
-# 17408 x 5120 layer.
-@pytest.mark.parametrize("rows,cols,seed", [(5, 1024, 40), (77, 3072, 41), (130, 8192, 42), (17408, 5120, 43)])
+# Batches 2 and 3 on whole 1024-column cells (2: 1-19, 3: 1-12) take the
+# one-row-per-wave kernel (every batch row's x block in LDS, one decode per
+# weight for all rows): 4-wave groups up to 8 cells, 10-wave groups past
+# that, last groups partly past the end, the largest cell counts, and the
+# two MLP layers.
+@pytest.mark.parametrize("rows,cols,seed,batch", [(5, 1024, 40, 2), (77, 3072, 41, 3), (130, 8192, 42, 2),
+                                                  (23, 9216, 44, 2), (41, 12288, 45, 3), (11, 19456, 46, 2),
+                                                  (17408, 5120, 43, 2), (17408, 5120, 43, 3), (5120, 17408, 47, 2)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_gemv_batch2_rows_kernel(rows, cols, seed, out):
+def test_gemv_batch_rows_kernel(rows, cols, seed, batch, out):
     inp, packed = lut6_case(rows, cols, seed)
     w = lut6_weights(rows, cols, seed)
-    assert fqm.workspace_size(w, 2) == 0
-    x = synth.activations(2, cols, seed + 1)
+    assert fqm.workspace_size(w, batch) == 0
+    x = synth.activations(batch, cols, seed + 1)
     dt = torch.float32 if out == "f32" else torch.bfloat16
-    buf, y = guarded((2, rows), dt)
-    print(f"lut6 batch-2 rows kernel {rows}x{cols} {out}", flush=True)
+    buf, y = guarded((batch, rows), dt)
+    print(f"lut6 batch-{batch} rows kernel {rows}x{cols} {out}", flush=True)
     fqm.gemv(w, bf16_dev(x), y=y)
     torch.cuda.synchronize()
     assert canaries_intact(buf)
-    assert_close(to_f64(y), oracle.lut6.gemv(packed, inp.lut, x, cols), out, f"{rows}x{cols} b2 {out}")
+    assert_close(to_f64(y), oracle.lut6.gemv(packed, inp.lut, x, cols), out, f"{rows}x{cols} b{batch} {out}")
     if out == "f32" and rows < 1000:
         # each batch row as its own batch-1 call: the same decode, the same sums
-        y1 = torch.stack([fqm.gemv(w, bf16_dev(x[b:b + 1]), out_dtype=torch.float32)[0] for b in range(2)])
+        y1 = torch.stack([fqm.gemv(w, bf16_dev(x[b:b + 1]), out_dtype=torch.float32)[0] for b in range(batch)])
         assert torch.allclose(y, y1, rtol=1e-6, atol=0)
 
 

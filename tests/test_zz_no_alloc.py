@@ -1,6 +1,6 @@
 """fqm_gemv_static (no workspace argument, for callers that cannot allocate)
 against fqm_gemv with a caller workspace, on the paths that use scratch: the
-K-split batch 2-16 LUT GEMV, FABQ with vector centroids and MDBF.  Two calls in a row share the library's
+K-split matrix-core LUT GEMV (batch 2-16 where it runs), FABQ with vector centroids and MDBF.  Two calls in a row share the library's
 static scratch, the second with a smaller input, so a kernel reading scratch
 it did not write in the same call would show up as a mismatch."""
 import numpy as np
@@ -28,7 +28,7 @@ def _both(w, x, out_dtype):
 
 
 def test_lut6_two_calls_second_smaller():
-    for rows, cols, seed, batch in ((5120, 17408, 3, 8), (300, 4096, 21, 3)):
+    for rows, cols, seed, batch in ((5120, 17408, 3, 8), (300, 4096, 21, 5)):
         inp, packed = lut6_case(rows, cols, seed)
         w = lut6_weights(rows, cols, seed)
         x = synth.activations(batch, cols, seed + 7)
