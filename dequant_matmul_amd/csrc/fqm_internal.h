@@ -84,6 +84,9 @@ hipError_t launch_lut4_gemv(const fqm_weights& w, const uint16_t* x, void* y, in
 // true when launch_lut4_gemv takes a tuned kernel for this shape and batch
 // (the cell kernel at batch 1, the matrix-core kernel at 2..16)
 bool lut4_gemv_fast_path(const fqm_weights& w, int batch);
+// true when launch_lut4_gemv takes the one-row-per-wave kernels (batch 1 on
+// 1-31 whole cells, batch 2 on 1-19, batch 3 on 1-12); no workspace
+bool lut4_gemv_rows_path(const fqm_weights& w, int batch);
 hipError_t launch_dequant_fabq(const fqm_weights& w, uint16_t* W, hipStream_t s);
 
 hipError_t launch_lut6_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32,

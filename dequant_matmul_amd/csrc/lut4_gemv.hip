@@ -137,6 +137,111 @@ __global__ __launch_bounds__(64 * WPG) void lut4_gemv_cells(const uint8_t* __res
     }
 }
 
+// Batches 2 and 3: the batch-1 structure with every batch row's x block in
+// LDS (row b at piece offset b * CPR * 128); each pair of gathered weights
+// meets the B x pairs in B v_dot2, so a weight is decoded once for all batch
+// rows.  Every chunk ends in a scheduling barrier and passes the sums through
+// an empty asm, so the compiler cannot sink the dot2 chains to the final
+// reduction (that kept every chunk's operands live).
+template <int CPR, int WPG, int PC, int B>
+__global__ __launch_bounds__(64 * WPG) void lut4_gemv_cells_batch(const uint8_t* __restrict__ packed, int64_t ld,
+                                                                  const uint16_t* __restrict__ lut,
+                                                                  const uint16_t* __restrict__ x,
+                                                                  void* __restrict__ y, int y_f32, int rows) {
+    constexpr int NX = CPR * 128;                              // x of one batch row in 16-byte pieces
+    constexpr int XS = (B * NX + 64 * WPG - 1) / (64 * WPG);   // staging pieces per thread
+    __shared__ __attribute__((aligned(16))) u32x4_t s_x[B * NX];
+    __shared__ __attribute__((aligned(32))) uint32_t s_tab[WPG][8];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row_u = blockIdx.x * WPG + wv;
+    const int row = min(row_u, rows - 1);  // rows past the end repeat the last row (not stored)
+    const uint8_t* rowp = packed + (int64_t)row * ld + 8 * lane;
+
+    u32x4_t xs[XS];
+#pragma unroll
+    for (int u = 0; u < XS; ++u)
+        xs[u] = reinterpret_cast<const u32x4_t*>(x)[min(tid + u * 64 * WPG, B * NX - 1)];
+    const uint32_t tv = reinterpret_cast<const uint32_t*>(lut + (int64_t)row * 16)[lane & 7];
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint32_t cr[PC + 1][2];
+    auto load_codes = [&](int c) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(rowp + 512 * c);
+        cr[c % (PC + 1)][0] = __builtin_nontemporal_load(q);
+        cr[c % (PC + 1)][1] = __builtin_nontemporal_load(q + 1);
+    };
+#pragma unroll
+    for (int c = 0; c < PC && c < CPR; ++c) load_codes(c);
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int u = 0; u < XS; ++u) {
+        const int t = min(tid + u * 64 * WPG, B * NX - 1), k = t % NX;  // batch row t / NX, piece k
+        s_x[(t - k) + (((k >> 7) << 7) | ((k & 1) << 6) | ((k >> 1) & 63))] = xs[u];
+    }
+    s_tab[wv][lane & 7] = tv;
+    __syncthreads();
+
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_u8*)s_tab + 32u * wv;
+    uint32_t mask = 0x1Eu;
+    asm volatile("" : "+v"(mask));
+    const uint32_t xb = (uint32_t)(uintptr_t)(lds_u8*)s_x + 16u * lane;
+    float acc0[B], acc1[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc0[b] = acc1[b] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) {
+        if (c + PC < CPR) load_codes(c + PC);
+        const uint32_t d0 = cr[c % (PC + 1)][0], d1 = cr[c % (PC + 1)][1];
+        uint32_t a[16];
+        a[0] = (code4_x2<0>(d0, d1) & mask) | base;
+        a[1] = (code4_x2<1>(d0, d1) & mask) | base;
+        a[2] = (code4_x2<2>(d0, d1) & mask) | base;
+        a[3] = (code4_x2<3>(d0, d1) & mask) | base;
+        a[4] = (code4_x2<4>(d0, d1) & mask) | base;
+        a[5] = (code4_x2<5>(d0, d1) & mask) | base;
+        a[6] = (code4_x2<6>(d0, d1) & mask) | base;
+        a[7] = (code4_x2<7>(d0, d1) & mask) | base;
+        a[8] = (code4_x2<8>(d0, d1) & mask) | base;
+        a[9] = (code4_x2<9>(d0, d1) & mask) | base;
+        a[10] = (code4_x2<10>(d0, d1) & mask) | base;
+        a[11] = (code4_x2<11>(d0, d1) & mask) | base;
+        a[12] = (code4_x2<12>(d0, d1) & mask) | base;
+        a[13] = (code4_x2<13>(d0, d1) & mask) | base;
+        a[14] = (code4_x2<14>(d0, d1) & mask) | base;
+        a[15] = (code4_x2<15>(d0, d1) & mask) | base;
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            w[j] = __builtin_amdgcn_perm(*(lds_u16*)(uintptr_t)a[2 * j + 1], *(lds_u16*)(uintptr_t)a[2 * j],
+                                         0x05040100u);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const u32x4_t xl = *(lds_u4*)(uintptr_t)(xb + 16u * NX * b + 2048u * c);
+            const u32x4_t xh = *(lds_u4*)(uintptr_t)(xb + 16u * NX * b + 2048u * c + 1024u);
+            const uint32_t xv[8] = {xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]};
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                acc0[b] = dot2(w[j], xv[j], acc0[b]);
+                acc1[b] = dot2(w[j + 1], xv[j + 1], acc1[b]);
+            }
+            asm volatile("" : "+v"(acc0[b]), "+v"(acc1[b]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float sum = wave_sum_lane63(acc0[b] + acc1[b]);
+        if (lane == 63 && row_u < rows) {
+            if (y_f32)
+                reinterpret_cast<float*>(y)[(int64_t)b * rows + row_u] = sum;
+            else
+                reinterpret_cast<uint16_t*>(y)[(int64_t)b * rows + row_u] = f32_to_bf16(sum);
+        }
+    }
+}
+
 // Any width (cols % 16 == 0) and batch 1..16: one row per wave, lane i takes
 // the 8-byte pieces i, i + 64, ..., decodes its 16 codes through the row's
 // table in LDS and adds the B products in fp32.
@@ -212,6 +317,25 @@ hipError_t launch_cells(const fqm_weights& w, const uint16_t* x, void* y, int y_
     }
 }
 
+// Batches 2 and 3 while two groups of the batch kernel fit a CU (B * cells
+// <= 38, as for the 6-bit codes).
+constexpr int kRowsMaxBatch = 3;
+constexpr int batch_max_cells(int b) { return 38 / b; }
+
+template <int CPR, int B>
+hipError_t launch_cells_batch(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
+    if constexpr (CPR > batch_max_cells(B)) {
+        return hipErrorInvalidValue;
+    } else {
+        if ((w.cols >> 10) != CPR) return launch_cells_batch<CPR + 1, B>(w, x, y, y_f32, s);
+        constexpr int WPG = CPR <= 8 ? 4 : 10;
+        const unsigned grid = (unsigned)((w.rows + WPG - 1) / WPG);
+        hipLaunchKernelGGL((lut4_gemv_cells_batch<CPR, WPG, 4, B>), dim3(grid), dim3(64 * WPG), 0, s,
+                           w.lut4.packed, w.lut4.ld, w.lut4.lut, x, y, y_f32, (int)w.rows);
+        return hipGetLastError();
+    }
+}
+
 template <int B>
 hipError_t launch_generic(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, hipStream_t s) {
     const unsigned grid = (unsigned)((w.rows + kWaves - 1) / kWaves);
@@ -236,8 +360,13 @@ static bool cells_supported(const fqm_weights& w) {
     return w.cols > 0 && (w.cols & 1023) == 0 && (w.cols >> 10) <= kMaxCells;
 }
 
+bool lut4_gemv_rows_path(const fqm_weights& w, int batch) {
+    if (batch == 1) return cells_supported(w);
+    return batch >= 2 && batch <= kRowsMaxBatch && cells_supported(w) && (w.cols >> 10) <= batch_max_cells(batch);
+}
+
 bool lut4_gemv_fast_path(const fqm_weights& w, int batch) {
-    return batch == 1 ? cells_supported(w) : lut_gemv_mfma_supported(w, batch);
+    return lut4_gemv_rows_path(w, batch) || (batch > 1 && lut_gemv_mfma_supported(w, batch));
 }
 
 hipError_t launch_lut4_gemv(const fqm_weights& w, const uint16_t* x, void* y, int y_f32, int batch,
@@ -245,6 +374,10 @@ hipError_t launch_lut4_gemv(const fqm_weights& w, const uint16_t* x, void* y, in
     if (w.rows > 0x7fffffff) return hipErrorInvalidValue;
     if (batch == 1 && cells_supported(w))
         return launch_cells<1>(w, x, y, y_f32, s);
+    if (lut4_gemv_rows_path(w, batch)) {
+        if (batch == 2) return launch_cells_batch<1, 2>(w, x, y, y_f32, s);
+        return launch_cells_batch<1, 3>(w, x, y, y_f32, s);
+    }
     if (lut_gemv_mfma_supported(w, batch)) return launch_lut_gemv_mfma(w, x, y, y_f32, batch, ws, s);
     return launch_batch<1>(w, x, y, y_f32, batch, s);
 }

@@ -368,7 +368,8 @@ bool lut_gemv_mfma_supported(const fqm_weights& w, int batch) {
 
 size_t lut_gemv_mfma_workspace(const fqm_weights& w, int batch) {
     if (!lut_gemv_mfma_supported(w, batch)) return 0;
-    if (w.format == FQM_LUT6 && lut6_gemv_rows_path(w, batch)) return 0;  // launch_lut6_gemv takes that kernel
+    // the one-row-per-wave kernels take these batches
+    if (w.format == FQM_LUT6 ? lut6_gemv_rows_path(w, batch) : lut4_gemv_rows_path(w, batch)) return 0;
     int64_t nb;
     int ns, cps;
     lut_mfma_split(w, &nb, &ns, &cps);

@@ -158,9 +158,11 @@ def test_lut4_batch_workspace_follows_the_lut6_rule(lib):
         a = lib.fqm_workspace_size(ctypes.byref(lut4(rows, cols, ld=cols // 2)), batch)
         b = lib.fqm_workspace_size(ctypes.byref(lut6(rows, cols, ld=cols * 3 // 4)), batch)
         assert a == b, (rows, cols, batch)
-    # except LUT6 at batch 2 (3) on 1-19 (1-12) whole 1024-column cells: one row per wave, no K split
-    assert lib.fqm_workspace_size(ctypes.byref(lut4(300, 4096, ld=2048)), 2) > 0
-    assert lib.fqm_workspace_size(ctypes.byref(lut6(300, 4096, ld=3072)), 2) == 0
+    # batch 2 (3) on 1-19 (1-12) whole 1024-column cells runs one row per wave in
+    # both formats: no K split, no workspace
+    for batch, cols in ((2, 4096), (2, 17408), (3, 12288)):
+        assert lib.fqm_workspace_size(ctypes.byref(lut4(300, cols, ld=cols // 2)), batch) == 0
+        assert lib.fqm_workspace_size(ctypes.byref(lut6(300, cols, ld=cols * 3 // 4)), batch) == 0
     need = lib.fqm_workspace_size(ctypes.byref(lut4(5120, 17408, ld=8704)), 8)
     assert need > 0
     w = lut4(5120, 17408, ld=8704)

@@ -66,6 +66,27 @@ def test_gemv_generic_widths_and_batches(batch):
         assert_close(to_f64(y), oracle.lut4.gemv(packed, inp.lut, x, cols), "f32", f"{rows}x{cols} b{batch}")
 
 
+# Batches 2 and 3 on whole 1024-column cells (2: 1-19, 3: 1-12) take the
+# one-row-per-wave kernel with every batch row's x in LDS: 4- and 10-wave
+# groups, ragged last groups, the largest cell counts and the MLP layers.
+@pytest.mark.parametrize("rows,cols,seed,batch", [(5, 1024, 50, 2), (77, 3072, 51, 3), (23, 9216, 52, 2),
+                                                  (41, 12288, 53, 3), (11, 19456, 54, 2), (17408, 5120, 55, 2),
+                                                  (5120, 17408, 56, 2)])
+def test_gemv_batch_rows_kernel(rows, cols, seed, batch):
+    inp = synth.lut4_input(rows, cols, seed)
+    packed = oracle.lut4.pack_codes(inp.codes)
+    w = fqm.Lut4Weights.from_codes(inp.codes, inp.lut, device=DEV)
+    assert fqm.workspace_size(w, batch) == 0
+    x = synth.activations(batch, cols, seed + 1)
+    out = "f32" if rows * cols < 10_000_000 else "bf16"
+    buf, y = guarded((batch, rows), torch.float32 if out == "f32" else torch.bfloat16)
+    print(f"lut4 batch-{batch} rows kernel {rows}x{cols}", flush=True)
+    fqm.gemv(w, bf16_dev(x), y=y)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf)
+    assert_close(to_f64(y), oracle.lut4.gemv(packed, inp.lut, x, cols), out, f"{rows}x{cols} b{batch}")
+
+
 @pytest.mark.parametrize("batch", [2, 3, 8, 9, 16])
 @pytest.mark.parametrize("rows,cols,seed", [(70, 1536, 13), (301, 4096, 14), (16, 512, 15)])
 def test_gemv_matrix_cores(batch, rows, cols, seed):
@@ -87,7 +108,7 @@ def test_gemv_matrix_cores_full_layers(rows, cols, seed, batch):
     partials in the workspace, added in split order)."""
     inp, packed = case(rows, cols, seed)
     w = weights(rows, cols, seed)
-    assert (fqm.workspace_size(w, batch) > 0) == (rows == 5120)
+    assert (fqm.workspace_size(w, batch) > 0) == (rows == 5120)  # batch 8, 16: the matrix-core kernel's K split
     x = synth.activations(batch, cols, 11)
     y = fqm.gemv(w, bf16_dev(x))
     ref = oracle.lut4.gemv(packed, inp.lut, x, cols)
