@@ -199,3 +199,31 @@ def test_blocks_of_16_with_a_half_sign_dword(hi_bits, cb_mode, batch):
         W = fqm.dequant(w).view(torch.int16).cpu().numpy().view(np.uint16)
         ref = oracle.numerics.bf16_bits_from_f64_rne(oracle.fabq.decode(p, rows, cols, bs, inp.n_hi))
         assert np.array_equal(W, ref)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_vector_centroids_graph_replays_match_eager(batch):
+    """Vector centroids run two kernels per call (the fold into the workspace,
+    then the GEMV).  Captured in a HIP graph and replayed with new x, with
+    eager work in between, every replay gives the eager result bit for bit."""
+    inp, p = variant(5120, 5120, 5, 4, 2, 512)
+    w = weights(inp)
+    xs = [bf16_dev(synth.activations(batch, 5120, 70 + i)) for i in range(3)]
+    x = xs[0].clone()
+    need = fqm.workspace_size(w, batch)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    y = torch.empty((batch, 5120), dtype=torch.float32, device=DEV)
+    fqm.gemv(w, x, y=y, workspace=ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fqm.gemv(w, x, y=y, workspace=ws)
+    for xi in xs:
+        x.copy_(xi)
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        eager = fqm.gemv(w, xi, out_dtype=torch.float32)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager)

@@ -104,3 +104,31 @@ def test_gemv_mfma_exact_invariants():
     y1 = to_f64(fqm.gemv(w, bf16_dev(np.repeat(x[2:3], 2, axis=0)), out_dtype=torch.float32))
     assert np.array_equal(y1[0], y1[1])
     assert np.linalg.norm(y1[0] - y[2]) <= 1e-6 * np.linalg.norm(y[2])
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 8])
+def test_graph_replays_match_eager(batch):
+    """The down layer (17 cells: batches 1-2 on the one-row-per-wave kernels,
+    3 and 8 on the matrix cores with their K split and sum in the workspace),
+    captured in a HIP graph and replayed with new x, with eager work in
+    between: every replay gives the eager result bit for bit."""
+    rows, cols, seed = 5120, 17408, 3
+    w = lut6_weights(rows, cols, seed)
+    xs = [bf16_dev(synth.activations(batch, cols, 80 + i)) for i in range(3)]
+    x = xs[0].clone()
+    need = fqm.workspace_size(w, batch)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV) if need else None
+    y = torch.empty((batch, rows), dtype=torch.float32, device=DEV)
+    fqm.gemv(w, x, y=y, workspace=ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fqm.gemv(w, x, y=y, workspace=ws)
+    for xi in xs:
+        x.copy_(xi)
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        eager = fqm.gemv(w, xi, out_dtype=torch.float32, workspace=ws)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager)
