@@ -71,6 +71,21 @@ def test_all_int4_and_all_binary_layers(batch):
         assert_close(to_f64(y), oracle.fabq.gemv(p, x, 64, 1024, 64, inp.n_hi), "f32", f"hi={frac}")
 
 
+@pytest.mark.parametrize("batch", [1, 5])
+def test_vector_centroids_all_int4_and_all_binary_layers(batch):
+    """Vector centroids: a layer without binary rows needs no fold and no
+    workspace (nothing reads the centroid terms); an all-binary layer folds
+    every block.  Batch 1 on the VALU kernel, 5 on the matrix-core one."""
+    for frac in (1.0, 0.0):
+        inp = synth.fabq_input(64, 1024, 53, blocksize=128, hi_frac=frac, cb_mode=2)
+        p = oracle.fabq.pack(inp)
+        w = weights(inp)
+        assert (fqm.workspace_size(w, batch) == 0) == (frac == 1.0)
+        x = synth.activations(batch, 1024, 53)
+        y = fqm.gemv(w, bf16_dev(x), out_dtype=torch.float32)
+        assert_close(to_f64(y), oracle.fabq.gemv(p, x, 64, 1024, 128, inp.n_hi), "f32", f"vector hi={frac}")
+
+
 def _full_nibble_range(rows, cols, seed, bs, hi_frac):
     """A layer whose int4 rows hold every value -8..7.  The quantizer's
     max|w|/7 scale never produces -8 (nibble 0x8), so the int4 values are

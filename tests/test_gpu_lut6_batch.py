@@ -45,7 +45,8 @@ def test_gemv_mfma_cases(rows, cols, seed, batches, out):
 # weight for all rows): 4-wave groups up to 8 cells, 10-wave groups past
 # that, last groups partly past the end, the largest cell counts, and the
 # two MLP layers.
-@pytest.mark.parametrize("rows,cols,seed,batch", [(5, 1024, 40, 2), (77, 3072, 41, 3), (130, 8192, 42, 2),
+@pytest.mark.parametrize("rows,cols,seed,batch", [(1, 1024, 39, 2), (1, 9216, 39, 3), (5, 1024, 40, 2),
+                                                  (77, 3072, 41, 3), (130, 8192, 42, 2),
                                                   (23, 9216, 44, 2), (41, 12288, 45, 3), (11, 19456, 46, 2),
                                                   (17408, 5120, 43, 2), (17408, 5120, 43, 3), (5120, 17408, 47, 2)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
