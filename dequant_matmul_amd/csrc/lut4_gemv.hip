@@ -19,6 +19,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32c;
 typedef __attribute__((address_space(3))) const u32x4_t lds_u4;
 
 constexpr int kWaves = 4;
@@ -48,8 +49,16 @@ __device__ __forceinline__ uint32_t code4_x2(uint32_t d0, uint32_t d1) {
 // becomes a gather address in a shift and one v_and_or_b32; the 64 lanes read
 // 8 dwords in 8 distinct banks.  Codes are requested PC chunks ahead, every
 // load unconditional; the row sum is one DPP reduction per wave.
+// With PT the wave's slot holds a 1 KB table of weight pairs instead: entry p
+// is lut[p & 15] | lut[p >> 4] << 16, so byte j of a lane's codes (codes 2j
+// and 2j + 1) addresses the pair that meets x pair j in v_dot2 directly: one
+// shift, one v_and_or_b32 and one 32-bit gather per two weights, and no
+// v_perm_b32.  The dot2 operands and their order are those of the 16-entry
+// path, so the result is the same bit for bit.  Building the pairs costs
+// five table loads and four LDS stores per lane and row, which only rows of
+// many cells repay.
 // ---------------------------------------------------------------------------
-template <int CPR, int WPG, int PC>
+template <int CPR, int WPG, int PC, bool PT>
 __global__ __launch_bounds__(64 * WPG) void lut4_gemv_cells(const uint8_t* __restrict__ packed, int64_t ld,
                                                             const uint16_t* __restrict__ lut,
                                                             const uint16_t* __restrict__ x,
@@ -57,7 +66,7 @@ __global__ __launch_bounds__(64 * WPG) void lut4_gemv_cells(const uint8_t* __res
     constexpr int NX = CPR * 128;                          // x in 16-byte pieces
     constexpr int XS = (NX + 64 * WPG - 1) / (64 * WPG);   // staging pieces per thread
     __shared__ __attribute__((aligned(16))) u32x4_t s_x[NX];
-    __shared__ __attribute__((aligned(32))) uint32_t s_tab[WPG][8];
+    __shared__ __attribute__((aligned(PT ? 1024 : 32))) uint32_t s_tab[WPG][PT ? 256 : 8];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int row_u = blockIdx.x * WPG + wv;
@@ -68,7 +77,11 @@ __global__ __launch_bounds__(64 * WPG) void lut4_gemv_cells(const uint8_t* __res
 #pragma unroll
     for (int u = 0; u < XS; ++u)
         xs[u] = reinterpret_cast<const u32x4_t*>(x)[min(tid + u * 64 * WPG, NX - 1)];
-    const uint32_t tv = reinterpret_cast<const uint32_t*>(lut + (int64_t)row * 16)[lane & 7];
+    const uint16_t* lr = lut + (int64_t)row * 16;
+    const uint32_t tv = PT ? (uint32_t)lr[lane & 15] : reinterpret_cast<const uint32_t*>(lr)[lane & 7];
+    uint32_t t_hi[4];  // PT: entries (lane >> 4) + 4 t, the high halves of pairs lane + 64 t
+#pragma unroll
+    for (int t = 0; t < 4; ++t) t_hi[t] = PT ? lr[(lane >> 4) + 4 * t] : 0u;
     __builtin_amdgcn_sched_barrier(0);
 
     uint32_t cr[PC + 1][2];
@@ -86,11 +99,16 @@ __global__ __launch_bounds__(64 * WPG) void lut4_gemv_cells(const uint8_t* __res
         const int k = min(tid + u * 64 * WPG, NX - 1);
         s_x[((k >> 7) << 7) | ((k & 1) << 6) | ((k >> 1) & 63)] = xs[u];  // clamped duplicates store equal values
     }
-    s_tab[wv][lane & 7] = tv;  // unconditional (lanes repeat), so the load stays ahead of the codes
+    if constexpr (PT) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s_tab[wv][lane + 64 * t] = tv | (t_hi[t] << 16);
+    } else {
+        s_tab[wv][lane & 7] = tv;  // unconditional (lanes repeat), so the load stays ahead of the codes
+    }
     __syncthreads();
 
-    const uint32_t base = (uint32_t)(uintptr_t)(lds_u8*)s_tab + 32u * wv;  // multiple of 32
-    uint32_t mask = 0x1Eu;
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_u8*)s_tab + (PT ? 1024u : 32u) * wv;  // multiple of the slot
+    uint32_t mask = PT ? 0x3FCu : 0x1Eu;
     asm volatile("" : "+v"(mask));  // in a VGPR: (code & mask) | base is one v_and_or_b32
     const uint32_t xb = (uint32_t)(uintptr_t)(lds_u8*)s_x + 16u * lane;
     float acc0 = 0.f, acc1 = 0.f;
@@ -101,6 +119,23 @@ __global__ __launch_bounds__(64 * WPG) void lut4_gemv_cells(const uint8_t* __res
         const u32x4_t xh = *(lds_u4*)(uintptr_t)(xb + 2048u * c + 1024u);
         const uint32_t xv[8] = {xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]};
         const uint32_t d0 = cr[c % (PC + 1)][0], d1 = cr[c % (PC + 1)][1];
+        if constexpr (PT) {
+            uint32_t p[8];  // byte j of the lane's codes, as the LDS address of its pair
+            p[0] = ((d0 << 2) & mask) | base;
+            p[1] = ((d0 >> 6) & mask) | base;
+            p[2] = ((d0 >> 14) & mask) | base;
+            p[3] = ((d0 >> 22) & mask) | base;
+            p[4] = ((d1 << 2) & mask) | base;
+            p[5] = ((d1 >> 6) & mask) | base;
+            p[6] = ((d1 >> 14) & mask) | base;
+            p[7] = ((d1 >> 22) & mask) | base;
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                acc0 = dot2(*(lds_u32c*)(uintptr_t)p[j], xv[j], acc0);
+                acc1 = dot2(*(lds_u32c*)(uintptr_t)p[j + 1], xv[j + 1], acc1);
+            }
+            continue;
+        }
         uint32_t a[16];
         a[0] = (code4_x2<0>(d0, d1) & mask) | base;
         a[1] = (code4_x2<1>(d0, d1) & mask) | base;
@@ -311,7 +346,9 @@ hipError_t launch_cells(const fqm_weights& w, const uint16_t* x, void* y, int y_
         if ((w.cols >> 10) != CPR) return launch_cells<CPR + 1>(w, x, y, y_f32, s);
         constexpr int WPG = CPR <= 8 ? 4 : 10;
         const unsigned grid = (unsigned)((w.rows + WPG - 1) / WPG);
-        hipLaunchKernelGGL((lut4_gemv_cells<CPR, WPG, 4>), dim3(grid), dim3(64 * WPG), 0, s, w.lut4.packed,
+        // pair tables on rows of more than 8 cells: 5120 x 17408 took 14.4-14.6 us
+        // against 15.2-15.4 us; on 17408 x 5120 they cost 8 % (14.9-15.0 against 13.8 us)
+        hipLaunchKernelGGL((lut4_gemv_cells<CPR, WPG, 4, (CPR > 8)>), dim3(grid), dim3(64 * WPG), 0, s, w.lut4.packed,
                            w.lut4.ld, w.lut4.lut, x, y, y_f32, (int)w.rows);
         return hipGetLastError();
     }
